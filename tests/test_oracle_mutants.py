@@ -1,0 +1,138 @@
+"""Plants plausible mistakes in the CPU oracle and checks that the pins catch each one.
+
+The mistakes are planted in the oracle module for the duration of one test (monkeypatch),
+on the CPU only: a dropped term, a wrong index or sign, a transposed operand, a wrong
+denominator. A mutant that no pin rejects would mean the pins leave that part unchecked.
+"""
+import numpy as np
+import pytest
+
+from oracle import saf_oracle as so
+from tests.oracle_pins import PINS
+
+
+def _frozen_alpha_by_query(alpha, rho):
+    alpha, rho = np.asarray(alpha, float), np.asarray(rho, float)
+    T = alpha.shape[0]
+    i, j = np.arange(T)[:, None], np.arange(T)[None, :]
+    c = j <= i
+    E = np.where(c, np.exp(alpha[i] + rho[np.where(c, i - j, 0)]), 0.0)
+    Z = E.sum(1)
+    return E / Z[:, None], np.log(Z)
+
+
+def _frozen_no_alpha(alpha, rho):
+    return so.__dict__["_orig_frozen"](np.zeros_like(np.asarray(alpha, float)), rho)
+
+
+def _frozen_rho_by_key(alpha, rho):
+    alpha, rho = np.asarray(alpha, float), np.asarray(rho, float)
+    T = alpha.shape[0]
+    i, j = np.arange(T)[:, None], np.arange(T)[None, :]
+    c = j <= i
+    E = np.where(c, np.exp(alpha[j] + rho[np.broadcast_to(j, (T, T))]), 0.0)
+    Z = E.sum(1)
+    return E / Z[:, None], np.log(Z)
+
+
+def _frozen_strict(alpha, rho):
+    alpha, rho = np.asarray(alpha, float), np.asarray(rho, float)
+    T = alpha.shape[0]
+    i, j = np.arange(T)[:, None], np.arange(T)[None, :]
+    c = (j < i) | ((i == 0) & (j == 0))
+    E = np.where(c, np.exp(alpha[j] + rho[np.where(c, i - j, 0)]), 0.0)
+    Z = E.sum(1)
+    return E / Z[:, None], np.log(Z)
+
+
+def _dynamic_no_scale(q, k, scale):
+    return so.__dict__["_orig_dynamic"](q, k, 1.0)
+
+
+def _dynamic_swapped(q, k, scale):
+    return so.__dict__["_orig_dynamic"](k, q, scale)
+
+
+def _dynamic_lse_no_max(q, k, scale):
+    A, lse = so.__dict__["_orig_dynamic"](q, k, scale)
+    S = scale * np.asarray(q, float) @ np.asarray(k, float).T
+    m = np.where(so.causal_mask(S.shape[0]), S, -np.inf).max(1)
+    return A, lse - m
+
+
+def _bwd_factory(kind):
+    def attn_bwd(q, k, v, do, frozen, alpha, rho, scale):
+        v, do = np.asarray(v, float), np.asarray(do, float)
+        B, H, T, D = v.shape
+        dq = np.full(v.shape, np.nan); dk = np.full(v.shape, np.nan); dv = np.empty(v.shape)
+        for h in range(H):
+            for b in range(B):
+                if frozen[h]:
+                    P, _ = so.frozen_probs(alpha[h, :T], rho[h, :T])
+                    dv[b, h] = (P if kind == "frozen_no_T" else P.T) @ do[b, h]
+                    continue
+                qb, kb = np.asarray(q[b, h], float), np.asarray(k[b, h], float)
+                A, _ = so.dynamic_probs(qb, kb, scale)
+                dv[b, h] = A.T @ do[b, h]
+                dA = do[b, h] @ v[b, h].T
+                if kind == "no_rowterm":
+                    dS = A * dA
+                else:
+                    dS = A * (dA - (A * dA).sum(1, keepdims=True))
+                dq[b, h] = scale * (dS @ kb)
+                dk[b, h] = scale * ((dS if kind == "dk_untransposed" else dS.T) @ qb)
+                if kind == "dq_no_scale":
+                    dq[b, h] = dS @ kb
+        return dq, dk, dv
+    return attn_bwd
+
+
+def _var_div_n(A_stack):
+    A_stack = np.asarray(A_stack, float)
+    N, T, _ = A_stack.shape
+    A_hat = A_stack.mean(0)
+    return float(((A_stack - A_hat) ** 2).sum() / (N * T * T)), A_hat
+
+
+def _var_div_pairs(A_stack):
+    A_stack = np.asarray(A_stack, float)
+    N, T, _ = A_stack.shape
+    A_hat = A_stack.mean(0)
+    return float(((A_stack - A_hat) ** 2).sum() / ((N - 1) * T * (T + 1) / 2)), A_hat
+
+
+def _rank_desc(s):
+    return np.argsort(-np.asarray(s), kind="stable").astype(np.int32)
+
+
+MUTANTS = {
+    "frozen: alpha indexed by query": ("frozen_probs", _frozen_alpha_by_query),
+    "frozen: alpha dropped": ("frozen_probs", _frozen_no_alpha),
+    "frozen: rho indexed by key, not distance": ("frozen_probs", _frozen_rho_by_key),
+    "frozen: diagonal excluded": ("frozen_probs", _frozen_strict),
+    "dynamic: 1/sqrt(d) scale dropped": ("dynamic_probs", _dynamic_no_scale),
+    "dynamic: q and k swapped": ("dynamic_probs", _dynamic_swapped),
+    "dynamic: lse without the max": ("dynamic_probs", _dynamic_lse_no_max),
+    "bwd: softmax row term dropped": ("attn_bwd", _bwd_factory("no_rowterm")),
+    "bwd: dK operand not transposed": ("attn_bwd", _bwd_factory("dk_untransposed")),
+    "bwd: dQ scale dropped": ("attn_bwd", _bwd_factory("dq_no_scale")),
+    "bwd: frozen dV with P instead of P^T": ("attn_bwd", _bwd_factory("frozen_no_T")),
+    "var: divides by N": ("variance_score", _var_div_n),
+    "var: divides by causal pairs": ("variance_score", _var_div_pairs),
+    "rank: descending": ("rank_heads", _rank_desc),
+}
+
+
+@pytest.mark.parametrize("name", list(MUTANTS))
+def test_pins_reject_mutant(name, monkeypatch):
+    attr, fn = MUTANTS[name]
+    monkeypatch.setitem(so.__dict__, "_orig_frozen", so.frozen_probs)
+    monkeypatch.setitem(so.__dict__, "_orig_dynamic", so.dynamic_probs)
+    monkeypatch.setattr(so, attr, fn)
+    caught = []
+    for pin in PINS:
+        try:
+            pin(so)
+        except Exception:  # an assertion, or the mutant breaking the pin outright
+            caught.append(pin.__name__)
+    assert caught, f"no pin rejects the mutant '{name}'"
