@@ -1,0 +1,190 @@
+"""Throughput of the SAF hybrid attention layer (forward + backward) on one MI355X.
+
+A step is one hybrid forward (saf_attn_fwd) plus one backward (saf_attn_bwd) of one layer
+over resident synthetic inputs. Default workload: the 1B-shaped layer, B=2, H=16, T=8192,
+d_h=128, bf16, 25% of heads frozen (4 of 16). Prints one JSON line.
+
+    python bench.py [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "hybrid attn fwd+bwd tokens/s per layer + MFMA util (1B-shape, T=8192, r=25%)"
+PEAK_BF16_TFLOPS = 2516.6  # MI355X dense bf16 MFMA (published)
+
+
+def causal_pairs(T: int) -> int:
+    return T * (T + 1) // 2
+
+
+def kernel_flops(B, T, D, n_dyn, n_frz):
+    """Algorithmic FLOPs per launch of each kernel (only causal pairs, no recomputation
+    counted twice): ordinary head fwd 4 D Pc (Q K^T, P V); dK/dV kernel 8 D Pc (S recompute,
+    dP, P^T dO, dS^T Q); dQ kernel 2 D Pc (dS K); frozen head fwd 2 D Pc and bwd 2 D Pc."""
+    pc = causal_pairs(T)
+    nd, nf = B * n_dyn, B * n_frz
+    return {
+        "hybrid_fwd": (4 * nd + 2 * nf) * D * pc,
+        "dkdv": (8 * nd + 2 * nf) * D * pc,
+        "dq": 2 * nd * D * pc,
+    }
+
+
+def layer_flops(B, T, D, n_dyn, n_frz):
+    pc = causal_pairs(T)
+    return (14 * B * n_dyn + 4 * B * n_frz) * D * pc
+
+
+def cpu_baseline(L, n_dyn, n_frz):
+    """The CPU oracle (numpy float64, dense T x T) timed on a bounded sample of the workload:
+    one ordinary and one frozen (b, h) of the layer, forward + backward, scaled to the layer."""
+    from oracle import saf_oracle
+    try:
+        import threadpoolctl
+        threads = max([i.get("num_threads", 1) for i in threadpoolctl.threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        threads = 1
+    scale = 1.0 / math.sqrt(L["D"])
+    B, T = L["B"], L["T"]
+    t_head = {}
+    for kind, sel in (("dyn", L["frozen"] == 0), ("frz", L["frozen"] != 0)):
+        if not sel.any():
+            continue
+        h = int(np.flatnonzero(sel)[0])
+        s = lambda x: x[0:1, h:h + 1]
+        fz, al, rh = L["frozen"][h:h + 1], L["alpha"][h:h + 1], L["rho"][h:h + 1]
+        t0 = time.perf_counter()
+        saf_oracle.attn_fwd(s(L["q"]), s(L["k"]), s(L["v"]), fz, al, rh, scale)
+        saf_oracle.attn_bwd(s(L["q"]), s(L["k"]), s(L["v"]), s(L["do"]), fz, al, rh, scale)
+        t_head[kind] = time.perf_counter() - t0
+    layer_s = B * n_dyn * t_head.get("dyn", 0.0) + B * n_frz * t_head.get("frz", 0.0)
+    return {
+        "value": B * T / layer_s, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
+        "sample": (f"one ordinary and one frozen (b,h) head at T={T} (fwd+bwd, float64, dense TxT), "
+                   f"{sum(t_head.values()):.1f} s measured, scaled to the layer's {B * n_dyn} ordinary "
+                   f"and {B * n_frz} frozen heads; BLAS threads={threads}, host cores="
+                   f"{len(os.sched_getaffinity(0))}, numpy elementwise ops single-threaded"),
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="l1b_fwdbwd")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-sweep", action="store_true", help="skip the r=0 / r=50%% timings")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU: the layer's heads are independent and this build has no "
+              "multi-GPU path; run with --gpus 1", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    from hybrid_static_pattern_amd import inputs, saf
+
+    saf.load()
+    spec = dict(inputs.WORKLOADS[args.workload])
+    L = inputs.make_layer(**spec)
+    B, H, T, D = L["B"], L["H"], L["T"], L["D"]
+    dev = torch.device("cuda:0")
+    cast = torch.bfloat16 if L["dtype"] == "bf16" else torch.float32
+    up = lambda x: torch.from_numpy(x).to(dev).to(cast)
+    q, k, v, do = (up(L[x]) for x in ("q", "k", "v", "do"))
+    alpha, rho = torch.from_numpy(L["alpha"]).to(dev), torch.from_numpy(L["rho"]).to(dev)
+    o = torch.empty_like(v)
+    lse = torch.empty((B, H, T), dtype=torch.float32, device=dev)
+    dq, dk, dv = (torch.zeros((B, H, T, D), dtype=torch.float32, device=dev) for _ in range(3))
+    ws = torch.empty(max(saf.attn_workspace_size(v, L["frozen"], alpha), 1), dtype=torch.uint8, device=dev)
+
+    def step(mask):
+        saf.attn_fwd(q, k, v, mask, alpha, rho, o=o, lse=lse)
+        saf.attn_bwd(q, k, v, o, do, lse, mask, alpha, rho, dq=dq, dk=dk, dv=dv, workspace=ws)
+
+    def timed(mask, steps, warmup, prof=False):
+        for _ in range(warmup):
+            step(mask)
+        torch.cuda.synchronize()
+        if prof:
+            saf.prof_enable(True)
+        s = torch.cuda.current_stream()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(s)
+        for _ in range(steps):
+            step(mask)
+        e1.record(s)
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / steps
+        recs = saf.prof_read() if prof else []
+        if prof:
+            saf.prof_enable(False)
+        return ms, recs
+
+    mask = L["frozen"]
+    n_frz = int(mask.sum())
+    n_dyn = H - n_frz
+    ms, recs = timed(mask, args.steps, args.warmup, prof=True)
+
+    per_kernel = {}
+    for name, t in recs:
+        per_kernel.setdefault(name, []).append(t)
+    kern_ms = {name: float(np.mean(ts)) for name, ts in per_kernel.items()}
+    flops_k = kernel_flops(B, T, D, n_dyn, n_frz)
+    dominant = max(kern_ms, key=lambda n: kern_ms[n])
+    achieved = flops_k.get(dominant, 0) / (kern_ms[dominant] * 1e-3) / 1e12
+    total_flops = layer_flops(B, T, D, n_dyn, n_frz)
+    tflops = total_flops / (ms * 1e-3) / 1e12
+
+    out = {
+        "metric": METRIC,
+        "value": B * T / (ms * 1e-3),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if L["dtype"] == "bf16" else "f32",
+        "data": "synthetic (seeded N(0,1) Q/K/V/dO, alpha/rho recency tables; no trained weights)",
+        "config": {"workload": args.workload, "B": B, "H": H, "T": T, "D": D,
+                   "frozen_heads": n_frz, "r": n_frz / H},
+        "tflops": tflops,
+        "mfma_frac": tflops / PEAK_BF16_TFLOPS,
+        "kernels_ms": kern_ms,
+        "roofline": {
+            "kernel": dominant, "bound": "mfma", "achieved": achieved, "peak": PEAK_BF16_TFLOPS,
+            "unit": "TFLOP/s", "frac": achieved / PEAK_BF16_TFLOPS, "traffic": None,
+        },
+    }
+    if not args.no_sweep:
+        sweep = {}
+        for r_name, nf in (("r0", 0), ("r50", H // 2)):
+            m2 = np.zeros(H, np.uint8)
+            if nf:
+                m2[np.sort(np.random.default_rng(spec["seed"]).choice(H, nf, replace=False))] = 1
+            ms2, _ = timed(m2, args.steps, args.warmup)
+            sweep[r_name] = {"ms_per_step": ms2, "tokens_per_s": B * T / (ms2 * 1e-3),
+                             "tflops": layer_flops(B, T, D, H - nf, nf) / (ms2 * 1e-3) / 1e12}
+        out["sweep"] = sweep
+        out["speedup_vs_r0"] = sweep["r0"]["ms_per_step"] / ms
+    out["cpu_baseline"] = None if args.no_cpu_baseline else cpu_baseline(L, n_dyn, n_frz)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

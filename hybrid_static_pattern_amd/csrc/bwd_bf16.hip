@@ -1,0 +1,648 @@
+// Hybrid causal attention backward, bf16 inputs, fp32 gradients, gfx950 MFMA.
+//
+// Method: "When Can Attention Heads Be Statically Defined?: 中文精读笔记".
+//   ordinary heads: the textbook softmax-attention gradient of part 一's layer,
+//       dV = A^T dO, dS = A o (dO V^T - delta), dQ = scale dS K, dK = scale dS^T Q,
+//       delta_i = sum_c dO_ic O_ic, with A recomputed from the saved log-normaliser;
+//   frozen heads (part 二.4 / Algorithm 1): alpha and rho are fixed buffers without
+//       gradient and there is no query or key, so the only gradient is dV = P^T dO,
+//       P rebuilt from alpha, rho and log Z exactly as in the forward (Eq. (3)).
+//
+// Kernels, in launch order:
+//   bwd_delta   delta for ordinary heads (one 8-lane group per row);
+//   dkdv        one launch holding two kinds of work items:
+//       ordinary (b, h, 128-key tile): each wave keeps 32 keys (K, V fragments and the
+//           fp32 dK, dV tiles) in registers and walks the 64-query steps from the
+//           diagonal down; S and dP are computed with the key as the lane index so P
+//           and dS feed the dV and dK products straight from registers;
+//       frozen (h, 128-key tile, column chunk): the batch is folded into up to 256
+//           columns of [dO_0 | dO_1 | ...]; P^T is regenerated per lane and split into a
+//           bf16 high and low part (two MFMAs) so the fp32 dV keeps ~16 bits of P;
+//   dq          ordinary (b, h, 128-query tile), keys from 0 to the diagonal, the query
+//           as the lane index (as in the forward): dQ = scale * sum_J dS K_J.
+// The split into a key-stationary and a query-stationary kernel recomputes S and dP once
+// more instead of accumulating dQ with atomics; every output is written exactly once.
+#include "saf_device.h"
+#include "saf_internal.h"
+
+namespace saf {
+
+namespace {
+
+constexpr int NTH = 256;
+constexpr int BNK = 128;   // keys per dK/dV workgroup
+constexpr int BMQ = 64;    // queries per dK/dV step
+constexpr int BMD = 128;   // queries per dQ workgroup
+constexpr int BND = 64;    // keys per dQ step
+constexpr int FCOLS = 256;
+
+struct BwdParams {
+  const bf16* q;
+  const bf16* k;
+  const bf16* v;
+  const bf16* dO;
+  const float* lse;
+  const float* delta;
+  const float* alpha;
+  const float* rho;
+  float* dq;
+  float* dk;
+  float* dv;
+  int tab_stride, B, H, T;
+  float c;      // scale * log2(e)
+  float scale;
+  int n_dyn, n_frz, n_chunks, per_tile, n_tiles;
+  uint8_t dyn[kMaxHeads];
+  uint8_t frz[kMaxHeads];
+};
+
+// ---------------------------------------------------------------- delta
+
+struct DeltaParams {
+  const void* o;
+  const void* dO;
+  float* delta;
+  int H, T, D, n_rows;  // n_rows = B * n_dyn * T
+  int n_dyn;
+  bool bf16;
+  uint8_t dyn[kMaxHeads];
+};
+
+__global__ __launch_bounds__(256) void bwd_delta_kernel(const DeltaParams p) {
+  const int row = blockIdx.x * 32 + (threadIdx.x >> 3), sub = threadIdx.x & 7;
+  float acc = 0.f;
+  size_t r = 0;
+  if (row < p.n_rows) {
+    const int i = row % p.T, bh = row / p.T;
+    const int h = p.dyn[bh % p.n_dyn], b = bh / p.n_dyn;
+    r = ((size_t)b * p.H + h) * p.T + i;
+    if (p.bf16) {
+      const uint16_t* O = static_cast<const uint16_t*>(p.o) + r * p.D;
+      const uint16_t* G = static_cast<const uint16_t*>(p.dO) + r * p.D;
+      for (int d = sub * 8; d < p.D; d += 64) {
+        const u32x4 a = *reinterpret_cast<const u32x4*>(O + d);
+        const u32x4 g = *reinterpret_cast<const u32x4*>(G + d);
+#pragma unroll
+        for (int x = 0; x < 4; ++x) {
+          acc = fmaf(bf16_to_f32(a[x] & 0xffff), bf16_to_f32(g[x] & 0xffff), acc);
+          acc = fmaf(bf16_to_f32(a[x] >> 16), bf16_to_f32(g[x] >> 16), acc);
+        }
+      }
+    } else {
+      const float* O = static_cast<const float*>(p.o) + r * p.D;
+      const float* G = static_cast<const float*>(p.dO) + r * p.D;
+      for (int d = sub * 4; d < p.D; d += 32) {
+        const f32x4 a = *reinterpret_cast<const f32x4*>(O + d);
+        const f32x4 g = *reinterpret_cast<const f32x4*>(G + d);
+#pragma unroll
+        for (int x = 0; x < 4; ++x) acc = fmaf(a[x], g[x], acc);
+      }
+    }
+  }
+#pragma unroll
+  for (int o = 1; o < 8; o <<= 1) acc += __shfl_xor(acc, o, 64);
+  if (row < p.n_rows && sub == 0) p.delta[r] = acc;
+}
+
+// ---------------------------------------------------------------- dK / dV
+
+template <int D>
+struct DkdvSmem {
+  bf16 qs[BMQ * D];   // Q rows, chunks swizzled by swz_pi(row)
+  bf16 gs[BMQ * D];   // dO rows
+  bf16 qt[D * BMQ];   // Q^T [d][q], chunks swizzled by swz_tr(d)
+  bf16 gt[D * BMQ];   // dO^T
+  float ls[BMQ];      // lse * log2(e)
+  float dl[BMQ];      // delta
+};
+
+struct FrzBwdSmem {
+  bf16 gt[FCOLS * BMQ];   // folded dO^T [column][q]
+  float lz[BMQ];          // log Z * log2(e)
+  float rw[BMQ + BNK];    // rho * log2(e) over the step's distance window
+};
+
+template <int D>
+constexpr int dkdv_smem_bytes() {
+  return sizeof(DkdvSmem<D>) > sizeof(FrzBwdSmem) ? (int)sizeof(DkdvSmem<D>) : (int)sizeof(FrzBwdSmem);
+}
+
+// Stages rows [i0, i0 + BMQ) of a [T, D] bf16 matrix: `reg` holds this thread's 4 x 8 block.
+template <int D>
+__device__ __forceinline__ void load_block(const bf16* X, int i0, int T, u32x4 (&reg)[4]) {
+  constexpr int CPR = D / 8;
+  const int t = threadIdx.x;
+  if (t < (BMQ / 4) * CPR) {
+    const int cg = t % CPR, rg = t / CPR;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int i = i0 + 4 * rg + r;
+      reg[r] = (i < T) ? *reinterpret_cast<const u32x4*>(X + (size_t)i * D + cg * 8) : u32x4{0, 0, 0, 0};
+    }
+  }
+}
+
+template <int D>
+__device__ __forceinline__ void store_block(const u32x4 (&reg)[4], bf16* rows, bf16* trans) {
+  constexpr int CPR = D / 8;
+  const int t = threadIdx.x;
+  if (t < (BMQ / 4) * CPR) {
+    const int cg = t % CPR, rg = t / CPR;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int row = 4 * rg + r;
+      *reinterpret_cast<u32x4*>(rows + row * D + ((cg ^ swz_pi(row)) * 8)) = reg[r];
+    }
+    u32x2 cols[8];
+    transpose_4x8(reg, cols);
+#pragma unroll
+    for (int c = 0; c < 8; ++c) {
+      const int d = cg * 8 + c;
+      *reinterpret_cast<u32x2*>(trans + d * BMQ + (((rg >> 1) ^ swz_tr(d)) * 8) + (rg & 1) * 4) = cols[c];
+    }
+  }
+}
+
+template <int D>
+__device__ void dkdv_dyn(const BwdParams& p, int b, int h, int kt, unsigned char* smem_raw) {
+  DkdvSmem<D>& sm = *reinterpret_cast<DkdvSmem<D>*>(smem_raw);
+  const int t = threadIdx.x, lane = lane_id(), w = wave_id();
+  const int m = lane & 31, hh = lane >> 5;
+  const int T = p.T;
+  const size_t head = ((size_t)b * p.H + h) * (size_t)T;
+  const bf16* Q = p.q + head * D;
+  const bf16* G = p.dO + head * D;
+  const int k0w = kt * BNK + 32 * w;
+  const int j = k0w + m;
+
+  bf16x8 kf[D / 16], vf[D / 16];
+#pragma unroll
+  for (int kk = 0; kk < D / 16; ++kk) {
+    const size_t off = (head + j) * D + kk * 16 + hh * 8;
+    kf[kk] = (j < T) ? *reinterpret_cast<const bf16x8*>(p.k + off) : bf16x8{};
+    vf[kk] = (j < T) ? *reinterpret_cast<const bf16x8*>(p.v + off) : bf16x8{};
+  }
+  f32x16 dv[D / 32], dk[D / 32];
+#pragma unroll
+  for (int db = 0; db < D / 32; ++db) {
+    dv[db] = f32x16{};
+    dk[db] = f32x16{};
+  }
+
+  const int i_start = kt * BNK;
+  const int n_steps = (T - i_start + BMQ - 1) / BMQ;
+  u32x4 qreg[4], greg[4];
+  float lreg = 0.f, dreg = 0.f;
+  auto gload = [&](int st) {
+    const int i0 = i_start + st * BMQ;
+    load_block<D>(Q, i0, T, qreg);
+    load_block<D>(G, i0, T, greg);
+    if (t < BMQ) {
+      const int i = i0 + t;
+      lreg = (i < T) ? p.lse[head + i] * kLog2e : __builtin_huge_valf();
+      dreg = (i < T) ? p.delta[head + i] : 0.f;
+    }
+  };
+  auto sstore = [&]() {
+    store_block<D>(qreg, sm.qs, sm.qt);
+    store_block<D>(greg, sm.gs, sm.gt);
+    if (t < BMQ) {
+      sm.ls[t] = lreg;
+      sm.dl[t] = dreg;
+    }
+  };
+
+  gload(0);
+  sstore();
+  __syncthreads();
+  for (int st = 0; st < n_steps; ++st) {
+    if (st + 1 < n_steps) gload(st + 1);
+    const int i0 = i_start + st * BMQ;
+#pragma unroll
+    for (int qb = 0; qb < BMQ / 32; ++qb) {
+      const int iq0 = i0 + 32 * qb;
+      if (k0w > iq0) continue;          // all keys of this wave after these queries
+      const bool diag = (k0w == iq0);
+      const int qrow = qb * 32 + perm_rows(m);
+      f32x16 s = f32x16{}, dp = f32x16{};
+#pragma unroll
+      for (int kk = 0; kk < D / 16; ++kk) {
+        const int ch = 2 * kk + hh;
+        const bf16x8 aq = *reinterpret_cast<const bf16x8*>(sm.qs + qrow * D + ((ch ^ swz_pi(qrow)) * 8));
+        s = mfma32(aq, kf[kk], s);
+      }
+#pragma unroll
+      for (int kk = 0; kk < D / 16; ++kk) {
+        const int ch = 2 * kk + hh;
+        const bf16x8 ag = *reinterpret_cast<const bf16x8*>(sm.gs + qrow * D + ((ch ^ swz_pi(qrow)) * 8));
+        dp = mfma32(ag, vf[kk], dp);
+      }
+      float pr[16], dsr[16];
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int qi = qb * 32 + acc_pos(r, hh);
+        float pv = __builtin_amdgcn_exp2f(__builtin_fmaf(s[r], p.c, -sm.ls[qi]));
+        if (diag && (32 * qb + acc_pos(r, hh)) + i0 < j) pv = 0.f;
+        pr[r] = pv;
+        dsr[r] = pv * (dp[r] - sm.dl[qi]);
+      }
+#pragma unroll
+      for (int sk = 0; sk < 2; ++sk) {
+        const bf16x8 pa = pack8(pr + 8 * sk);
+        const bf16x8 da = pack8(dsr + 8 * sk);
+        const int ch = 4 * qb + 2 * sk + hh;
+#pragma unroll
+        for (int db = 0; db < D / 32; ++db) {
+          const int d = db * 32 + m;
+          const bf16x8 bg = *reinterpret_cast<const bf16x8*>(sm.gt + d * BMQ + ((ch ^ swz_tr(d)) * 8));
+          dv[db] = mfma32(pa, bg, dv[db]);
+          const bf16x8 bq = *reinterpret_cast<const bf16x8*>(sm.qt + d * BMQ + ((ch ^ swz_tr(d)) * 8));
+          dk[db] = mfma32(da, bq, dk[db]);
+        }
+      }
+    }
+    __syncthreads();
+    if (st + 1 < n_steps) {
+      sstore();
+      __syncthreads();
+    }
+  }
+
+#pragma unroll
+  for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int key = k0w + acc_row(r, hh);
+      if (key < T) {
+        const size_t off = (head + key) * D + db * 32 + m;
+        p.dv[off] = dv[db][r];
+        p.dk[off] = dk[db][r] * p.scale;
+      }
+    }
+}
+
+template <int D>
+__device__ void dkdv_frz(const BwdParams& p, int h, int chunk, int kt, unsigned char* smem_raw) {
+  FrzBwdSmem& sm = *reinterpret_cast<FrzBwdSmem*>(smem_raw);
+  const int t = threadIdx.x, lane = lane_id(), w = wave_id();
+  const int m = lane & 31, hh = lane >> 5;
+  const int T = p.T, H = p.H;
+  const int ncol_all = p.B * D;
+  const int col0 = chunk * FCOLS;
+  const int ncols = min(FCOLS, ncol_all - col0);
+  const int kbase = kt * BNK, k0w = kbase + 32 * w, j = k0w + m;
+  const float a2 = (j < T) ? p.alpha[(size_t)h * p.tab_stride + j] * kLog2e : kNegInf;
+  const float* rho = p.rho + (size_t)h * p.tab_stride;
+
+  f32x16 dv[FCOLS / 32];
+#pragma unroll
+  for (int cb = 0; cb < FCOLS / 32; ++cb) dv[cb] = f32x16{};
+
+  const int n_steps = (T - kbase + BMQ - 1) / BMQ;
+  constexpr int NB = (BMQ / 4) * (FCOLS / 8);  // 4x8 blocks per step = 512
+  u32x4 greg[NB / NTH][4];
+  float treg = 0.f;
+  auto gload = [&](int st) {
+    const int i0 = kbase + st * BMQ;
+#pragma unroll
+    for (int x = 0; x < NB / NTH; ++x) {
+      const int blk = t + NTH * x, cg = blk % (FCOLS / 8), rg = blk / (FCOLS / 8);
+      const int col = col0 + cg * 8;
+      const bool ok = cg * 8 < ncols;
+      const int bb = col / D, d = col % D;
+      const bf16* Gb = p.dO + (((size_t)bb * H + h) * T) * D + d;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int i = i0 + 4 * rg + r;
+        greg[x][r] = (ok && i < T) ? *reinterpret_cast<const u32x4*>(Gb + (size_t)i * D) : u32x4{0, 0, 0, 0};
+      }
+    }
+    if (t < BMQ) {
+      const int i = i0 + t;
+      treg = (i < T) ? p.lse[(size_t)h * T + i] * kLog2e : __builtin_huge_valf();
+    } else if (t < BMQ + BMQ + BNK - 1) {
+      const int dd = i0 - kbase - (BNK - 1) + (t - BMQ);
+      treg = (dd >= 0 && dd < T) ? rho[dd] * kLog2e : kNegInf;
+    }
+  };
+  auto sstore = [&]() {
+#pragma unroll
+    for (int x = 0; x < NB / NTH; ++x) {
+      const int blk = t + NTH * x, cg = blk % (FCOLS / 8), rg = blk / (FCOLS / 8);
+      u32x2 cols[8];
+      transpose_4x8(greg[x], cols);
+#pragma unroll
+      for (int c = 0; c < 8; ++c) {
+        const int col = cg * 8 + c;
+        *reinterpret_cast<u32x2*>(sm.gt + col * BMQ + (((rg >> 1) ^ swz_tr(col)) * 8) + (rg & 1) * 4) = cols[c];
+      }
+    }
+    if (t < BMQ) sm.lz[t] = treg;
+    else if (t < BMQ + BMQ + BNK - 1) sm.rw[t - BMQ] = treg;
+  };
+
+  gload(0);
+  sstore();
+  __syncthreads();
+  for (int st = 0; st < n_steps; ++st) {
+    if (st + 1 < n_steps) gload(st + 1);
+    const int i0 = kbase + st * BMQ;
+#pragma unroll
+    for (int qb = 0; qb < BMQ / 32; ++qb) {
+      if (k0w > i0 + 32 * qb) continue;
+#pragma unroll
+      for (int sk = 0; sk < 2; ++sk) {
+        const int qofs = qb * 32 + sk * 16 + hh * 8;   // query offset within the step
+        // window index of distance (i0 + qofs + e) - j is qofs + e - (j - kbase) + BNK - 1;
+        // entries for j > i hold -inf, which masks the future for free.
+        const int rbase = qofs - (32 * w + m) + BNK - 1;
+        float ph[8], pl[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const float pv = __builtin_amdgcn_exp2f(a2 + sm.rw[rbase + e] - sm.lz[qofs + e]);
+          const bf16 hi = (bf16)pv;
+          ph[e] = (float)hi;
+          pl[e] = pv - ph[e];
+        }
+        const bf16x8 ahi = pack8(ph);
+        const bf16x8 alo = pack8(pl);
+        const int ch = 4 * qb + 2 * sk + hh;
+#pragma unroll
+        for (int cb = 0; cb < FCOLS / 32; ++cb) {
+          if (cb * 32 < ncols) {
+            const int col = cb * 32 + m;
+            const bf16x8 bg = *reinterpret_cast<const bf16x8*>(sm.gt + col * BMQ + ((ch ^ swz_tr(col)) * 8));
+            dv[cb] = mfma32(ahi, bg, dv[cb]);
+            dv[cb] = mfma32(alo, bg, dv[cb]);
+          }
+        }
+      }
+    }
+    __syncthreads();
+    if (st + 1 < n_steps) {
+      sstore();
+      __syncthreads();
+    }
+  }
+
+#pragma unroll
+  for (int cb = 0; cb < FCOLS / 32; ++cb) {
+    const int col = col0 + cb * 32 + m;
+    if (cb * 32 >= ncols) continue;
+    const int bb = col / D, d = col % D;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int key = k0w + acc_row(r, hh);
+      if (key < T) p.dv[(((size_t)bb * H + h) * T + key) * D + d] = dv[cb][r];
+    }
+  }
+}
+
+template <int D>
+__global__ __launch_bounds__(NTH, 1) void dkdv_kernel(const BwdParams p) {
+  __shared__ __attribute__((aligned(16))) unsigned char smem[dkdv_smem_bytes<D>()];
+  const int item = blockIdx.x;
+  const int kt = item / p.per_tile;  // key tile 0 has the most queries: heaviest first
+  int rem = item % p.per_tile;
+  const int nd = p.B * p.n_dyn;
+  if (rem < nd) {
+    dkdv_dyn<D>(p, rem / p.n_dyn, p.dyn[rem % p.n_dyn], kt, smem);
+  } else {
+    rem -= nd;
+    dkdv_frz<D>(p, p.frz[rem / p.n_chunks], rem % p.n_chunks, kt, smem);
+  }
+}
+
+// ---------------------------------------------------------------- dQ
+
+template <int D>
+struct DqSmem {
+  bf16 k[BND * D];    // K rows, swz_pi
+  bf16 v[BND * D];    // V rows, swz_pi
+  bf16 kt[D * BND];   // K^T [d][key], swz_tr
+};
+
+template <int D>
+__global__ __launch_bounds__(NTH, 1) void dq_kernel(const BwdParams p) {
+  constexpr int CPR = D / 8;
+  __shared__ __attribute__((aligned(16))) unsigned char smem_raw[sizeof(DqSmem<D>)];
+  DqSmem<D>& sm = *reinterpret_cast<DqSmem<D>*>(smem_raw);
+  const int item = blockIdx.x;
+  const int n_qt = p.n_tiles;
+  const int qt = n_qt - 1 - item / (p.B * p.n_dyn);
+  const int bh = item % (p.B * p.n_dyn);
+  const int b = bh / p.n_dyn, h = p.dyn[bh % p.n_dyn];
+  const int t = threadIdx.x, lane = lane_id(), w = wave_id();
+  const int m = lane & 31, hh = lane >> 5;
+  const int T = p.T;
+  const size_t head = ((size_t)b * p.H + h) * (size_t)T;
+  const bf16* K = p.k + head * D;
+  const bf16* V = p.v + head * D;
+  const int i0w = qt * BMD + 32 * w, i = i0w + m;
+
+  bf16x8 qf[D / 16], gf[D / 16];
+#pragma unroll
+  for (int kk = 0; kk < D / 16; ++kk) {
+    const size_t off = (head + i) * D + kk * 16 + hh * 8;
+    qf[kk] = (i < T) ? *reinterpret_cast<const bf16x8*>(p.q + off) : bf16x8{};
+    gf[kk] = (i < T) ? *reinterpret_cast<const bf16x8*>(p.dO + off) : bf16x8{};
+  }
+  const float lse2 = (i < T) ? p.lse[head + i] * kLog2e : __builtin_huge_valf();
+  const float dlt = (i < T) ? p.delta[head + i] : 0.f;
+  f32x16 acc[D / 32];
+#pragma unroll
+  for (int db = 0; db < D / 32; ++db) acc[db] = f32x16{};
+
+  const int n_kt = min(2 * qt + 2, (T + BND - 1) / BND);
+  u32x4 kreg[4], vreg[4];
+  auto gload = [&](int J) {
+    const int j0 = J * BND;
+    if (t < (BND / 4) * CPR) {
+      const int cg = t % CPR, rg = t / CPR;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int key = j0 + 4 * rg + r;
+        kreg[r] = (key < T) ? *reinterpret_cast<const u32x4*>(K + (size_t)key * D + cg * 8) : u32x4{0, 0, 0, 0};
+        vreg[r] = (key < T) ? *reinterpret_cast<const u32x4*>(V + (size_t)key * D + cg * 8) : u32x4{0, 0, 0, 0};
+      }
+    }
+  };
+  auto sstore = [&]() {
+    if (t < (BND / 4) * CPR) {
+      const int cg = t % CPR, rg = t / CPR;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int row = 4 * rg + r;
+        *reinterpret_cast<u32x4*>(sm.k + row * D + ((cg ^ swz_pi(row)) * 8)) = kreg[r];
+        *reinterpret_cast<u32x4*>(sm.v + row * D + ((cg ^ swz_pi(row)) * 8)) = vreg[r];
+      }
+      u32x2 cols[8];
+      transpose_4x8(kreg, cols);
+#pragma unroll
+      for (int c = 0; c < 8; ++c) {
+        const int d = cg * 8 + c;
+        *reinterpret_cast<u32x2*>(sm.kt + d * BND + (((rg >> 1) ^ swz_tr(d)) * 8) + (rg & 1) * 4) = cols[c];
+      }
+    }
+  };
+
+  gload(0);
+  sstore();
+  __syncthreads();
+  for (int J = 0; J < n_kt; ++J) {
+    if (J + 1 < n_kt) gload(J + 1);
+    const int j0 = J * BND;
+    if (j0 <= i0w) {
+      f32x16 s[2], dp[2];
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+        s[kb] = f32x16{};
+        dp[kb] = f32x16{};
+        const int krow = kb * 32 + perm_rows(m);
+#pragma unroll
+        for (int kk = 0; kk < D / 16; ++kk) {
+          const int ch = 2 * kk + hh;
+          const bf16x8 ak = *reinterpret_cast<const bf16x8*>(sm.k + krow * D + ((ch ^ swz_pi(krow)) * 8));
+          s[kb] = mfma32(ak, qf[kk], s[kb]);
+        }
+#pragma unroll
+        for (int kk = 0; kk < D / 16; ++kk) {
+          const int ch = 2 * kk + hh;
+          const bf16x8 av = *reinterpret_cast<const bf16x8*>(sm.v + krow * D + ((ch ^ swz_pi(krow)) * 8));
+          dp[kb] = mfma32(av, gf[kk], dp[kb]);
+        }
+      }
+      const bool diag = (j0 + BND - 1 > i0w);
+      bf16x8 dsb[4];
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+        float dsr[16];
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          float pv = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kb][r], p.c, -lse2));
+          if (diag && j0 + kb * 32 + acc_pos(r, hh) > i) pv = 0.f;
+          dsr[r] = pv * (dp[kb][r] - dlt);
+        }
+        dsb[2 * kb] = pack8(dsr);
+        dsb[2 * kb + 1] = pack8(dsr + 8);
+      }
+#pragma unroll
+      for (int db = 0; db < D / 32; ++db) {
+        const int d = db * 32 + m;
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) {
+          const int ch = 2 * ks + hh;
+          const bf16x8 a = *reinterpret_cast<const bf16x8*>(sm.kt + d * BND + ((ch ^ swz_tr(d)) * 8));
+          acc[db] = mfma32(a, dsb[ks], acc[db]);
+        }
+      }
+    }
+    __syncthreads();
+    if (J + 1 < n_kt) {
+      sstore();
+      __syncthreads();
+    }
+  }
+
+  if (i < T) {
+    float* out = p.dq + (head + i) * D;
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int d = db * 32 + acc_row(4 * g, hh);
+        f32x4 v4;
+        v4[0] = acc[db][4 * g] * p.scale;
+        v4[1] = acc[db][4 * g + 1] * p.scale;
+        v4[2] = acc[db][4 * g + 2] * p.scale;
+        v4[3] = acc[db][4 * g + 3] * p.scale;
+        *reinterpret_cast<f32x4*>(out + d) = v4;
+      }
+  }
+}
+
+BwdParams make_params(const AttnArgs& a, const void* q, const void* k, const void* v,
+                      const void* dO, const float* lse, const float* delta, const float* alpha,
+                      const float* rho, float* dq, float* dk, float* dv) {
+  BwdParams p;
+  p.q = static_cast<const bf16*>(q);
+  p.k = static_cast<const bf16*>(k);
+  p.v = static_cast<const bf16*>(v);
+  p.dO = static_cast<const bf16*>(dO);
+  p.lse = lse;
+  p.delta = delta;
+  p.alpha = alpha;
+  p.rho = rho;
+  p.dq = dq;
+  p.dk = dk;
+  p.dv = dv;
+  p.tab_stride = a.tab_stride;
+  p.B = a.B;
+  p.H = a.H;
+  p.T = a.T;
+  p.c = a.scale * kLog2e;
+  p.scale = a.scale;
+  p.n_dyn = a.heads.n_dyn;
+  p.n_frz = a.heads.n_frz;
+  for (int x = 0; x < kMaxHeads; ++x) {
+    p.dyn[x] = a.heads.dyn[x];
+    p.frz[x] = a.heads.frz[x];
+  }
+  return p;
+}
+
+}  // namespace
+
+hipError_t launch_delta(const AttnArgs& a, const void* o, const void* dO, float* delta,
+                        hipStream_t s) {
+  if (a.heads.n_dyn == 0) return hipSuccess;
+  DeltaParams p;
+  p.o = o;
+  p.dO = dO;
+  p.delta = delta;
+  p.H = a.H;
+  p.T = a.T;
+  p.D = a.D;
+  p.n_dyn = a.heads.n_dyn;
+  p.n_rows = a.B * a.heads.n_dyn * a.T;
+  p.bf16 = a.bf16;
+  for (int x = 0; x < kMaxHeads; ++x) p.dyn[x] = a.heads.dyn[x];
+  prof_begin("bwd_delta", s);
+  hipLaunchKernelGGL(bwd_delta_kernel, dim3((p.n_rows + 31) / 32), dim3(256), 0, s, p);
+  prof_end(s);
+  return hipGetLastError();
+}
+
+hipError_t launch_bwd_bf16(const AttnArgs& a, const void* q, const void* k, const void* v,
+                           const void* o, const void* dO, const float* lse,
+                           const float* alpha, const float* rho, float* dq, float* dk,
+                           float* dv, float* delta, hipStream_t s) {
+  hipError_t e = launch_delta(a, o, dO, delta, s);
+  if (e != hipSuccess) return e;
+  BwdParams p = make_params(a, q, k, v, dO, lse, delta, alpha, rho, dq, dk, dv);
+  p.n_chunks = (a.B * a.D + FCOLS - 1) / FCOLS;
+  p.per_tile = a.B * p.n_dyn + p.n_frz * p.n_chunks;
+  p.n_tiles = (a.T + BNK - 1) / BNK;
+  const int n_items = p.n_tiles * p.per_tile;
+  if (n_items > 0) {
+    prof_begin("dkdv", s);
+    if (a.D == 64)
+      hipLaunchKernelGGL(dkdv_kernel<64>, dim3(n_items), dim3(NTH), 0, s, p);
+    else
+      hipLaunchKernelGGL(dkdv_kernel<128>, dim3(n_items), dim3(NTH), 0, s, p);
+    prof_end(s);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+  }
+  if (p.n_dyn == 0) return hipSuccess;
+  p.n_tiles = (a.T + BMD - 1) / BMD;
+  const int n_dq = p.n_tiles * a.B * p.n_dyn;
+  prof_begin("dq", s);
+  if (a.D == 64)
+    hipLaunchKernelGGL(dq_kernel<64>, dim3(n_dq), dim3(NTH), 0, s, p);
+  else
+    hipLaunchKernelGGL(dq_kernel<128>, dim3(n_dq), dim3(NTH), 0, s, p);
+  prof_end(s);
+  return hipGetLastError();
+}
+
+}  // namespace saf

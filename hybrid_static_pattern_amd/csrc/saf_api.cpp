@@ -1,0 +1,293 @@
+// libsaf C ABI: argument validation, head lists, workspace layout and kernel dispatch.
+// The entry points and their contracts are declared in include/saf.h.
+#include "saf.h"
+
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <numeric>
+#include <string>
+#include <vector>
+
+#include "saf_internal.h"
+
+namespace {
+
+thread_local std::string g_err;
+
+saf_status fail(saf_status st, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
+saf_status fail(saf_status st, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_err = buf;
+  return st;
+}
+
+saf_status hip_fail(hipError_t e, const char* where) {
+  return fail(SAF_EHIP, "%s: %s", where, hipGetErrorString(e));
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+size_t align256(size_t x) { return (x + 255) & ~static_cast<size_t>(255); }
+
+// ---------------------------------------------------------------- timing log
+
+struct ProfRec {
+  const char* name;
+  hipEvent_t start, stop;
+};
+
+struct ProfState {
+  bool on = false;
+  std::vector<hipEvent_t> pool;
+  std::vector<ProfRec> recs;
+  static constexpr size_t kCap = 4096;
+
+  hipEvent_t take() {
+    if (!pool.empty()) {
+      hipEvent_t e = pool.back();
+      pool.pop_back();
+      return e;
+    }
+    hipEvent_t e = nullptr;
+    if (hipEventCreate(&e) != hipSuccess) return nullptr;
+    return e;
+  }
+  void recycle() {
+    for (auto& r : recs) {
+      pool.push_back(r.start);
+      pool.push_back(r.stop);
+    }
+    recs.clear();
+  }
+  ~ProfState() {
+    recycle();
+    for (hipEvent_t e : pool) (void)hipEventDestroy(e);
+  }
+};
+
+thread_local ProfState g_prof;
+
+saf_status validate_attn(const saf_attn_desc* d, saf::AttnArgs* a) {
+  if (!d) return fail(SAF_EINVAL, "desc is NULL");
+  if (d->B < 1 || d->H < 1 || d->T < 1)
+    return fail(SAF_EINVAL, "B, H, T must be >= 1 (got %d, %d, %d)", d->B, d->H, d->T);
+  if (d->D != 64 && d->D != 128) return fail(SAF_EUNSUPPORTED, "D must be 64 or 128 (got %d)", d->D);
+  if (d->H > saf::kMaxHeads) return fail(SAF_EUNSUPPORTED, "H must be <= %d (got %d)", saf::kMaxHeads, d->H);
+  if (d->io_dtype != SAF_FP32 && d->io_dtype != SAF_BF16) return fail(SAF_EINVAL, "unknown io_dtype %d", (int)d->io_dtype);
+  if (d->grad_dtype != SAF_FP32)
+    return fail(SAF_EUNSUPPORTED, "grad_dtype must be SAF_FP32 (float32 gradients)");
+  if (!(d->scale > 0.f) || !std::isfinite(d->scale)) return fail(SAF_EINVAL, "scale must be finite and > 0");
+  if (!d->frozen_mask) return fail(SAF_EINVAL, "frozen_mask is NULL");
+  if ((int64_t)d->B * d->H * d->T > (int64_t)1 << 31)
+    return fail(SAF_EUNSUPPORTED, "B*H*T must be <= 2^31");
+  a->B = d->B;
+  a->H = d->H;
+  a->T = d->T;
+  a->D = d->D;
+  a->bf16 = d->io_dtype == SAF_BF16;
+  a->scale = d->scale;
+  a->tab_stride = d->tab_stride;
+  a->heads.n_dyn = a->heads.n_frz = 0;
+  std::memset(a->heads.dyn, 0, sizeof(a->heads.dyn));
+  std::memset(a->heads.frz, 0, sizeof(a->heads.frz));
+  for (int h = 0; h < d->H; ++h) {
+    if (d->frozen_mask[h]) a->heads.frz[a->heads.n_frz++] = (uint8_t)h;
+    else a->heads.dyn[a->heads.n_dyn++] = (uint8_t)h;
+  }
+  if (a->heads.n_frz > 0 && d->tab_stride < d->T)
+    return fail(SAF_EINVAL, "tab_stride (%d) must be >= T (%d)", d->tab_stride, d->T);
+  return SAF_OK;
+}
+
+saf_status check_ptr(const void* p, bool required, const char* name) {
+  if (!p) return required ? fail(SAF_EINVAL, "%s is NULL", name) : SAF_OK;
+  if (!aligned16(p)) return fail(SAF_EINVAL, "%s is not 16-byte aligned", name);
+  return SAF_OK;
+}
+
+#define SAF_TRY(x)                       \
+  do {                                   \
+    saf_status _st = (x);                \
+    if (_st != SAF_OK) return _st;       \
+  } while (0)
+
+}  // namespace
+
+namespace saf {
+
+void prof_begin(const char* name, hipStream_t s) {
+  if (!g_prof.on || g_prof.recs.size() >= ProfState::kCap) return;
+  ProfRec r{name, g_prof.take(), g_prof.take()};
+  if (!r.start || !r.stop) return;
+  (void)hipEventRecord(r.start, s);
+  g_prof.recs.push_back(r);
+}
+
+void prof_end(hipStream_t s) {
+  if (!g_prof.on || g_prof.recs.empty()) return;
+  (void)hipEventRecord(g_prof.recs.back().stop, s);
+}
+
+}  // namespace saf
+
+extern "C" {
+
+saf_status saf_attn_fwd(const saf_attn_desc* desc, const void* q, const void* k, const void* v,
+                        const float* alpha, const float* rho, void* o, float* lse, void* stream) {
+  saf::AttnArgs a;
+  SAF_TRY(validate_attn(desc, &a));
+  const bool any_dyn = a.heads.n_dyn > 0, any_frz = a.heads.n_frz > 0;
+  SAF_TRY(check_ptr(q, any_dyn, "q"));
+  SAF_TRY(check_ptr(k, any_dyn, "k"));
+  SAF_TRY(check_ptr(v, true, "v"));
+  SAF_TRY(check_ptr(alpha, any_frz, "alpha"));
+  SAF_TRY(check_ptr(rho, any_frz, "rho"));
+  SAF_TRY(check_ptr(o, true, "o"));
+  SAF_TRY(check_ptr(lse, true, "lse"));
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  (void)hipGetLastError();
+  hipError_t e = saf::launch_frozen_logz(a, alpha, rho, lse, s);
+  if (e != hipSuccess) return hip_fail(e, "frozen_logz launch");
+  e = a.bf16 ? saf::launch_fwd_bf16(a, q, k, v, alpha, rho, o, lse, s)
+             : saf::launch_fwd_fp32(a, q, k, v, alpha, rho, o, lse, s);
+  if (e != hipSuccess) return hip_fail(e, "hybrid forward launch");
+  return SAF_OK;
+}
+
+size_t saf_attn_workspace_size(const saf_attn_desc* desc) {
+  saf::AttnArgs a;
+  if (validate_attn(desc, &a) != SAF_OK) return 0;
+  return align256((size_t)a.B * a.H * a.T * sizeof(float));
+}
+
+saf_status saf_attn_bwd(const saf_attn_desc* desc, const void* q, const void* k, const void* v,
+                        const void* o, const void* dO, const float* lse, const float* alpha,
+                        const float* rho, void* dq, void* dk, void* dv, void* workspace,
+                        size_t ws_bytes, void* stream) {
+  saf::AttnArgs a;
+  SAF_TRY(validate_attn(desc, &a));
+  const bool any_dyn = a.heads.n_dyn > 0, any_frz = a.heads.n_frz > 0;
+  SAF_TRY(check_ptr(q, any_dyn, "q"));
+  SAF_TRY(check_ptr(k, any_dyn, "k"));
+  SAF_TRY(check_ptr(v, any_dyn, "v"));
+  SAF_TRY(check_ptr(o, any_dyn, "o"));
+  SAF_TRY(check_ptr(dO, true, "dO"));
+  SAF_TRY(check_ptr(lse, true, "lse"));
+  SAF_TRY(check_ptr(alpha, any_frz, "alpha"));
+  SAF_TRY(check_ptr(rho, any_frz, "rho"));
+  SAF_TRY(check_ptr(dq, any_dyn, "dq"));
+  SAF_TRY(check_ptr(dk, any_dyn, "dk"));
+  SAF_TRY(check_ptr(dv, true, "dv"));
+  const size_t need = saf_attn_workspace_size(desc);
+  SAF_TRY(check_ptr(workspace, need > 0, "workspace"));
+  if (ws_bytes < need) return fail(SAF_EWORKSPACE, "workspace has %zu bytes, needs %zu", ws_bytes, need);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  (void)hipGetLastError();
+  float* delta = static_cast<float*>(workspace);
+  hipError_t e = a.bf16 ? saf::launch_bwd_bf16(a, q, k, v, o, dO, lse, alpha, rho, static_cast<float*>(dq),
+                                               static_cast<float*>(dk), static_cast<float*>(dv), delta, s)
+                        : saf::launch_bwd_fp32(a, q, k, v, o, dO, lse, alpha, rho, static_cast<float*>(dq),
+                                               static_cast<float*>(dk), static_cast<float*>(dv), delta, s);
+  if (e != hipSuccess) return hip_fail(e, "hybrid backward launch");
+  return SAF_OK;
+}
+
+static saf_status validate_var(const saf_var_desc* d, saf::VarArgs* a) {
+  if (!d) return fail(SAF_EINVAL, "desc is NULL");
+  if (d->N < 2) return fail(SAF_EINVAL, "N must be >= 2 (Eq. (1) divides by N - 1), got %d", d->N);
+  if (d->H < 1 || d->T < 1) return fail(SAF_EINVAL, "H and T must be >= 1 (got %d, %d)", d->H, d->T);
+  if (d->D != 64 && d->D != 128) return fail(SAF_EUNSUPPORTED, "D must be 64 or 128 (got %d)", d->D);
+  if (d->H > saf::kMaxHeads) return fail(SAF_EUNSUPPORTED, "H must be <= %d (got %d)", saf::kMaxHeads, d->H);
+  if (d->io_dtype != SAF_BF16) return fail(SAF_EUNSUPPORTED, "saf_var_score implements bf16 inputs only");
+  if (!(d->scale > 0.f) || !std::isfinite(d->scale)) return fail(SAF_EINVAL, "scale must be finite and > 0");
+  if ((int64_t)d->N * d->H * d->T > (int64_t)1 << 31) return fail(SAF_EUNSUPPORTED, "N*H*T must be <= 2^31");
+  a->N = d->N;
+  a->H = d->H;
+  a->T = d->T;
+  a->D = d->D;
+  a->bf16 = true;
+  a->scale = d->scale;
+  return SAF_OK;
+}
+
+size_t saf_var_workspace_size(const saf_var_desc* desc) {
+  saf::VarArgs a;
+  if (validate_var(desc, &a) != SAF_OK) return 0;
+  return saf::var_workspace_bytes(a);
+}
+
+saf_status saf_var_score(const saf_var_desc* desc, const void* q, const void* k, float* a_hat,
+                         double* s_var, int32_t* rank, void* workspace, size_t ws_bytes,
+                         void* stream) {
+  saf::VarArgs a;
+  SAF_TRY(validate_var(desc, &a));
+  SAF_TRY(check_ptr(q, true, "q"));
+  SAF_TRY(check_ptr(k, true, "k"));
+  SAF_TRY(check_ptr(a_hat, true, "a_hat"));
+  SAF_TRY(check_ptr(s_var, true, "s_var"));
+  SAF_TRY(check_ptr(rank, true, "rank"));
+  SAF_TRY(check_ptr(workspace, true, "workspace"));
+  const size_t need = saf::var_workspace_bytes(a);
+  if (ws_bytes < need) return fail(SAF_EWORKSPACE, "workspace has %zu bytes, needs %zu", ws_bytes, need);
+  (void)hipGetLastError();
+  hipError_t e = saf::launch_var_score(a, q, k, a_hat, s_var, rank, workspace, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "var_score launch");
+  return SAF_OK;
+}
+
+int32_t saf_select_heads(const double* s_var_all, int32_t n_heads, double r, int32_t* out) {
+  if (!s_var_all || !out || n_heads < 1 || !(r >= 0.0 && r <= 1.0)) {
+    fail(SAF_EINVAL, "saf_select_heads: bad arguments");
+    return -1;
+  }
+  std::vector<int32_t> idx(n_heads);
+  std::iota(idx.begin(), idx.end(), 0);
+  std::stable_sort(idx.begin(), idx.end(), [&](int32_t x, int32_t y) { return s_var_all[x] < s_var_all[y]; });
+  const int32_t kk = (int32_t)std::floor(r * n_heads + 0.5);
+  for (int32_t x = 0; x < kk; ++x) out[x] = idx[x];
+  return kk;
+}
+
+const char* saf_status_string(saf_status st) {
+  switch (st) {
+    case SAF_OK: return "SAF_OK";
+    case SAF_EINVAL: return "SAF_EINVAL: invalid argument";
+    case SAF_EUNSUPPORTED: return "SAF_EUNSUPPORTED: unsupported shape or dtype";
+    case SAF_EWORKSPACE: return "SAF_EWORKSPACE: workspace too small";
+    case SAF_EHIP: return "SAF_EHIP: HIP runtime error";
+  }
+  return "unknown saf_status";
+}
+
+const char* saf_last_error(void) { return g_err.c_str(); }
+
+saf_status saf_prof_enable(int enable) {
+  g_prof.recycle();
+  g_prof.on = enable != 0;
+  return SAF_OK;
+}
+
+int32_t saf_prof_read(const char** names, float* ms, int32_t cap) {
+  int32_t n = 0;
+  for (auto& r : g_prof.recs) {
+    if (n >= cap) break;
+    float t = -1.f;
+    if (hipEventSynchronize(r.stop) == hipSuccess) (void)hipEventElapsedTime(&t, r.start, r.stop);
+    if (names) names[n] = r.name;
+    if (ms) ms[n] = t;
+    ++n;
+  }
+  g_prof.recycle();
+  return n;
+}
+
+}  // extern "C"

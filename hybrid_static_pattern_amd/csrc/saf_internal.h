@@ -1,0 +1,64 @@
+// Internal interface between the C-ABI layer (saf_api.cpp) and the kernel launchers.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace saf {
+
+constexpr int kMaxHeads = 256;
+
+// Head lists of one layer: the dynamic (ordinary) heads and the frozen heads, in
+// ascending head order.
+struct HeadLists {
+  int n_dyn, n_frz;
+  uint8_t dyn[kMaxHeads];
+  uint8_t frz[kMaxHeads];
+};
+
+struct AttnArgs {
+  int B, H, T, D;
+  bool bf16;            // io dtype
+  float scale;
+  int tab_stride;
+  HeadLists heads;
+};
+
+// Kernel timing hooks (saf_prof_*); no-ops unless enabled on this thread.
+void prof_begin(const char* name, hipStream_t s);
+void prof_end(hipStream_t s);
+
+// Forward: logZ prologue for frozen heads, then the hybrid forward.
+hipError_t launch_frozen_logz(const AttnArgs& a, const float* alpha, const float* rho,
+                              float* lse, hipStream_t s);
+hipError_t launch_fwd_bf16(const AttnArgs& a, const void* q, const void* k, const void* v,
+                           const float* alpha, const float* rho, void* o, float* lse,
+                           hipStream_t s);
+hipError_t launch_fwd_fp32(const AttnArgs& a, const void* q, const void* k, const void* v,
+                           const float* alpha, const float* rho, void* o, float* lse,
+                           hipStream_t s);
+
+// delta_i = sum_c dO_ic O_ic for ordinary heads, into `delta` [B, H, T] float32.
+hipError_t launch_delta(const AttnArgs& a, const void* o, const void* dO, float* delta,
+                        hipStream_t s);
+
+// Backward. `delta` is workspace [B, H, T] float32.
+hipError_t launch_bwd_bf16(const AttnArgs& a, const void* q, const void* k, const void* v,
+                           const void* o, const void* dO, const float* lse,
+                           const float* alpha, const float* rho, float* dq, float* dk,
+                           float* dv, float* delta, hipStream_t s);
+hipError_t launch_bwd_fp32(const AttnArgs& a, const void* q, const void* k, const void* v,
+                           const void* o, const void* dO, const float* lse,
+                           const float* alpha, const float* rho, float* dq, float* dk,
+                           float* dv, float* delta, hipStream_t s);
+
+// Calibration score.
+struct VarArgs {
+  int N, H, T, D;
+  bool bf16;
+  float scale;
+};
+size_t var_workspace_bytes(const VarArgs& a);
+hipError_t launch_var_score(const VarArgs& a, const void* q, const void* k, float* a_hat,
+                            double* s_var, int32_t* rank, void* ws, hipStream_t s);
+
+}  // namespace saf

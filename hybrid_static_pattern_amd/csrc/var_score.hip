@@ -1,0 +1,312 @@
+// Calibration variance score, Eq. (1) of "When Can Attention Heads Be Statically Defined?:
+// 中文精读笔记" (part 二.1): for each head, over N calibration sequences,
+//     A_hat = (1/N) sum_n A^(n),   s_var = sum_n ||A^(n) - A_hat||_F^2 / ((N - 1) T^2),
+// A^(n) = softmax_causal(scale Q_n K_n^T); heads are then ranked by ascending s_var.
+//
+// The T x T attention matrices are never stored. Three kernels:
+//   var_lse      per (n, h, 128-query tile): the log2-domain row normaliser of every row
+//                (max and sum over the causal keys, MFMA for Q K^T);
+//   var_welford  per (h, 128-query tile, 64-key tile): loops over n, recomputes the tile
+//                of A^(n) from Q_n, K_n and the row normaliser, and keeps Welford's running
+//                mean and sum of squared deviations per entry in registers; writes the
+//                A_hat tile and the tile's sum of squared deviations;
+//   var_final    sums the per-tile partials in float64, divides by (N - 1) T^2 and ranks
+//                the heads (stable: equal scores keep the lower head index first).
+#include "saf_device.h"
+#include "saf_internal.h"
+
+namespace saf {
+
+namespace {
+
+constexpr int NTH = 256;
+constexpr int BM = 128;
+constexpr int BN = 64;
+
+struct VarParams {
+  const bf16* q;
+  const bf16* k;
+  float* lse2;      // [N, H, T] log2 units
+  float* partial;   // [H, n_it, n_jt]
+  float* a_hat;
+  double* s_var;
+  int32_t* rank;
+  int N, H, T;
+  float c;          // scale * log2(e)
+  int n_it, n_jt;
+};
+
+template <int D>
+struct KTile {
+  bf16 k[BN * D];
+};
+
+template <int D>
+__device__ __forceinline__ void load_k(const bf16* K, int j0, int T, u32x4 (&reg)[BN * D / 8 / NTH]) {
+  constexpr int CPR = D / 8;
+  const int t = threadIdx.x;
+#pragma unroll
+  for (int x = 0; x < BN * CPR / NTH; ++x) {
+    const int c = t + NTH * x, row = c / CPR, cc = c % CPR;
+    reg[x] = (j0 + row < T) ? *reinterpret_cast<const u32x4*>(K + (size_t)(j0 + row) * D + cc * 8)
+                            : u32x4{0, 0, 0, 0};
+  }
+}
+
+template <int D>
+__device__ __forceinline__ void store_k(const u32x4 (&reg)[BN * D / 8 / NTH], bf16* ks) {
+  constexpr int CPR = D / 8;
+  const int t = threadIdx.x;
+#pragma unroll
+  for (int x = 0; x < BN * CPR / NTH; ++x) {
+    const int c = t + NTH * x, row = c / CPR, cc = c % CPR;
+    *reinterpret_cast<u32x4*>(ks + row * D + ((cc ^ swz_pi(row)) * 8)) = reg[x];
+  }
+}
+
+// S^T tile (64 keys x this lane's query) for the 64-key tile held in LDS.
+template <int D>
+__device__ __forceinline__ void scores(const bf16* ks, const bf16x8 (&qf)[D / 16], int m, int hh,
+                                       f32x16 (&s)[2]) {
+#pragma unroll
+  for (int kb = 0; kb < 2; ++kb) {
+    s[kb] = f32x16{};
+    const int krow = kb * 32 + perm_rows(m);
+#pragma unroll
+    for (int kk = 0; kk < D / 16; ++kk) {
+      const int ch = 2 * kk + hh;
+      const bf16x8 a = *reinterpret_cast<const bf16x8*>(ks + krow * D + ((ch ^ swz_pi(krow)) * 8));
+      s[kb] = mfma32(a, qf[kk], s[kb]);
+    }
+  }
+}
+
+template <int D>
+__device__ __forceinline__ void load_q(const bf16* Q, int i, int T, int hh, bf16x8 (&qf)[D / 16]) {
+#pragma unroll
+  for (int kk = 0; kk < D / 16; ++kk)
+    qf[kk] = (i < T) ? *reinterpret_cast<const bf16x8*>(Q + (size_t)i * D + kk * 16 + hh * 8) : bf16x8{};
+}
+
+template <int D>
+__global__ __launch_bounds__(NTH, 2) void var_lse_kernel(const VarParams p) {
+  __shared__ __attribute__((aligned(16))) KTile<D> sm;
+  const int n_qt = p.n_it;
+  const int qt = n_qt - 1 - blockIdx.x / (p.N * p.H);
+  const int nh = blockIdx.x % (p.N * p.H);
+  const int lane = lane_id(), w = wave_id(), m = lane & 31, hh = lane >> 5;
+  const int T = p.T;
+  const size_t head = (size_t)nh * T;
+  const int i0w = qt * BM + 32 * w, i = i0w + m;
+  bf16x8 qf[D / 16];
+  load_q<D>(p.q + head * D, i, T, hh, qf);
+  const bf16* K = p.k + head * D;
+  float mx_run = kNegInf, l = 0.f;
+  const int n_kt = min(2 * qt + 2, (T + BN - 1) / BN);
+  u32x4 reg[BN * D / 8 / NTH];
+  load_k<D>(K, 0, T, reg);
+  store_k<D>(reg, sm.k);
+  __syncthreads();
+  for (int J = 0; J < n_kt; ++J) {
+    if (J + 1 < n_kt) load_k<D>(K, (J + 1) * BN, T, reg);
+    const int j0 = J * BN;
+    if (j0 <= i0w) {
+      f32x16 s[2];
+      scores<D>(sm.k, qf, m, hh, s);
+      const bool diag = j0 + BN - 1 > i0w;
+      float mx = kNegInf;
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          float x = s[kb][r] * p.c;
+          if (diag && j0 + kb * 32 + acc_pos(r, hh) > i) x = kNegInf;
+          s[kb][r] = x;
+          mx = fmaxf(mx, x);
+        }
+      mx = fmaxf(mx, wave_shfl_xor32(mx));
+      const float m_new = fmaxf(mx_run, mx);
+      l *= (mx_run == kNegInf) ? 0.f : __builtin_amdgcn_exp2f(mx_run - m_new);
+      mx_run = m_new;
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) l += __builtin_amdgcn_exp2f(s[kb][r] - mx_run);
+    }
+    __syncthreads();
+    if (J + 1 < n_kt) {
+      store_k<D>(reg, sm.k);
+      __syncthreads();
+    }
+  }
+  const float lt = l + wave_shfl_xor32(l);
+  if (i < T && hh == 0) p.lse2[head + i] = mx_run + __log2f(lt);
+}
+
+template <int D>
+__global__ __launch_bounds__(NTH, 2) void var_welford_kernel(const VarParams p) {
+  __shared__ __attribute__((aligned(16))) KTile<D> sm;
+  __shared__ float red[NTH / 64];
+  const int jt = blockIdx.x % p.n_jt;
+  const int it = (blockIdx.x / p.n_jt) % p.n_it;
+  const int h = blockIdx.x / (p.n_jt * p.n_it);
+  const int t = threadIdx.x, lane = lane_id(), w = wave_id(), m = lane & 31, hh = lane >> 5;
+  const int T = p.T;
+  const int i0 = it * BM, i0w = i0 + 32 * w, i = i0w + m, j0 = jt * BN;
+  float* A = p.a_hat + (size_t)h * T * T;
+  float* part = p.partial + ((size_t)h * p.n_it + it) * p.n_jt + jt;
+
+  if (j0 > i0 + BM - 1) {  // tile above the diagonal: A_hat is 0 there
+    for (int x = t; x < BM * (BN / 4); x += NTH) {
+      const int r = x / (BN / 4), c4 = x % (BN / 4);
+      const int ii = i0 + r, jj = j0 + 4 * c4;
+      if (ii < T) {
+        if ((T & 3) == 0 && jj + 3 < T) {
+          *reinterpret_cast<f32x4*>(A + (size_t)ii * T + jj) = f32x4{0.f, 0.f, 0.f, 0.f};
+        } else {
+          for (int e = 0; e < 4; ++e)
+            if (jj + e < T) A[(size_t)ii * T + jj + e] = 0.f;
+        }
+      }
+    }
+    if (t == 0) *part = 0.f;
+    return;
+  }
+
+  float mean[32], m2[32];
+#pragma unroll
+  for (int x = 0; x < 32; ++x) {
+    mean[x] = 0.f;
+    m2[x] = 0.f;
+  }
+  const bool active = j0 <= i0w;     // wave has causal entries in this tile
+  const bool diag = j0 + BN - 1 > i0w;
+  const size_t nh_stride = (size_t)p.H * T;
+  u32x4 reg[BN * D / 8 / NTH];
+  load_k<D>(p.k + ((size_t)h * T) * D, j0, T, reg);
+  store_k<D>(reg, sm.k);
+  __syncthreads();
+  for (int n = 0; n < p.N; ++n) {
+    const size_t head = (size_t)n * nh_stride + (size_t)h * T;
+    if (n + 1 < p.N) load_k<D>(p.k + (head + nh_stride) * D, j0, T, reg);
+    if (active) {
+      bf16x8 qf[D / 16];
+      load_q<D>(p.q + head * D, i, T, hh, qf);
+      const float l2 = (i < T) ? p.lse2[head + i] : __builtin_huge_valf();
+      f32x16 s[2];
+      scores<D>(sm.k, qf, m, hh, s);
+      const float rn = 1.f / (float)(n + 1);
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          float a = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kb][r], p.c, -l2));
+          if (diag && j0 + kb * 32 + acc_pos(r, hh) > i) a = 0.f;
+          const int x = kb * 16 + r;
+          const float dlt = a - mean[x];
+          mean[x] = __builtin_fmaf(dlt, rn, mean[x]);
+          m2[x] = __builtin_fmaf(dlt, a - mean[x], m2[x]);
+        }
+    }
+    __syncthreads();
+    if (n + 1 < p.N) {
+      store_k<D>(reg, sm.k);
+      __syncthreads();
+    }
+  }
+
+  float sum = 0.f;
+  if (i < T) {
+    float* row = A + (size_t)i * T;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int sk = 0; sk < 2; ++sk) {
+        const int jj = j0 + kb * 32 + sk * 16 + hh * 8;
+        const float* mv = mean + kb * 16 + sk * 8;
+        if ((T & 3) == 0 && jj + 7 < T) {
+          *reinterpret_cast<f32x4*>(row + jj) = f32x4{mv[0], mv[1], mv[2], mv[3]};
+          *reinterpret_cast<f32x4*>(row + jj + 4) = f32x4{mv[4], mv[5], mv[6], mv[7]};
+        } else {
+          for (int e = 0; e < 8; ++e)
+            if (jj + e < T) row[jj + e] = mv[e];
+        }
+      }
+#pragma unroll
+    for (int x = 0; x < 32; ++x) sum += m2[x];
+  }
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) sum += __shfl_xor(sum, o, 64);
+  if (lane == 0) red[w] = sum;
+  __syncthreads();
+  if (t == 0) *part = red[0] + red[1] + red[2] + red[3];
+}
+
+__global__ __launch_bounds__(256) void var_final_kernel(const VarParams p) {
+  __shared__ double sv[kMaxHeads];
+  const int h = threadIdx.x;
+  const int per = p.n_it * p.n_jt;
+  if (h < p.H) {
+    double acc = 0.0;
+    const float* part = p.partial + (size_t)h * per;
+    for (int x = 0; x < per; ++x) acc += (double)part[x];
+    const double v = acc / ((double)(p.N - 1) * (double)p.T * (double)p.T);
+    sv[h] = v;
+    p.s_var[h] = v;
+  }
+  __syncthreads();
+  if (h < p.H) {
+    const double v = sv[h];
+    int pos = 0;
+    for (int x = 0; x < p.H; ++x) pos += (sv[x] < v) || (sv[x] == v && x < h);
+    p.rank[pos] = h;
+  }
+}
+
+size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+}  // namespace
+
+size_t var_workspace_bytes(const VarArgs& a) {
+  const size_t n_it = (a.T + BM - 1) / BM, n_jt = (a.T + BN - 1) / BN;
+  return align256((size_t)a.N * a.H * a.T * sizeof(float)) + align256((size_t)a.H * n_it * n_jt * sizeof(float));
+}
+
+hipError_t launch_var_score(const VarArgs& a, const void* q, const void* k, float* a_hat,
+                            double* s_var, int32_t* rank, void* ws, hipStream_t s) {
+  VarParams p;
+  p.q = static_cast<const bf16*>(q);
+  p.k = static_cast<const bf16*>(k);
+  p.lse2 = static_cast<float*>(ws);
+  p.partial = reinterpret_cast<float*>(static_cast<char*>(ws) + align256((size_t)a.N * a.H * a.T * sizeof(float)));
+  p.a_hat = a_hat;
+  p.s_var = s_var;
+  p.rank = rank;
+  p.N = a.N;
+  p.H = a.H;
+  p.T = a.T;
+  p.c = a.scale * kLog2e;
+  p.n_it = (a.T + BM - 1) / BM;
+  p.n_jt = (a.T + BN - 1) / BN;
+  prof_begin("var_lse", s);
+  if (a.D == 64)
+    hipLaunchKernelGGL(var_lse_kernel<64>, dim3(p.n_it * a.N * a.H), dim3(NTH), 0, s, p);
+  else
+    hipLaunchKernelGGL(var_lse_kernel<128>, dim3(p.n_it * a.N * a.H), dim3(NTH), 0, s, p);
+  prof_end(s);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  prof_begin("var_welford", s);
+  if (a.D == 64)
+    hipLaunchKernelGGL(var_welford_kernel<64>, dim3(p.n_jt * p.n_it * a.H), dim3(NTH), 0, s, p);
+  else
+    hipLaunchKernelGGL(var_welford_kernel<128>, dim3(p.n_jt * p.n_it * a.H), dim3(NTH), 0, s, p);
+  prof_end(s);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  prof_begin("var_final", s);
+  hipLaunchKernelGGL(var_final_kernel, dim3(1), dim3(256), 0, s, p);
+  prof_end(s);
+  return hipGetLastError();
+}
+
+}  // namespace saf

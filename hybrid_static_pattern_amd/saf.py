@@ -1,0 +1,256 @@
+"""Python binding of libsaf (include/saf.h): argument marshalling only.
+
+Every computation runs in the HIP kernels behind the C ABI. torch supplies device
+memory and the current stream; the functions below check shapes, dtypes and devices,
+allocate outputs when none are given, and pass raw pointers through ctypes. If
+libsaf.so has not been built they raise SafError; there is no fallback.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+
+import numpy as np
+import torch
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libsaf.so")
+
+SAF_OK, SAF_EINVAL, SAF_EUNSUPPORTED, SAF_EWORKSPACE, SAF_EHIP = range(5)
+SAF_FP32, SAF_BF16 = 0, 1
+
+# Every symbol include/saf.h declares.
+EXPORTS = (
+    "saf_attn_fwd", "saf_attn_workspace_size", "saf_attn_bwd", "saf_var_workspace_size",
+    "saf_var_score", "saf_select_heads", "saf_status_string", "saf_last_error",
+    "saf_prof_enable", "saf_prof_read",
+)
+
+
+class SafError(RuntimeError):
+    def __init__(self, status: int, msg: str):
+        super().__init__(msg)
+        self.status = status
+
+
+class AttnDesc(ctypes.Structure):
+    _fields_ = [
+        ("B", ctypes.c_int32), ("H", ctypes.c_int32), ("T", ctypes.c_int32), ("D", ctypes.c_int32),
+        ("io_dtype", ctypes.c_int), ("grad_dtype", ctypes.c_int), ("scale", ctypes.c_float),
+        ("frozen_mask", ctypes.POINTER(ctypes.c_uint8)), ("tab_stride", ctypes.c_int32),
+    ]
+
+
+class VarDesc(ctypes.Structure):
+    _fields_ = [
+        ("N", ctypes.c_int32), ("H", ctypes.c_int32), ("T", ctypes.c_int32), ("D", ctypes.c_int32),
+        ("io_dtype", ctypes.c_int), ("scale", ctypes.c_float),
+    ]
+
+
+_lib = None
+
+
+def load(path: str = LIB_PATH) -> ctypes.CDLL:
+    """Loads libsaf.so once and declares the C signatures."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise SafError(SAF_EHIP, f"{path} is missing: build it with hybrid_static_pattern_amd.build_lib")
+    lib = ctypes.CDLL(path)
+    vp, sz, i32 = ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int32
+    pd, pv = ctypes.POINTER(AttnDesc), ctypes.POINTER(VarDesc)
+    lib.saf_attn_fwd.argtypes = [pd, vp, vp, vp, vp, vp, vp, vp, vp]
+    lib.saf_attn_workspace_size.argtypes = [pd]
+    lib.saf_attn_workspace_size.restype = sz
+    lib.saf_attn_bwd.argtypes = [pd, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+    lib.saf_var_workspace_size.argtypes = [pv]
+    lib.saf_var_workspace_size.restype = sz
+    lib.saf_var_score.argtypes = [pv, vp, vp, vp, vp, vp, vp, sz, vp]
+    lib.saf_select_heads.argtypes = [ctypes.POINTER(ctypes.c_double), i32, ctypes.c_double, ctypes.POINTER(i32)]
+    lib.saf_select_heads.restype = i32
+    lib.saf_status_string.argtypes = [ctypes.c_int]
+    lib.saf_status_string.restype = ctypes.c_char_p
+    lib.saf_last_error.restype = ctypes.c_char_p
+    lib.saf_prof_enable.argtypes = [ctypes.c_int]
+    lib.saf_prof_read.argtypes = [ctypes.POINTER(ctypes.c_char_p), ctypes.POINTER(ctypes.c_float), i32]
+    lib.saf_prof_read.restype = i32
+    for fn in ("saf_attn_fwd", "saf_attn_bwd", "saf_var_score", "saf_prof_enable"):
+        getattr(lib, fn).restype = ctypes.c_int
+    _lib = lib
+    return lib
+
+
+def _check(status: int) -> None:
+    if status != SAF_OK:
+        lib = load()
+        raise SafError(status, f"{lib.saf_status_string(status).decode()}: {lib.saf_last_error().decode()}")
+
+
+def _ptr(x):
+    return None if x is None else ctypes.c_void_p(x.data_ptr())
+
+
+def _stream(t: torch.Tensor):
+    return ctypes.c_void_p(torch.cuda.current_stream(t.device).cuda_stream)
+
+
+def _io_dtype(t: torch.Tensor) -> int:
+    if t.dtype == torch.bfloat16:
+        return SAF_BF16
+    if t.dtype == torch.float32:
+        return SAF_FP32
+    raise ValueError(f"unsupported dtype {t.dtype} (bfloat16 or float32)")
+
+
+def _need(t, name, shape=None, dtype=None, device=None):
+    if t is None:
+        return
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+    if dtype is not None and t.dtype != dtype:
+        raise ValueError(f"{name} has dtype {t.dtype}, expected {dtype}")
+    if device is not None and t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
+
+
+def _mask(frozen, H):
+    m = np.ascontiguousarray(np.asarray(frozen, dtype=np.uint8).reshape(-1))
+    if m.size != H:
+        raise ValueError(f"frozen mask has {m.size} entries, expected H={H}")
+    return m
+
+
+def _attn_desc(v, frozen, alpha, scale):
+    B, H, T, D = v.shape
+    mask = _mask(frozen, H)
+    tab = alpha.shape[-1] if alpha is not None else T
+    desc = AttnDesc(B, H, T, D, _io_dtype(v), SAF_FP32,
+                    float(scale if scale is not None else 1.0 / math.sqrt(D)),
+                    mask.ctypes.data_as(ctypes.POINTER(ctypes.c_uint8)), tab)
+    return desc, mask
+
+
+def _tables(alpha, rho, H, T, dev):
+    for name, t in (("alpha", alpha), ("rho", rho)):
+        if t is None:
+            continue
+        _need(t, name, dtype=torch.float32, device=dev)
+        if t.dim() != 2 or t.shape[0] != H or t.shape[1] < T:
+            raise ValueError(f"{name} must be [H, >=T] float32, got {tuple(t.shape)}")
+    if (alpha is None) != (rho is None) or (alpha is not None and alpha.shape != rho.shape):
+        raise ValueError("alpha and rho must both be given with the same shape")
+
+
+def attn_fwd(q, k, v, frozen, alpha=None, rho=None, scale=None, o=None, lse=None):
+    """Hybrid forward (saf_attn_fwd). q, k, v: [B,H,T,D] bf16 or fp32 device tensors (q, k may
+    be None if every head is frozen); frozen: host sequence of H flags; alpha, rho: [H, >=T]
+    float32. Returns (o [B,H,T,D] in v's dtype, lse [B,H,T] float32)."""
+    lib = load()
+    B, H, T, D = v.shape
+    for name, t in (("q", q), ("k", k), ("v", v), ("o", o)):
+        _need(t, name, shape=(B, H, T, D), dtype=v.dtype, device=v.device)
+    _need(lse, "lse", shape=(B, H, T), dtype=torch.float32, device=v.device)
+    _tables(alpha, rho, H, T, v.device)
+    desc, mask = _attn_desc(v, frozen, alpha, scale)
+    if o is None:
+        o = torch.empty_like(v)
+    if lse is None:
+        lse = torch.empty((B, H, T), dtype=torch.float32, device=v.device)
+    _check(lib.saf_attn_fwd(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(rho),
+                            _ptr(o), _ptr(lse), _stream(v)))
+    return o, lse
+
+
+def attn_workspace_size(v, frozen, alpha=None, scale=None) -> int:
+    desc, mask = _attn_desc(v, frozen, alpha, scale)
+    return int(load().saf_attn_workspace_size(ctypes.byref(desc)))
+
+
+def attn_bwd(q, k, v, o, do, lse, frozen, alpha=None, rho=None, scale=None,
+             dq=None, dk=None, dv=None, workspace=None):
+    """Hybrid backward (saf_attn_bwd). Returns (dq, dk, dv), float32 [B,H,T,D]. dq and dk of
+    frozen heads are never written (they keep whatever the given buffers, or zeros, hold)."""
+    lib = load()
+    B, H, T, D = v.shape
+    for name, t in (("q", q), ("k", k), ("v", v), ("o", o), ("do", do)):
+        _need(t, name, shape=(B, H, T, D), dtype=v.dtype, device=v.device)
+    _need(lse, "lse", shape=(B, H, T), dtype=torch.float32, device=v.device)
+    for name, t in (("dq", dq), ("dk", dk), ("dv", dv)):
+        _need(t, name, shape=(B, H, T, D), dtype=torch.float32, device=v.device)
+    _tables(alpha, rho, H, T, v.device)
+    desc, mask = _attn_desc(v, frozen, alpha, scale)
+    need = int(lib.saf_attn_workspace_size(ctypes.byref(desc)))
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=v.device)
+    _need(workspace, "workspace", device=v.device)
+    if dq is None:
+        dq = torch.zeros((B, H, T, D), dtype=torch.float32, device=v.device)
+    if dk is None:
+        dk = torch.zeros((B, H, T, D), dtype=torch.float32, device=v.device)
+    if dv is None:
+        dv = torch.empty((B, H, T, D), dtype=torch.float32, device=v.device)
+    _check(lib.saf_attn_bwd(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(do), _ptr(lse),
+                            _ptr(alpha), _ptr(rho), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(workspace),
+                            workspace.numel() * workspace.element_size(), _stream(v)))
+    return dq, dk, dv
+
+
+def var_workspace_size(N, H, T, D, scale=None) -> int:
+    desc = VarDesc(N, H, T, D, SAF_BF16, float(scale if scale is not None else 1.0 / math.sqrt(D)))
+    return int(load().saf_var_workspace_size(ctypes.byref(desc)))
+
+
+def var_score(q, k, scale=None, a_hat=None, s_var=None, rank=None, workspace=None):
+    """Calibration score (saf_var_score). q, k: [N,H,T,D] bf16 device tensors. Returns
+    (a_hat [H,T,T] float32, s_var [H] float64, rank [H] int32), all on the device."""
+    lib = load()
+    N, H, T, D = q.shape
+    _need(q, "q", dtype=q.dtype)
+    _need(k, "k", shape=(N, H, T, D), dtype=q.dtype, device=q.device)
+    _need(a_hat, "a_hat", shape=(H, T, T), dtype=torch.float32, device=q.device)
+    _need(s_var, "s_var", shape=(H,), dtype=torch.float64, device=q.device)
+    _need(rank, "rank", shape=(H,), dtype=torch.int32, device=q.device)
+    desc = VarDesc(N, H, T, D, _io_dtype(q), float(scale if scale is not None else 1.0 / math.sqrt(D)))
+    need = int(lib.saf_var_workspace_size(ctypes.byref(desc)))
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    if a_hat is None:
+        a_hat = torch.empty((H, T, T), dtype=torch.float32, device=q.device)
+    if s_var is None:
+        s_var = torch.empty((H,), dtype=torch.float64, device=q.device)
+    if rank is None:
+        rank = torch.empty((H,), dtype=torch.int32, device=q.device)
+    _check(lib.saf_var_score(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(a_hat), _ptr(s_var), _ptr(rank),
+                             _ptr(workspace), workspace.numel() * workspace.element_size(), _stream(q)))
+    return a_hat, s_var, rank
+
+
+def select_heads(s_var_all, r: float) -> np.ndarray:
+    """Indices of the k = round(r * n) lowest-scoring heads over all layers (host only)."""
+    s = np.ascontiguousarray(np.asarray(s_var_all, dtype=np.float64).reshape(-1))
+    out = np.zeros(s.size, dtype=np.int32)
+    kk = load().saf_select_heads(s.ctypes.data_as(ctypes.POINTER(ctypes.c_double)), s.size, float(r),
+                                 out.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)))
+    if kk < 0:
+        _check(SAF_EINVAL)
+    return out[:kk].copy()
+
+
+def prof_enable(on: bool = True) -> None:
+    _check(load().saf_prof_enable(1 if on else 0))
+
+
+def prof_read(cap: int = 4096):
+    """(kernel name, milliseconds) for each library launch since the last read; synchronises."""
+    names = (ctypes.c_char_p * cap)()
+    ms = (ctypes.c_float * cap)()
+    n = load().saf_prof_read(names, ms, cap)
+    return [(names[x].decode(), float(ms[x])) for x in range(n)]

@@ -1,0 +1,142 @@
+/*
+ * libsaf: Selective Attention Freezing (SAF) hybrid causal attention for AMD MI355X
+ * (gfx950), as a C ABI over hand-written HIP kernels.
+ *
+ * Citations refer to the web page "When Can Attention Heads Be Statically Defined?:
+ * 中文精读笔记" (reading notes on the SAF paper). Positions are 0-indexed: query i, key j,
+ * distance d = i - j; the page's 1-indexed sums over k = 1..i become j = 0..i.
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ *  - Tensors Q, K, V, O, dO, dQ, dK, dV are [B, H, T, D], contiguous, D fastest.
+ *    lse is [B, H, T] float32. alpha and rho are [H, tab_stride] float32 (row h is used
+ *    only when head h is frozen; entries 0..T-1 are read).
+ *  - Device pointers are HIP device (or managed) memory; `frozen_mask` is HOST memory.
+ *    The caller owns every buffer. The library allocates no device memory and keeps no
+ *    mutable global state apart from a thread-local error string and an optional
+ *    per-thread timing log (saf_prof_*).
+ *  - Every call only enqueues work on `stream` (a hipStream_t; NULL = the null stream)
+ *    and never synchronises. Argument errors return before anything is enqueued.
+ *    A failed launch returns SAF_EHIP; faults during execution surface at the
+ *    caller's next synchronisation.
+ *  - Device pointers must be 16-byte aligned. D must be 64 or 128.
+ *  - Status codes: SAF_EINVAL (bad pointer, size or alignment), SAF_EUNSUPPORTED
+ *    (D or a dtype combination the kernels do not implement), SAF_EWORKSPACE
+ *    (workspace smaller than the matching *_workspace_size), SAF_EHIP (launch error).
+ *    saf_last_error() returns a thread-local description of the last non-OK status.
+ */
+#ifndef SAF_H
+#define SAF_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  SAF_OK = 0,
+  SAF_EINVAL = 1,
+  SAF_EUNSUPPORTED = 2,
+  SAF_EWORKSPACE = 3,
+  SAF_EHIP = 4
+} saf_status;
+
+typedef enum { SAF_FP32 = 0, SAF_BF16 = 1 } saf_dtype;
+
+/* One hybrid attention layer.
+ *  B, H, T, D   batch, heads, sequence length (>= 1), head width (64 or 128).
+ *  io_dtype     storage type of Q, K, V, O and dO (SAF_BF16 or SAF_FP32).
+ *  grad_dtype   storage type of dQ, dK, dV. Only SAF_FP32 is implemented: the frozen-head
+ *               sink column of dV needs it to stay within a 2e-2 absolute error.
+ *  scale        multiplier of Q K^T for ordinary heads (1/sqrt(D) in part 一 of the page);
+ *               frozen-head logits alpha + rho are not scaled (Eq. (3)).
+ *  frozen_mask  HOST array [H]; nonzero marks a frozen (static-pattern) head (the selected
+ *               head set of part 二.1 / Algorithm 1).
+ *  tab_stride   row stride, in elements, of alpha and rho (>= T). */
+typedef struct {
+  int32_t B, H, T, D;
+  saf_dtype io_dtype;
+  saf_dtype grad_dtype;
+  float scale;
+  const uint8_t* frozen_mask;
+  int32_t tab_stride;
+} saf_attn_desc;
+
+/* Hybrid forward (part 一; part 二.3 Eq. (3); part 二.4 and Fig. 2).
+ * Ordinary head h:  O[b,h] = softmax_causal(scale * Q K^T) V,
+ *                   lse[b,h,i] = log sum_{j<=i} exp(scale * q_i . k_j).
+ * Frozen head h:    P(i,j) = exp(alpha[h,j] + rho[h,i-j]) / Z(i) for j <= i, 0 for j > i,
+ *                   Z(i) = sum_{j<=i} exp(alpha[h,j] + rho[h,i-j]);
+ *                   O[b,h] = P V[b,h] with the current V; lse[b,h,i] = log Z(i) for every b.
+ * Q and K slices of frozen heads are never read (Q and K may be NULL when every head is
+ * frozen); alpha and rho may be NULL when no head is frozen. alpha/rho entries must be
+ * finite or -inf, and every row i must keep at least one finite logit alpha(j)+rho(i-j).
+ * O and lse are written for every head. The forward needs no workspace. */
+saf_status saf_attn_fwd(const saf_attn_desc* desc, const void* q, const void* k,
+                        const void* v, const float* alpha, const float* rho, void* o,
+                        float* lse, void* stream);
+
+/* Workspace bytes saf_attn_bwd needs for `desc` (0 on a NULL or invalid descriptor). */
+size_t saf_attn_workspace_size(const saf_attn_desc* desc);
+
+/* Hybrid backward for the upstream gradient dO = dL/dO.
+ * Ordinary heads: dV = A^T dO, dS = A o (dO V^T - rowsum(dO o O)), dQ = scale dS K,
+ *                 dK = scale dS^T Q, with A recomputed from Q, K and the forward's lse.
+ * Frozen heads:   dV = P^T dO only (part 二.4: alpha, rho are fixed buffers without
+ *                 gradient and there is no query or key); lse must hold log Z(i).
+ * o and lse are the forward's outputs for the same inputs. dQ/dK slices of frozen heads
+ * are never written; dV is written for every head. Gradients are float32.
+ * workspace: device memory of at least saf_attn_workspace_size(desc) bytes, caller-owned,
+ * contents need not be initialised and are garbage afterwards. */
+saf_status saf_attn_bwd(const saf_attn_desc* desc, const void* q, const void* k,
+                        const void* v, const void* o, const void* dO, const float* lse,
+                        const float* alpha, const float* rho, void* dq, void* dk,
+                        void* dv, void* workspace, size_t ws_bytes, void* stream);
+
+/* Calibration batch of one layer: N sequences (N >= 2), H heads, length T, width D. */
+typedef struct {
+  int32_t N, H, T, D;
+  saf_dtype io_dtype;
+  float scale;
+} saf_var_desc;
+
+/* Workspace bytes saf_var_score needs for `desc` (0 on a NULL or invalid descriptor). */
+size_t saf_var_workspace_size(const saf_var_desc* desc);
+
+/* Variance score of part 二.1, Eq. (1), for every head of one layer.
+ * q, k:   [N, H, T, D] (io_dtype), the ordinary-attention queries and keys of the N
+ *         calibration sequences.
+ * a_hat:  [H, T, T] float32 output, the mean causal attention (1/N) sum_n A^(n); entries
+ *         with j > i are written as 0.
+ * s_var:  [H] float64 output, sum_n ||A^(n) - A_hat||_F^2 / ((N - 1) T^2).
+ * rank:   [H] int32 output, head indices by ascending s_var; equal scores keep the lower
+ *         head index first.
+ * workspace as for saf_attn_bwd. */
+saf_status saf_var_score(const saf_var_desc* desc, const void* q, const void* k,
+                         float* a_hat, double* s_var, int32_t* rank, void* workspace,
+                         size_t ws_bytes, void* stream);
+
+/* Host-only selection across layers (part 二.1): sorts n_heads scores (all L*H heads of a
+ * model) ascending, ties to the lower index, and writes the first k = floor(r*n + 1/2)
+ * indices to out[0..k-1] (out holds n_heads entries). Returns k, or -1 on bad arguments. */
+int32_t saf_select_heads(const double* s_var_all, int32_t n_heads, double r, int32_t* out);
+
+const char* saf_status_string(saf_status status);
+const char* saf_last_error(void);
+
+/* Optional timing of the library's own kernel launches, for profiling. While enabled on
+ * the calling thread, each kernel the entry points launch is bracketed by a pair of
+ * hipEvents recorded on the launch stream. saf_prof_read synchronises on those events and
+ * copies up to `cap` records (kernel name, milliseconds) in launch order, returning the
+ * number of records; saf_prof_enable(0) drops the log. The events are created once per
+ * thread and reused. */
+saf_status saf_prof_enable(int enable);
+int32_t saf_prof_read(const char** names, float* ms, int32_t cap);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SAF_H */

@@ -1,0 +1,300 @@
+"""GPU parity: the HIP path (through the C ABI) against the float64 CPU oracle on the same
+seeded inputs, element by element, plus the pages' closed forms and the ABI's read/write
+contract. Run on an MI355X with `pytest -m gpu`."""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+from hybrid_static_pattern_amd import inputs
+from oracle import saf_oracle
+from tests.gpu_util import check, dev, down, layer_on_device, oracle_head, up
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def S():
+    from hybrid_static_pattern_amd import saf
+    saf.load()
+    return saf
+
+
+def run(S, L, bwd=True, sentinel=float("nan")):
+    g = layer_on_device(L)
+    fz = L["frozen"]
+    allf = bool(fz.all())
+    q = None if allf else g["q"]
+    k = None if allf else g["k"]
+    o, lse = S.attn_fwd(q, k, g["v"], fz, g["alpha"], g["rho"])
+    res = dict(o=o, lse=lse)
+    if bwd:
+        shape = tuple(g["v"].shape)
+        dq = torch.full(shape, sentinel, dtype=torch.float32, device=dev())
+        dk = torch.full(shape, sentinel, dtype=torch.float32, device=dev())
+        dq, dk, dv = S.attn_bwd(q, k, g["v"], o, g["do"], lse, fz, g["alpha"], g["rho"], dq=dq, dk=dk)
+        res.update(dq=dq, dk=dk, dv=dv)
+    torch.cuda.synchronize()
+    return {key: down(val) for key, val in res.items()}
+
+
+def compare_layer(L, out, bwd=True):
+    scale = 1.0 / math.sqrt(L["D"])
+    dt = L["dtype"]
+    O, lse = saf_oracle.attn_fwd(L["q"], L["k"], L["v"], L["frozen"], L["alpha"], L["rho"], scale)
+    check(out["o"], O, dt, "O")
+    check(out["lse"], lse, dt, "lse", lse=True)
+    if not bwd:
+        return
+    dq, dk, dv = saf_oracle.attn_bwd(L["q"], L["k"], L["v"], L["do"], L["frozen"], L["alpha"], L["rho"], scale)
+    dyn = L["frozen"] == 0
+    if dyn.any():
+        check(out["dq"][:, dyn], dq[:, dyn], dt, "dQ")
+        check(out["dk"][:, dyn], dk[:, dyn], dt, "dK")
+    check(out["dv"], dv, dt, "dV")
+    frz = ~dyn
+    # dQ/dK slices of frozen heads are never written (NaN sentinels survive)
+    assert np.all(np.isnan(out["dq"][:, frz])) and np.all(np.isnan(out["dk"][:, frz]))
+
+
+# ---------------------------------------------------------------- small layers
+
+def test_tiny_fp32_forward(S):
+    """The tiny float32 workload: B=1, H=4 (head 3 frozen), T=256, d_h=64."""
+    L = inputs.make_layer(**inputs.WORKLOADS["tiny_fwd_fp32"])
+    compare_layer(L, run(S, L, bwd=False), bwd=False)
+
+
+@pytest.mark.parametrize("B,H,T,D,frozen", [
+    (1, 3, 150, 128, [2]), (2, 2, 70, 64, [0]), (1, 2, 1, 64, [1]), (2, 2, 33, 64, [0, 1]),
+])
+def test_fp32_forward_backward(S, B, H, T, D, frozen):
+    L = inputs.make_layer(B, H, T, D, dtype="fp32", seed=11, frozen_heads=frozen)
+    compare_layer(L, run(S, L))
+
+
+BF16_CASES = [
+    (2, 4, 300, 64, [1, 3]),      # several tiles, ragged tail
+    (1, 3, 257, 128, [0]),        # ragged; folded columns 128 < 256
+    (3, 2, 130, 128, [1]),        # folded columns 384: two chunks, the second partial
+    (8, 2, 129, 64, [0]),         # folded columns 512: two full chunks
+    (1, 2, 1, 64, [1]),           # T = 1
+    (2, 3, 64, 64, []),           # all ordinary (r = 0)
+    (2, 2, 200, 128, [0, 1]),     # all frozen: q, k are NULL
+    (1, 2, 513, 128, [1]),        # crosses the 512-key boundary of the dK/dV tiles
+]
+
+
+@pytest.mark.parametrize("B,H,T,D,frozen", BF16_CASES)
+def test_bf16_forward_backward(S, B, H, T, D, frozen):
+    L = inputs.make_layer(B, H, T, D, dtype="bf16", seed=7, frozen_heads=frozen)
+    compare_layer(L, run(S, L))
+
+
+# ---------------------------------------------------------------- closed forms on the GPU
+
+def _frozen_layer(B, T, D, dtype, alpha, rho, seed=3):
+    L = inputs.make_layer(B, 1, T, D, dtype=dtype, seed=seed, frozen_heads=[0])
+    L["alpha"] = np.asarray(alpha, np.float32).reshape(1, T)
+    L["rho"] = np.asarray(rho, np.float32).reshape(1, T)
+    return L
+
+
+@pytest.mark.parametrize("dtype", ["fp32", "bf16"])
+def test_identity_pattern(S, dtype):
+    """rho(0) = 0, rho(d >= 1) = -inf: P = I, so O = V and dV = dO."""
+    T = 190
+    rho = np.full(T, -np.inf)
+    rho[0] = 0.0
+    L = _frozen_layer(2, T, 64, dtype, np.random.default_rng(1).standard_normal(T), rho)
+    out = run(S, L)
+    tol = 1e-6 if dtype == "fp32" else 1e-2
+    assert np.max(np.abs(out["o"] - L["v"])) <= tol
+    assert np.max(np.abs(out["dv"] - L["do"])) <= tol
+
+
+@pytest.mark.parametrize("dtype", ["fp32", "bf16"])
+def test_uniform_pattern_is_prefix_mean(S, dtype):
+    """alpha = rho = 0: P(i, j) = 1/(i+1), O = prefix mean, dV = reverse cumsum of dO/(i+1)."""
+    T = 333
+    L = _frozen_layer(1, T, 128, dtype, np.zeros(T), np.zeros(T))
+    out = run(S, L)
+    cnt = np.arange(1, T + 1)[None, None, :, None]
+    check(out["o"], np.cumsum(L["v"].astype(np.float64), 2) / cnt, dtype, "O")
+    ref = np.cumsum((L["do"].astype(np.float64) / cnt)[:, :, ::-1], 2)[:, :, ::-1]
+    check(out["dv"], ref, dtype, "dV")
+
+
+def test_alpha_rho_shift_invariance(S):
+    """alpha + 80 and rho + 80 leave the pattern unchanged (a naive float32 exp overflows)."""
+    L = inputs.make_layer(2, 3, 260, 64, dtype="bf16", seed=5, frozen_heads=[0, 2])
+    base = run(S, L)
+    L2 = dict(L)
+    L2["alpha"] = (L["alpha"] + 80.0).astype(np.float32)
+    L2["rho"] = (L["rho"] + 80.0).astype(np.float32)
+    shifted = run(S, L2)
+    for key in ("o", "dv"):
+        assert np.max(np.abs(shifted[key] - base[key])) <= 2e-2
+    assert np.max(np.abs(shifted["lse"][:, [0, 2]] - base["lse"][:, [0, 2]] - 160.0)) <= 1e-3
+    compare_layer(L2, shifted)
+
+
+def test_frozen_equals_dynamic_rank1(S):
+    """Affine rho(d) = -lam d: the frozen head equals an ordinary head with q_i = e0/scale,
+    k_j = (alpha(j) + lam j) e0 (float32 path)."""
+    T, D, lam = 300, 64, 0.05
+    scale = 1.0 / math.sqrt(D)
+    r = np.random.default_rng(9)
+    alpha = (0.5 * r.standard_normal(T)).astype(np.float32)
+    q = np.zeros((1, 2, T, D), np.float32)
+    q[..., 0] = 1.0 / scale
+    k = np.zeros((1, 2, T, D), np.float32)
+    k[:, :, :, 0] = alpha + lam * np.arange(T)
+    v = r.standard_normal((1, 2, T, D)).astype(np.float32)
+    v[:, 1] = v[:, 0]
+    tabs = np.stack([alpha, alpha]).astype(np.float32)
+    rho = np.stack([-lam * np.arange(T)] * 2).astype(np.float32)
+    o, lse = S.attn_fwd(up(q, "fp32"), up(k, "fp32"), up(v, "fp32"), [0, 1],
+                        torch.from_numpy(tabs).to(dev()), torch.from_numpy(rho).to(dev()))
+    o = down(o)
+    rel = np.max(np.abs(o[:, 0] - o[:, 1])) / np.max(np.abs(o[:, 0]))
+    assert rel <= 1e-5
+
+
+# ---------------------------------------------------------------- read/write contract
+
+def test_frozen_qk_never_read(S):
+    """NaN in the q, k slices of frozen heads changes nothing."""
+    L = inputs.make_layer(2, 3, 150, 64, dtype="bf16", seed=13, frozen_heads=[1])
+    a = run(S, L)
+    L2 = dict(L)
+    for key in ("q", "k"):
+        x = L[key].copy()
+        x[:, 1] = np.nan
+        L2[key] = x
+    b = run(S, L2)
+    for key in ("o", "lse", "dv"):
+        assert np.array_equal(a[key], b[key]), key
+    dyn = [0, 2]
+    for key in ("dq", "dk"):
+        assert np.array_equal(a[key][:, dyn], b[key][:, dyn]), key
+
+
+def test_frozen_grads_untouched_and_deterministic(S):
+    L = inputs.make_layer(1, 4, 200, 128, dtype="bf16", seed=17, frozen_heads=[0, 3])
+    a = run(S, L, sentinel=12345.0)
+    assert np.all(a["dq"][:, [0, 3]] == 12345.0) and np.all(a["dk"][:, [0, 3]] == 12345.0)
+    b = run(S, L, sentinel=12345.0)
+    for key in a:
+        assert np.array_equal(a[key], b[key]), key  # no atomics: bit-identical reruns
+
+
+def test_bad_workspace_is_rejected(S):
+    L = inputs.make_layer(1, 2, 64, 64, dtype="bf16", seed=1, frozen_heads=[1])
+    g = layer_on_device(L)
+    o, lse = S.attn_fwd(g["q"], g["k"], g["v"], L["frozen"], g["alpha"], g["rho"])
+    ws = torch.empty(16, dtype=torch.uint8, device=dev())
+    with pytest.raises(S.SafError) as e:
+        S.attn_bwd(g["q"], g["k"], g["v"], o, g["do"], lse, L["frozen"], g["alpha"], g["rho"], workspace=ws)
+    assert e.value.status == S.SAF_EWORKSPACE
+
+
+# ---------------------------------------------------------------- calibration score
+
+def _check_var(S, C, heads=None):
+    scale = 1.0 / math.sqrt(C["D"])
+    a_hat, s_var, rank = S.var_score(up(C["q"], "bf16"), up(C["k"], "bf16"))
+    torch.cuda.synchronize()
+    a_hat, s_var, rank = a_hat.cpu().numpy(), s_var.cpu().numpy(), rank.cpu().numpy()
+    H = C["H"]
+    heads = range(H) if heads is None else heads
+    ref_s = {}
+    for h in heads:
+        A_hat, sv, _ = saf_oracle.var_score(C["q"][:, h:h + 1], C["k"][:, h:h + 1], scale)
+        assert np.max(np.abs(a_hat[h] - A_hat[0])) <= 1e-5, h
+        assert abs(s_var[h] - sv[0]) <= 1e-3 * sv[0], (h, s_var[h], sv[0])
+        ref_s[h] = sv[0]
+    # the ranking is the stable ascending order of the scores
+    assert list(rank) == list(np.argsort(s_var, kind="stable"))
+    return ref_s, s_var, rank
+
+
+def test_var_score_small(S):
+    C = inputs.make_calibration(6, 4, 200, 64, seed=21)
+    ref, s_var, rank = _check_var(S, C)
+    assert list(rank) == list(saf_oracle.rank_heads([ref[h] for h in range(4)]))
+
+
+def test_var_score_d128_ragged(S):
+    C = inputs.make_calibration(3, 2, 67, 128, seed=22)
+    _check_var(S, C)
+
+
+def test_var_score_identical_sequences(S):
+    C = inputs.make_calibration(2, 3, 96, 64, seed=23)
+    for key in ("q", "k"):
+        C[key] = np.repeat(C[key][:1], 4, axis=0)
+    C["N"] = 4
+    a_hat, s_var, rank = S.var_score(up(C["q"], "bf16"), up(C["k"], "bf16"))
+    assert np.all(s_var.cpu().numpy() < 1e-12)
+
+
+# ---------------------------------------------------------------- full-size workloads, sampled
+
+def _full(S, name, heads, bwd=True, n_frozen=None):
+    spec = dict(inputs.WORKLOADS[name])
+    if n_frozen is not None:
+        spec["n_frozen"] = n_frozen
+    L = inputs.make_layer(**spec)
+    out = run(S, L, bwd=bwd)
+    scale = 1.0 / math.sqrt(L["D"])
+    dt = L["dtype"]
+    for b, hsel in heads:
+        h = hsel(L["frozen"])
+        O, lse, dq, dk, dv = oracle_head(L, b, h, scale)
+        check(out["o"][b, h], O, dt, f"O[{b},{h}]")
+        check(out["lse"][b, h], lse, dt, f"lse[{b},{h}]", lse=True)
+        if bwd:
+            check(out["dv"][b, h], dv, dt, f"dV[{b},{h}]")
+            if not L["frozen"][h]:
+                check(out["dq"][b, h], dq, dt, f"dQ[{b},{h}]")
+                check(out["dk"][b, h], dk, dt, f"dK[{b},{h}]")
+
+
+def first_frozen(fz):
+    return int(np.flatnonzero(fz)[0])
+
+
+def last_dynamic(fz):
+    return int(np.flatnonzero(fz == 0)[-1])
+
+
+def test_full_124m_forward(S):
+    _full(S, "l124m_fwd", [(7, first_frozen), (3, last_dynamic)], bwd=False)
+
+
+def test_full_124m_forward_backward(S):
+    _full(S, "l124m_fwdbwd", [(0, first_frozen), (5, last_dynamic)])
+
+
+def test_full_124m_all_dynamic(S):
+    _full(S, "l124m_fwdbwd", [(2, last_dynamic)], n_frozen=0)
+
+
+def test_full_1b_forward_backward(S):
+    _full(S, "l1b_fwdbwd", [(1, first_frozen), (0, last_dynamic)])
+
+
+def test_full_1b_half_frozen(S):
+    _full(S, "l1b_fwdbwd", [(0, first_frozen)], n_frozen=8)
+
+
+def test_full_calibration_sampled(S):
+    C = inputs.make_calibration(**inputs.CALIBRATION)
+    tau = C["tau"]
+    heads = [int(np.argmin(tau)), int(np.argmax(tau)), 5]
+    ref, s_var, rank = _check_var(S, C, heads=heads)
+    # sharper heads (small temperature) score higher: the sampled order must agree
+    order = sorted(heads, key=lambda h: ref[h])
+    assert [h for h in rank if h in heads] == order
