@@ -1,6 +1,7 @@
 """Helpers shared by the GPU tests: device upload, the accuracy bars, and oracle runs on
 sampled heads. The bars are the ones the hot path is held to:
-  float32 storage: normwise relative error max|g - o| / max|o| <= 1e-5 per tensor;
+  float32 storage: normwise relative error max|g - o| / max|o| <= 1e-5 per tensor
+                   (max|o| replaced by 1 for a tensor that is identically zero);
   bf16 storage:    max |g - o| <= 2e-2 and mean |g - o| <= 2e-3 on values (outputs and
                    float32 gradients), against the float64 oracle on the same inputs.
 """
@@ -40,7 +41,10 @@ def check(gpu: np.ndarray, ref: np.ndarray, dtype: str, name: str, lse: bool = F
         assert err.max() <= LSE_ABS, f"{name}: max abs err {err.max():.3e}"
         return err.max()
     if dtype == "fp32":
-        rel = err.max() / max(np.abs(ref).max(), 1e-30)
+        # A tensor that vanishes identically (dQ, dK at T = 1, where the softmax over a single
+        # key has zero gradient) is held to the same 1e-5 against unit scale.
+        scale = np.abs(ref).max()
+        rel = err.max() / (scale if scale > 0 else 1.0)
         assert rel <= FP32_REL, f"{name}: normwise rel err {rel:.3e}"
         return rel
     assert err.max() <= BF16_MAX, f"{name}: max abs err {err.max():.3e}"
