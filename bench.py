@@ -86,6 +86,9 @@ def main():
     ap.add_argument("--workload", default="l1b_fwdbwd")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-sweep", action="store_true", help="skip the r=0 / r=50%% timings")
+    ap.add_argument("--calib-copy-mib", type=int, default=0,
+                    help="first run one plain device copy of this many MiB (a known-size reference "
+                         "for the FETCH_SIZE / WRITE_SIZE counters)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU: the layer's heads are independent and this build has no "
@@ -97,6 +100,14 @@ def main():
     from hybrid_static_pattern_amd import inputs, saf
 
     saf.load()
+    if args.calib_copy_mib:
+        n = args.calib_copy_mib * (1 << 20) // 4
+        src = torch.ones(n, dtype=torch.float32, device="cuda:0")
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
     spec = dict(inputs.WORKLOADS[args.workload])
     L = inputs.make_layer(**spec)
     B, H, T, D = L["B"], L["H"], L["T"], L["D"]

@@ -20,7 +20,9 @@
 //           bf16 high and low part (two MFMAs) so the fp32 dV keeps ~16 bits of P;
 //   dq          ordinary (b, h, 128-query tile), keys from 0 to the diagonal, the query
 //           as the lane index (as in the forward): dQ = scale * sum_J dS K_J.
-// The split into a key-stationary and a query-stationary kernel recomputes S and dP once
+// Q/dO (dK/dV kernel) and K/V (dQ kernel) tiles go from HBM straight into double-buffered
+// LDS, one barrier per step; the transposed operands (dO^T, Q^T, K^T) are read from the
+// same row-major tiles with ds_read_b64_tr_b16. The split into a key-stationary and a query-stationary kernel recomputes S and dP once
 // more instead of accumulating dQ with atomics; every output is written exactly once.
 #include "saf_device.h"
 #include "saf_internal.h"
@@ -108,17 +110,15 @@ __global__ __launch_bounds__(256) void bwd_delta_kernel(const DeltaParams p) {
 
 template <int D>
 struct DkdvSmem {
-  bf16 qs[BMQ * D];   // Q rows, chunks swizzled by swz_pi(row)
-  bf16 gs[BMQ * D];   // dO rows
-  bf16 qt[D * BMQ];   // Q^T [d][q], chunks swizzled by swz_tr(d)
-  bf16 gt[D * BMQ];   // dO^T
-  float ls[BMQ];      // lse * log2(e)
+  bf16 qs[BMQ * D];   // Q rows of the step, swizzled (swz<D/8>); also read transposed
+  bf16 gs[BMQ * D];   // dO rows of the step; also read transposed
+  float ls[BMQ];      // lse * log2(e) (+inf past T)
   float dl[BMQ];      // delta
 };
 
 struct FrzBwdSmem {
-  bf16 gt[FCOLS * BMQ];   // folded dO^T [column][q]
-  float lz[BMQ];          // log Z * log2(e)
+  bf16 gs[BMQ * FCOLS];   // folded dO [q][column], swizzled; read transposed
+  float lz[BMQ];          // log Z * log2(e) (+inf past T)
   float rw[BMQ + BNK];    // rho * log2(e) over the step's distance window
 };
 
@@ -127,45 +127,11 @@ constexpr int dkdv_smem_bytes() {
   return sizeof(DkdvSmem<D>) > sizeof(FrzBwdSmem) ? (int)sizeof(DkdvSmem<D>) : (int)sizeof(FrzBwdSmem);
 }
 
-// Stages rows [i0, i0 + BMQ) of a [T, D] bf16 matrix: `reg` holds this thread's 4 x 8 block.
-template <int D>
-__device__ __forceinline__ void load_block(const bf16* X, int i0, int T, u32x4 (&reg)[4]) {
-  constexpr int CPR = D / 8;
-  const int t = threadIdx.x;
-  if (t < (BMQ / 4) * CPR) {
-    const int cg = t % CPR, rg = t / CPR;
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int i = i0 + 4 * rg + r;
-      reg[r] = (i < T) ? *reinterpret_cast<const u32x4*>(X + (size_t)i * D + cg * 8) : u32x4{0, 0, 0, 0};
-    }
-  }
-}
-
-template <int D>
-__device__ __forceinline__ void store_block(const u32x4 (&reg)[4], bf16* rows, bf16* trans) {
-  constexpr int CPR = D / 8;
-  const int t = threadIdx.x;
-  if (t < (BMQ / 4) * CPR) {
-    const int cg = t % CPR, rg = t / CPR;
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int row = 4 * rg + r;
-      *reinterpret_cast<u32x4*>(rows + row * D + ((cg ^ swz_pi(row)) * 8)) = reg[r];
-    }
-    u32x2 cols[8];
-    transpose_4x8(reg, cols);
-#pragma unroll
-    for (int c = 0; c < 8; ++c) {
-      const int d = cg * 8 + c;
-      *reinterpret_cast<u32x2*>(trans + d * BMQ + (((rg >> 1) ^ swz_tr(d)) * 8) + (rg & 1) * 4) = cols[c];
-    }
-  }
-}
-
 template <int D>
 __device__ void dkdv_dyn(const BwdParams& p, int b, int h, int kt, unsigned char* smem_raw) {
-  DkdvSmem<D>& sm = *reinterpret_cast<DkdvSmem<D>*>(smem_raw);
+  constexpr int CPR = D / 8;
+  constexpr int NDB = D / 32;
+  DkdvSmem<D>* stg = reinterpret_cast<DkdvSmem<D>*>(smem_raw);
   const int t = threadIdx.x, lane = lane_id(), w = wave_id();
   const int m = lane & 31, hh = lane >> 5;
   const int T = p.T;
@@ -178,98 +144,90 @@ __device__ void dkdv_dyn(const BwdParams& p, int b, int h, int kt, unsigned char
   bf16x8 kf[D / 16], vf[D / 16];
 #pragma unroll
   for (int kk = 0; kk < D / 16; ++kk) {
-    const size_t off = (head + j) * D + kk * 16 + hh * 8;
-    kf[kk] = (j < T) ? *reinterpret_cast<const bf16x8*>(p.k + off) : bf16x8{};
-    vf[kk] = (j < T) ? *reinterpret_cast<const bf16x8*>(p.v + off) : bf16x8{};
+    const size_t off = (head + min(j, T - 1)) * D + kk * 16 + hh * 8;
+    kf[kk] = *reinterpret_cast<const bf16x8*>(p.k + off);
+    vf[kk] = *reinterpret_cast<const bf16x8*>(p.v + off);
   }
-  f32x16 dv[D / 32], dk[D / 32];
+  f32x16 dv[NDB], dk[NDB];
 #pragma unroll
-  for (int db = 0; db < D / 32; ++db) {
+  for (int db = 0; db < NDB; ++db) {
     dv[db] = f32x16{};
     dk[db] = f32x16{};
   }
 
   const int i_start = kt * BNK;
   const int n_steps = (T - i_start + BMQ - 1) / BMQ;
-  u32x4 qreg[4], greg[4];
   float lreg = 0.f, dreg = 0.f;
-  auto gload = [&](int st) {
+  auto load = [&](int st, DkdvSmem<D>& sm) {
     const int i0 = i_start + st * BMQ;
-    load_block<D>(Q, i0, T, qreg);
-    load_block<D>(G, i0, T, greg);
+    tile_load<CPR, BMQ>(sm.qs, [&](int row, int c) { return Q + (size_t)min(i0 + row, T - 1) * D + c * 8; });
+    tile_load<CPR, BMQ>(sm.gs, [&](int row, int c) { return G + (size_t)min(i0 + row, T - 1) * D + c * 8; });
     if (t < BMQ) {
       const int i = i0 + t;
       lreg = (i < T) ? p.lse[head + i] * kLog2e : __builtin_huge_valf();
       dreg = (i < T) ? p.delta[head + i] : 0.f;
     }
   };
-  auto sstore = [&]() {
-    store_block<D>(qreg, sm.qs, sm.qt);
-    store_block<D>(greg, sm.gs, sm.gt);
+  auto store_rows = [&](DkdvSmem<D>& sm) {
     if (t < BMQ) {
       sm.ls[t] = lreg;
       sm.dl[t] = dreg;
     }
   };
 
-  gload(0);
-  sstore();
+  load(0, stg[0]);
+  store_rows(stg[0]);
+  wait_vm0();
   __syncthreads();
   for (int st = 0; st < n_steps; ++st) {
-    if (st + 1 < n_steps) gload(st + 1);
+    if (st + 1 < n_steps) load(st + 1, stg[(st + 1) & 1]);
+    const DkdvSmem<D>& sm = stg[st & 1];
     const int i0 = i_start + st * BMQ;
 #pragma unroll
     for (int qb = 0; qb < BMQ / 32; ++qb) {
       const int iq0 = i0 + 32 * qb;
       if (k0w > iq0) continue;          // all keys of this wave after these queries
-      const bool diag = (k0w == iq0);
       const int qrow = qb * 32 + perm_rows(m);
-      f32x16 s = f32x16{}, dp = f32x16{};
-#pragma unroll
-      for (int kk = 0; kk < D / 16; ++kk) {
-        const int ch = 2 * kk + hh;
-        const bf16x8 aq = *reinterpret_cast<const bf16x8*>(sm.qs + qrow * D + ((ch ^ swz_pi(qrow)) * 8));
-        s = mfma32(aq, kf[kk], s);
-      }
-#pragma unroll
-      for (int kk = 0; kk < D / 16; ++kk) {
-        const int ch = 2 * kk + hh;
-        const bf16x8 ag = *reinterpret_cast<const bf16x8*>(sm.gs + qrow * D + ((ch ^ swz_pi(qrow)) * 8));
-        dp = mfma32(ag, vf[kk], dp);
-      }
+      // S = Q K^T and dP = dO V^T, two independent chains interleaved
+      f32x16 sd[2] = {f32x16{}, f32x16{}};
+      pipelined<D / 8>(
+          [&](int x) { return lds_row_operand<CPR>((x & 1) ? sm.gs : sm.qs, qrow, 2 * (x >> 1) + hh); },
+          [&](int x, const bf16x8& a) { sd[x & 1] = mfma32(a, (x & 1) ? vf[x >> 1] : kf[x >> 1], sd[x & 1]); });
       float pr[16], dsr[16];
+      const bool diag = (k0w == iq0);
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int qi = qb * 32 + acc_pos(r, hh);
-        float pv = __builtin_amdgcn_exp2f(__builtin_fmaf(s[r], p.c, -sm.ls[qi]));
-        if (diag && (32 * qb + acc_pos(r, hh)) + i0 < j) pv = 0.f;
+        float pv = __builtin_amdgcn_exp2f(__builtin_fmaf(sd[0][r], p.c, -sm.ls[qi]));
+        if (diag && acc_pos(r, hh) < m) pv = 0.f;  // query before this lane's key
         pr[r] = pv;
-        dsr[r] = pv * (dp[r] - sm.dl[qi]);
+        dsr[r] = pv * (sd[1][r] - sm.dl[qi]);
       }
+      bf16x8 pa[2], da[2];
 #pragma unroll
       for (int sk = 0; sk < 2; ++sk) {
-        const bf16x8 pa = pack8(pr + 8 * sk);
-        const bf16x8 da = pack8(dsr + 8 * sk);
-        const int ch = 4 * qb + 2 * sk + hh;
-#pragma unroll
-        for (int db = 0; db < D / 32; ++db) {
-          const int d = db * 32 + m;
-          const bf16x8 bg = *reinterpret_cast<const bf16x8*>(sm.gt + d * BMQ + ((ch ^ swz_tr(d)) * 8));
-          dv[db] = mfma32(pa, bg, dv[db]);
-          const bf16x8 bq = *reinterpret_cast<const bf16x8*>(sm.qt + d * BMQ + ((ch ^ swz_tr(d)) * 8));
-          dk[db] = mfma32(da, bq, dk[db]);
-        }
+        pa[sk] = pack8(pr + 8 * sk);
+        da[sk] = pack8(dsr + 8 * sk);
       }
+      // dV += P^T dO, dK += dS^T Q; the dO^T / Q^T operands are transposed LDS reads
+      pipelined<4 * NDB>(
+          [&](int x) {
+            const int sk = x / (2 * NDB), db = (x / 2) % NDB;
+            return lds_tr_operand<CPR>((x & 1) ? sm.qs : sm.gs, qb * 32 + sk * 16, db * 32, lane);
+          },
+          [&](int x, const bf16x8& bop) {
+            const int sk = x / (2 * NDB), db = (x / 2) % NDB;
+            if (x & 1) dk[db] = mfma32(da[sk], bop, dk[db]);
+            else dv[db] = mfma32(pa[sk], bop, dv[db]);
+          });
     }
+    if (st + 1 < n_steps) store_rows(stg[(st + 1) & 1]);
+    wait_vm0();
     __syncthreads();
-    if (st + 1 < n_steps) {
-      sstore();
-      __syncthreads();
-    }
   }
 
 #pragma unroll
-  for (int db = 0; db < D / 32; ++db)
+  for (int db = 0; db < NDB; ++db)
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
       const int key = k0w + acc_row(r, hh);
@@ -283,40 +241,31 @@ __device__ void dkdv_dyn(const BwdParams& p, int b, int h, int kt, unsigned char
 
 template <int D>
 __device__ void dkdv_frz(const BwdParams& p, int h, int chunk, int kt, unsigned char* smem_raw) {
-  FrzBwdSmem& sm = *reinterpret_cast<FrzBwdSmem*>(smem_raw);
+  constexpr int CPR = FCOLS / 8;
+  FrzBwdSmem* stg = reinterpret_cast<FrzBwdSmem*>(smem_raw);
   const int t = threadIdx.x, lane = lane_id(), w = wave_id();
   const int m = lane & 31, hh = lane >> 5;
-  const int T = p.T, H = p.H;
-  const int ncol_all = p.B * D;
+  const int T = p.T, H = p.H, B = p.B;
   const int col0 = chunk * FCOLS;
-  const int ncols = min(FCOLS, ncol_all - col0);
+  const int ncols = min(FCOLS, B * D - col0);
   const int kbase = kt * BNK, k0w = kbase + 32 * w, j = k0w + m;
   const float a2 = (j < T) ? p.alpha[(size_t)h * p.tab_stride + j] * kLog2e : kNegInf;
   const float* rho = p.rho + (size_t)h * p.tab_stride;
 
+  // Columns past B*D (a partial last chunk) read clamped, valid data and are not stored.
   f32x16 dv[FCOLS / 32];
 #pragma unroll
   for (int cb = 0; cb < FCOLS / 32; ++cb) dv[cb] = f32x16{};
 
   const int n_steps = (T - kbase + BMQ - 1) / BMQ;
-  constexpr int NB = (BMQ / 4) * (FCOLS / 8);  // 4x8 blocks per step = 512
-  u32x4 greg[NB / NTH][4];
   float treg = 0.f;
-  auto gload = [&](int st) {
+  auto load = [&](int st, FrzBwdSmem& sm) {
     const int i0 = kbase + st * BMQ;
-#pragma unroll
-    for (int x = 0; x < NB / NTH; ++x) {
-      const int blk = t + NTH * x, cg = blk % (FCOLS / 8), rg = blk / (FCOLS / 8);
-      const int col = col0 + cg * 8;
-      const bool ok = cg * 8 < ncols;
-      const int bb = col / D, d = col % D;
-      const bf16* Gb = p.dO + (((size_t)bb * H + h) * T) * D + d;
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int i = i0 + 4 * rg + r;
-        greg[x][r] = (ok && i < T) ? *reinterpret_cast<const u32x4*>(Gb + (size_t)i * D) : u32x4{0, 0, 0, 0};
-      }
-    }
+    tile_load<CPR, BMQ>(sm.gs, [&](int row, int c) {
+      const int col = col0 + c * 8;
+      const int bb = min(col / D, B - 1), d = col % D;
+      return p.dO + (((size_t)bb * H + h) * T + min(i0 + row, T - 1)) * D + d;
+    });
     if (t < BMQ) {
       const int i = i0 + t;
       treg = (i < T) ? p.lse[(size_t)h * T + i] * kLog2e : __builtin_huge_valf();
@@ -325,27 +274,18 @@ __device__ void dkdv_frz(const BwdParams& p, int h, int chunk, int kt, unsigned 
       treg = (dd >= 0 && dd < T) ? rho[dd] * kLog2e : kNegInf;
     }
   };
-  auto sstore = [&]() {
-#pragma unroll
-    for (int x = 0; x < NB / NTH; ++x) {
-      const int blk = t + NTH * x, cg = blk % (FCOLS / 8), rg = blk / (FCOLS / 8);
-      u32x2 cols[8];
-      transpose_4x8(greg[x], cols);
-#pragma unroll
-      for (int c = 0; c < 8; ++c) {
-        const int col = cg * 8 + c;
-        *reinterpret_cast<u32x2*>(sm.gt + col * BMQ + (((rg >> 1) ^ swz_tr(col)) * 8) + (rg & 1) * 4) = cols[c];
-      }
-    }
+  auto store_tables = [&](FrzBwdSmem& sm) {
     if (t < BMQ) sm.lz[t] = treg;
     else if (t < BMQ + BMQ + BNK - 1) sm.rw[t - BMQ] = treg;
   };
 
-  gload(0);
-  sstore();
+  load(0, stg[0]);
+  store_tables(stg[0]);
+  wait_vm0();
   __syncthreads();
   for (int st = 0; st < n_steps; ++st) {
-    if (st + 1 < n_steps) gload(st + 1);
+    if (st + 1 < n_steps) load(st + 1, stg[(st + 1) & 1]);
+    const FrzBwdSmem& sm = stg[st & 1];
     const int i0 = kbase + st * BMQ;
 #pragma unroll
     for (int qb = 0; qb < BMQ / 32; ++qb) {
@@ -366,23 +306,16 @@ __device__ void dkdv_frz(const BwdParams& p, int h, int chunk, int kt, unsigned 
         }
         const bf16x8 ahi = pack8(ph);
         const bf16x8 alo = pack8(pl);
-        const int ch = 4 * qb + 2 * sk + hh;
-#pragma unroll
-        for (int cb = 0; cb < FCOLS / 32; ++cb) {
-          if (cb * 32 < ncols) {
-            const int col = cb * 32 + m;
-            const bf16x8 bg = *reinterpret_cast<const bf16x8*>(sm.gt + col * BMQ + ((ch ^ swz_tr(col)) * 8));
-            dv[cb] = mfma32(ahi, bg, dv[cb]);
-            dv[cb] = mfma32(alo, bg, dv[cb]);
-          }
-        }
+        pipelined<FCOLS / 32>([&](int cb) { return lds_tr_operand<CPR>(sm.gs, qb * 32 + sk * 16, cb * 32, lane); },
+                              [&](int cb, const bf16x8& bg) {
+                                dv[cb] = mfma32(ahi, bg, dv[cb]);
+                                dv[cb] = mfma32(alo, bg, dv[cb]);
+                              });
       }
     }
+    if (st + 1 < n_steps) store_tables(stg[(st + 1) & 1]);
+    wait_vm0();
     __syncthreads();
-    if (st + 1 < n_steps) {
-      sstore();
-      __syncthreads();
-    }
   }
 
 #pragma unroll
@@ -400,7 +333,7 @@ __device__ void dkdv_frz(const BwdParams& p, int h, int chunk, int kt, unsigned 
 
 template <int D>
 __global__ __launch_bounds__(NTH, 1) void dkdv_kernel(const BwdParams p) {
-  __shared__ __attribute__((aligned(16))) unsigned char smem[dkdv_smem_bytes<D>()];
+  __shared__ __attribute__((aligned(16))) unsigned char smem[2 * dkdv_smem_bytes<D>()];
   const int item = blockIdx.x;
   const int kt = item / p.per_tile;  // key tile 0 has the most queries: heaviest first
   int rem = item % p.per_tile;
@@ -417,22 +350,22 @@ __global__ __launch_bounds__(NTH, 1) void dkdv_kernel(const BwdParams p) {
 
 template <int D>
 struct DqSmem {
-  bf16 k[BND * D];    // K rows, swz_pi
-  bf16 v[BND * D];    // V rows, swz_pi
-  bf16 kt[D * BND];   // K^T [d][key], swz_tr
+  bf16 k[BND * D];    // K rows, swizzled; also read transposed
+  bf16 v[BND * D];    // V rows, swizzled
 };
 
 template <int D>
-__global__ __launch_bounds__(NTH, 1) void dq_kernel(const BwdParams p) {
+__global__ __launch_bounds__(NTH, 2) void dq_kernel(const BwdParams p) {
   constexpr int CPR = D / 8;
-  __shared__ __attribute__((aligned(16))) unsigned char smem_raw[sizeof(DqSmem<D>)];
-  DqSmem<D>& sm = *reinterpret_cast<DqSmem<D>*>(smem_raw);
+  constexpr int NDB = D / 32;
+  __shared__ __attribute__((aligned(16))) unsigned char smem_raw[2 * sizeof(DqSmem<D>)];
+  DqSmem<D>* stg = reinterpret_cast<DqSmem<D>*>(smem_raw);
   const int item = blockIdx.x;
   const int n_qt = p.n_tiles;
   const int qt = n_qt - 1 - item / (p.B * p.n_dyn);
   const int bh = item % (p.B * p.n_dyn);
   const int b = bh / p.n_dyn, h = p.dyn[bh % p.n_dyn];
-  const int t = threadIdx.x, lane = lane_id(), w = wave_id();
+  const int lane = lane_id(), w = wave_id();
   const int m = lane & 31, hh = lane >> 5;
   const int T = p.T;
   const size_t head = ((size_t)b * p.H + h) * (size_t)T;
@@ -443,111 +376,69 @@ __global__ __launch_bounds__(NTH, 1) void dq_kernel(const BwdParams p) {
   bf16x8 qf[D / 16], gf[D / 16];
 #pragma unroll
   for (int kk = 0; kk < D / 16; ++kk) {
-    const size_t off = (head + i) * D + kk * 16 + hh * 8;
-    qf[kk] = (i < T) ? *reinterpret_cast<const bf16x8*>(p.q + off) : bf16x8{};
-    gf[kk] = (i < T) ? *reinterpret_cast<const bf16x8*>(p.dO + off) : bf16x8{};
+    const size_t off = (head + min(i, T - 1)) * D + kk * 16 + hh * 8;
+    qf[kk] = *reinterpret_cast<const bf16x8*>(p.q + off);
+    gf[kk] = *reinterpret_cast<const bf16x8*>(p.dO + off);
   }
   const float lse2 = (i < T) ? p.lse[head + i] * kLog2e : __builtin_huge_valf();
   const float dlt = (i < T) ? p.delta[head + i] : 0.f;
-  f32x16 acc[D / 32];
+  f32x16 acc[NDB];
 #pragma unroll
-  for (int db = 0; db < D / 32; ++db) acc[db] = f32x16{};
+  for (int db = 0; db < NDB; ++db) acc[db] = f32x16{};
 
   const int n_kt = min(2 * qt + 2, (T + BND - 1) / BND);
-  u32x4 kreg[4], vreg[4];
-  auto gload = [&](int J) {
+  auto load = [&](int J, DqSmem<D>& sm) {
     const int j0 = J * BND;
-    if (t < (BND / 4) * CPR) {
-      const int cg = t % CPR, rg = t / CPR;
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int key = j0 + 4 * rg + r;
-        kreg[r] = (key < T) ? *reinterpret_cast<const u32x4*>(K + (size_t)key * D + cg * 8) : u32x4{0, 0, 0, 0};
-        vreg[r] = (key < T) ? *reinterpret_cast<const u32x4*>(V + (size_t)key * D + cg * 8) : u32x4{0, 0, 0, 0};
-      }
-    }
-  };
-  auto sstore = [&]() {
-    if (t < (BND / 4) * CPR) {
-      const int cg = t % CPR, rg = t / CPR;
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int row = 4 * rg + r;
-        *reinterpret_cast<u32x4*>(sm.k + row * D + ((cg ^ swz_pi(row)) * 8)) = kreg[r];
-        *reinterpret_cast<u32x4*>(sm.v + row * D + ((cg ^ swz_pi(row)) * 8)) = vreg[r];
-      }
-      u32x2 cols[8];
-      transpose_4x8(kreg, cols);
-#pragma unroll
-      for (int c = 0; c < 8; ++c) {
-        const int d = cg * 8 + c;
-        *reinterpret_cast<u32x2*>(sm.kt + d * BND + (((rg >> 1) ^ swz_tr(d)) * 8) + (rg & 1) * 4) = cols[c];
-      }
-    }
+    tile_load<CPR, BND>(sm.k, [&](int row, int c) { return K + (size_t)min(j0 + row, T - 1) * D + c * 8; });
+    tile_load<CPR, BND>(sm.v, [&](int row, int c) { return V + (size_t)min(j0 + row, T - 1) * D + c * 8; });
   };
 
-  gload(0);
-  sstore();
+  load(0, stg[0]);
+  wait_vm0();
   __syncthreads();
   for (int J = 0; J < n_kt; ++J) {
-    if (J + 1 < n_kt) gload(J + 1);
+    if (J + 1 < n_kt) load(J + 1, stg[(J + 1) & 1]);
+    const DqSmem<D>& sm = stg[J & 1];
     const int j0 = J * BND;
     if (j0 <= i0w) {
-      f32x16 s[2], dp[2];
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-        s[kb] = f32x16{};
-        dp[kb] = f32x16{};
-        const int krow = kb * 32 + perm_rows(m);
-#pragma unroll
-        for (int kk = 0; kk < D / 16; ++kk) {
-          const int ch = 2 * kk + hh;
-          const bf16x8 ak = *reinterpret_cast<const bf16x8*>(sm.k + krow * D + ((ch ^ swz_pi(krow)) * 8));
-          s[kb] = mfma32(ak, qf[kk], s[kb]);
-        }
-#pragma unroll
-        for (int kk = 0; kk < D / 16; ++kk) {
-          const int ch = 2 * kk + hh;
-          const bf16x8 av = *reinterpret_cast<const bf16x8*>(sm.v + krow * D + ((ch ^ swz_pi(krow)) * 8));
-          dp[kb] = mfma32(av, gf[kk], dp[kb]);
-        }
-      }
+      // S^T = K Q^T and dP^T = V dO^T for two 32-key blocks: four independent chains
+      f32x16 sd[4] = {f32x16{}, f32x16{}, f32x16{}, f32x16{}};   // [kb * 2 + (0: S, 1: dP)]
+      pipelined<4 * (D / 16)>(
+          [&](int x) {
+            const int kk = x >> 2, kb = (x >> 1) & 1;
+            return lds_row_operand<CPR>((x & 1) ? sm.v : sm.k, kb * 32 + perm_rows(m), 2 * kk + hh);
+          },
+          [&](int x, const bf16x8& a) {
+            const int kk = x >> 2;
+            sd[x & 3] = mfma32(a, (x & 1) ? gf[kk] : qf[kk], sd[x & 3]);
+          });
       const bool diag = (j0 + BND - 1 > i0w);
+      const int lim = i - j0 - 8 * hh;
       bf16x8 dsb[4];
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) {
         float dsr[16];
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          float pv = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kb][r], p.c, -lse2));
-          if (diag && j0 + kb * 32 + acc_pos(r, hh) > i) pv = 0.f;
-          dsr[r] = pv * (dp[kb][r] - dlt);
+          float pv = __builtin_amdgcn_exp2f(__builtin_fmaf(sd[2 * kb][r], p.c, -lse2));
+          if (diag && kb * 32 + ((r >> 3) << 4) + (r & 7) > lim) pv = 0.f;
+          dsr[r] = pv * (sd[2 * kb + 1][r] - dlt);
         }
         dsb[2 * kb] = pack8(dsr);
         dsb[2 * kb + 1] = pack8(dsr + 8);
       }
-#pragma unroll
-      for (int db = 0; db < D / 32; ++db) {
-        const int d = db * 32 + m;
-#pragma unroll
-        for (int ks = 0; ks < 4; ++ks) {
-          const int ch = 2 * ks + hh;
-          const bf16x8 a = *reinterpret_cast<const bf16x8*>(sm.kt + d * BND + ((ch ^ swz_tr(d)) * 8));
-          acc[db] = mfma32(a, dsb[ks], acc[db]);
-        }
-      }
+      // dQ^T += K^T dS^T, K^T read transposed from the key tile
+      pipelined<4 * NDB>([&](int x) { return lds_tr_operand<CPR>(sm.k, (x / NDB) * 16, (x % NDB) * 32, lane); },
+                         [&](int x, const bf16x8& a) { acc[x % NDB] = mfma32(a, dsb[x / NDB], acc[x % NDB]); });
     }
+    wait_vm0();
     __syncthreads();
-    if (J + 1 < n_kt) {
-      sstore();
-      __syncthreads();
-    }
   }
 
   if (i < T) {
     float* out = p.dq + (head + i) * D;
 #pragma unroll
-    for (int db = 0; db < D / 32; ++db)
+    for (int db = 0; db < NDB; ++db)
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
         const int d = db * 32 + acc_row(4 * g, hh);

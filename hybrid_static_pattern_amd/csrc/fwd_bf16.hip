@@ -3,11 +3,17 @@
 // Method: "When Can Attention Heads Be Statically Defined?: 中文精读笔记".
 //   ordinary head (part 一):  O = softmax_causal(scale Q K^T) V
 //   frozen head (part 二.3, Eq. (3); part 二.4, Fig. 2):
-//       O(i) = sum_{j<=i} exp(alpha(j) + rho(i-j) - log Z(i)) V(j)
+//       O(i) = sum_{j<=i} exp(alpha(j) + rho(i-j)) V(j) / Z(i),
+//       Z(i) = sum_{j<=i} exp(alpha(j) + rho(i-j))
 // The page's fused kernel rebuilds a frozen tile from alpha, rho and Z and multiplies it
 // by V, with ordinary heads on flash-style online-softmax tiles, in one launch per layer.
 // Here both kinds of work items share one launch as well; the tiling is our own, built
 // around 64-wide wavefronts and the 32x32x16 bf16 MFMA.
+//
+// A frozen row is a softmax over the logits alpha(j) + rho(i-j), so a frozen item runs the
+// same online normaliser as an ordinary one, with the logits regenerated from alpha and
+// rho (staged in LDS) instead of computed by Q K^T; log Z(i) comes out of it and is
+// returned in lse for the backward. No separate pass over the T x T logits is needed.
 //
 // Work items (one 256-thread workgroup each, 4 waves x 32 queries = a 128-query tile):
 //   dynamic (b, h, q-tile): S^T = K Q^T per 64-key tile (each lane keeps one query),
@@ -16,7 +22,9 @@
 //   frozen (h, q-tile, column chunk): the batch is folded into the columns, so one
 //       item multiplies the regenerated pattern tile by up to 256 columns of
 //       [V_0 | V_1 | ...] and the exp work is shared by every batch entry.
-// Items are issued heaviest q-tile first; key tiles above the causal diagonal are skipped.
+// Key tiles go from HBM straight into double-buffered LDS (no staging registers), one
+// barrier per tile; V is stored row-major and read transposed (ds_read_b64_tr_b16). Items are issued heaviest
+// q-tile first; key tiles above the causal diagonal are skipped.
 #include "saf_device.h"
 #include "saf_internal.h"
 
@@ -47,31 +55,51 @@ struct FwdParams {
 };
 
 template <int D>
-struct DynSmem {
-  bf16 k[BN * D];   // row-major key tile, 16-byte chunks swizzled by swz_pi(row)
-  bf16 vt[D * BN];  // transposed value tile [d][key], chunks swizzled by swz_tr(d)
+struct DynStage {
+  bf16 k[BN * D];   // key tile, row-major, swizzled (swz<D/8>)
+  bf16 v[BN * D];   // value tile, row-major, swizzled; read transposed
 };
 
-struct FrzSmem {
-  bf16 vt[FCOLS * BN];   // transposed folded value tile [column][key]
+struct FrzStage {
+  bf16 v[BN * FCOLS];    // folded value tile [key][column], swizzled; read transposed
   float a2[BN];          // alpha * log2(e) of the tile's keys
   float rw[BM + BN];     // rho * log2(e) over the tile's distance window
 };
 
 template <int D>
-constexpr int smem_bytes() {
-  return sizeof(DynSmem<D>) > sizeof(FrzSmem) ? (int)sizeof(DynSmem<D>) : (int)sizeof(FrzSmem);
+constexpr int stage_bytes() {
+  return sizeof(DynStage<D>) > sizeof(FrzStage) ? (int)sizeof(DynStage<D>) : (int)sizeof(FrzStage);
+}
+
+// Online-softmax bookkeeping of one lane (one query row). `mx` is this lane's max over its
+// logits of the tile (-inf where masked) and c converts logits to log2 units; the other
+// half-wave holds the rest of the row. The running max m_used (log2 units) is raised
+// lazily, and the accumulators are rescaled when it is. Returns the value to subtract
+// before exp2: m_used, or 0 while no finite logit has been seen (then every exp2 of -inf
+// is 0, never NaN).
+template <int NACC>
+__device__ __forceinline__ float online_rescale(float mx, float c, float& m_used, float& l,
+                                                f32x16 (&acc)[NACC]) {
+  mx = fmaxf(mx, wave_shfl_xor32(mx)) * c;
+  const bool up = mx > m_used + kRescaleSlack;
+  if (__any(up)) {
+    const float m_new = up ? mx : m_used;
+    const float a = (m_used == kNegInf) ? 0.f : __builtin_amdgcn_exp2f(m_used - m_new);
+#pragma unroll
+    for (int x2 = 0; x2 < NACC; ++x2) acc[x2] *= a;
+    l *= a;
+    m_used = m_new;
+  }
+  return (m_used == kNegInf) ? 0.f : m_used;
 }
 
 // ---------------------------------------------------------------- dynamic item
 
 template <int D>
 __device__ void dyn_item(const FwdParams& p, int b, int h, int qt, unsigned char* smem_raw) {
-  constexpr int CPR = D / 8;              // 16-byte chunks per row
-  constexpr int NKC = BN * CPR / NTH;     // key-tile chunks per thread
-  constexpr int NVB = (BN / 4) * CPR;     // 4x8 value blocks per tile
-  DynSmem<D>& sm = *reinterpret_cast<DynSmem<D>*>(smem_raw);
-  const int t = threadIdx.x, lane = lane_id(), w = wave_id();
+  constexpr int CPR = D / 8;  // 16-byte chunks per row
+  DynStage<D>* st = reinterpret_cast<DynStage<D>*>(smem_raw);
+  const int lane = lane_id(), w = wave_id();
   const int m = lane & 31, hh = lane >> 5;
   const int T = p.T;
   const size_t head = ((size_t)b * p.H + h) * (size_t)T;
@@ -83,10 +111,8 @@ __device__ void dyn_item(const FwdParams& p, int b, int h, int qt, unsigned char
 
   bf16x8 qf[D / 16];
 #pragma unroll
-  for (int kk = 0; kk < D / 16; ++kk) {
-    if (i < T) qf[kk] = *reinterpret_cast<const bf16x8*>(Q + (size_t)i * D + kk * 16 + hh * 8);
-    else qf[kk] = bf16x8{};
-  }
+  for (int kk = 0; kk < D / 16; ++kk)
+    qf[kk] = *reinterpret_cast<const bf16x8*>(Q + (size_t)min(i, T - 1) * D + kk * 16 + hh * 8);
 
   f32x16 o[D / 32];
 #pragma unroll
@@ -94,115 +120,58 @@ __device__ void dyn_item(const FwdParams& p, int b, int h, int qt, unsigned char
   float m_used = kNegInf, l = 0.f;
 
   const int n_kt = min(2 * qt + 2, (T + BN - 1) / BN);
-
-  u32x4 kreg[NKC];
-  u32x4 vreg[4];
-  auto gload = [&](int J) {
+  auto load = [&](int J, DynStage<D>& sm) {
     const int j0 = J * BN;
-#pragma unroll
-    for (int x = 0; x < NKC; ++x) {
-      const int c = t + NTH * x, row = c / CPR, cc = c % CPR;
-      kreg[x] = (j0 + row < T) ? *reinterpret_cast<const u32x4*>(K + (size_t)(j0 + row) * D + cc * 8)
-                               : u32x4{0, 0, 0, 0};
-    }
-    if (t < NVB) {
-      const int db = t % CPR, kg = t / CPR;
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int key = j0 + 4 * kg + r;
-        vreg[r] = (key < T) ? *reinterpret_cast<const u32x4*>(V + (size_t)key * D + db * 8)
-                            : u32x4{0, 0, 0, 0};
-      }
-    }
-  };
-  auto sstore = [&]() {
-#pragma unroll
-    for (int x = 0; x < NKC; ++x) {
-      const int c = t + NTH * x, row = c / CPR, cc = c % CPR;
-      *reinterpret_cast<u32x4*>(sm.k + row * D + ((cc ^ swz_pi(row)) * 8)) = kreg[x];
-    }
-    if (t < NVB) {
-      const int db = t % CPR, kg = t / CPR;
-      u32x2 cols[8];
-      transpose_4x8(vreg, cols);
-#pragma unroll
-      for (int c = 0; c < 8; ++c) {
-        const int d = db * 8 + c;
-        *reinterpret_cast<u32x2*>(sm.vt + d * BN + (((kg >> 1) ^ swz_tr(d)) * 8) + (kg & 1) * 4) = cols[c];
-      }
-    }
+    tile_load<CPR, BN>(sm.k, [&](int row, int c) { return K + (size_t)min(j0 + row, T - 1) * D + c * 8; });
+    tile_load<CPR, BN>(sm.v, [&](int row, int c) { return V + (size_t)min(j0 + row, T - 1) * D + c * 8; });
   };
 
-  gload(0);
-  sstore();
+  load(0, st[0]);
+  wait_vm0();
   __syncthreads();
   for (int J = 0; J < n_kt; ++J) {
-    if (J + 1 < n_kt) gload(J + 1);
+    if (J + 1 < n_kt) load(J + 1, st[(J + 1) & 1]);
+    const DynStage<D>& sm = st[J & 1];
     const int j0 = J * BN;
     if (j0 <= i0w) {  // tile meets this wave's causal region
-      f32x16 s[2];
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-        s[kb] = f32x16{};
-        const int krow = kb * 32 + perm_rows(m);
-#pragma unroll
-        for (int kk = 0; kk < D / 16; ++kk) {
-          const int ch = 2 * kk + hh;
-          const bf16x8 a = *reinterpret_cast<const bf16x8*>(sm.k + krow * D + ((ch ^ swz_pi(krow)) * 8));
-          s[kb] = mfma32(a, qf[kk], s[kb]);
-        }
-      }
-      if (j0 + BN - 1 > i0w) {  // diagonal tile: mask keys after the query
+      // S^T for keys j0 .. j0+63: two independent 32-key chains, interleaved
+      f32x16 s[2] = {f32x16{}, f32x16{}};
+      pipelined<D / 8>(
+          [&](int x) { return lds_row_operand<CPR>(sm.k, (x & 1) * 32 + perm_rows(m), 2 * (x >> 1) + hh); },
+          [&](int x, const bf16x8& a) { s[x & 1] = mfma32(a, qf[x >> 1], s[x & 1]); });
+      if (j0 + BN - 1 > i0w) {  // diagonal tile: keys after the query get -inf
+        const int lim = i - j0 - 8 * hh;  // key offset kb*32 + acc_pos(r, hh) > i - j0
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
           for (int r = 0; r < 16; ++r)
-            if (j0 + kb * 32 + acc_pos(r, hh) > i) s[kb][r] = kNegInf;
+            if (kb * 32 + ((r >> 3) << 4) + (r & 7) > lim) s[kb][r] = kNegInf;
       }
       float mx = kNegInf;
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
         for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb][r]);
-      mx = fmaxf(mx, wave_shfl_xor32(mx));
-      const float mt = mx * p.c;
-      const bool up = mt > m_used + kRescaleSlack;
-      if (__any(up)) {
-        const float m_new = up ? mt : m_used;
-        const float alpha = (m_used == kNegInf) ? 0.f : __builtin_amdgcn_exp2f(m_used - m_new);
-#pragma unroll
-        for (int db = 0; db < D / 32; ++db) o[db] *= alpha;
-        l *= alpha;
-        m_used = m_new;
-      }
+      const float msub = online_rescale<D / 32>(mx, p.c, m_used, l, o);
       bf16x8 pb[4];
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-        float pv[16];
+      for (int ks = 0; ks < 4; ++ks) {
+        float pv[8];
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          pv[r] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kb][r], p.c, -m_used));
-          l += pv[r];
+        for (int e = 0; e < 8; ++e) {
+          pv[e] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[ks >> 1][(ks & 1) * 8 + e], p.c, -msub));
+          l += pv[e];
         }
-        pb[2 * kb] = pack8(pv);
-        pb[2 * kb + 1] = pack8(pv + 8);
+        pb[ks] = pack8(pv);
       }
-#pragma unroll
-      for (int db = 0; db < D / 32; ++db) {
-        const int d = db * 32 + m;
-#pragma unroll
-        for (int ks = 0; ks < 4; ++ks) {
-          const int ch = 2 * ks + hh;
-          const bf16x8 a = *reinterpret_cast<const bf16x8*>(sm.vt + d * BN + ((ch ^ swz_tr(d)) * 8));
-          o[db] = mfma32(a, pb[ks], o[db]);
-        }
-      }
+      // O^T += V^T P^T: the four d-blocks are independent accumulators
+      constexpr int NDB = D / 32;
+      pipelined<4 * NDB>(
+          [&](int x) { return lds_tr_operand<CPR>(sm.v, (x / NDB) * 16, (x % NDB) * 32, lane); },
+          [&](int x, const bf16x8& a) { o[x % NDB] = mfma32(a, pb[x / NDB], o[x % NDB]); });
     }
+    wait_vm0();
     __syncthreads();
-    if (J + 1 < n_kt) {
-      sstore();
-      __syncthreads();
-    }
   }
 
   const float lt = l + wave_shfl_xor32(l);
@@ -227,42 +196,32 @@ __device__ void dyn_item(const FwdParams& p, int b, int h, int qt, unsigned char
 
 template <int D>
 __device__ void frz_item(const FwdParams& p, int h, int chunk, int qt, unsigned char* smem_raw) {
-  FrzSmem& sm = *reinterpret_cast<FrzSmem*>(smem_raw);
+  constexpr int CPR = FCOLS / 8;
+  FrzStage* st = reinterpret_cast<FrzStage*>(smem_raw);
   const int t = threadIdx.x, lane = lane_id(), w = wave_id();
   const int m = lane & 31, hh = lane >> 5;
-  const int T = p.T, H = p.H;
-  const int ncol_all = p.B * D;
+  const int T = p.T, H = p.H, B = p.B;
   const int col0 = chunk * FCOLS;
-  const int ncols = min(FCOLS, ncol_all - col0);
+  const int ncols = min(FCOLS, B * D - col0);
   const int i0 = qt * BM, i0w = i0 + w * 32, i = i0w + m;
   const float* alpha = p.alpha + (size_t)h * p.tab_stride;
   const float* rho = p.rho + (size_t)h * p.tab_stride;
-  const float lz = (i < T) ? p.lse[(size_t)h * T + i] * kLog2e : 0.f;  // log Z(i), batch 0
 
+  // Columns past B*D (a partial last chunk) read clamped, valid data and are not stored.
   f32x16 o[FCOLS / 32];
 #pragma unroll
   for (int cb = 0; cb < FCOLS / 32; ++cb) o[cb] = f32x16{};
+  float m_used = kNegInf, l = 0.f;
 
   const int n_kt = min(2 * qt + 2, (T + BN - 1) / BN);
-  constexpr int NVB = (BN / 4) * (FCOLS / 8);  // 4x8 blocks per tile = 512
-  u32x4 vreg[NVB / NTH][4];
-  float treg;
-  auto gload = [&](int J) {
+  float treg = 0.f;
+  auto load = [&](int J, FrzStage& sm) {
     const int j0 = J * BN;
-#pragma unroll
-    for (int x = 0; x < NVB / NTH; ++x) {
-      const int blk = t + NTH * x, cg = blk % (FCOLS / 8), kg = blk / (FCOLS / 8);
-      const int col = col0 + cg * 8;
-      const bool ok = cg * 8 < ncols;
-      const int bb = col / D, d = col % D;
-      const bf16* Vb = p.v + (((size_t)bb * H + h) * T) * D + d;
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int key = j0 + 4 * kg + r;
-        vreg[x][r] = (ok && key < T) ? *reinterpret_cast<const u32x4*>(Vb + (size_t)key * D)
-                                     : u32x4{0, 0, 0, 0};
-      }
-    }
+    tile_load<CPR, BN>(sm.v, [&](int row, int c) {
+      const int col = col0 + c * 8;
+      const int bb = min(col / D, B - 1), d = col % D;
+      return p.v + (((size_t)bb * H + h) * T + min(j0 + row, T - 1)) * D + d;
+    });
     if (t < BN) {
       treg = (j0 + t < T) ? alpha[j0 + t] * kLog2e : kNegInf;
     } else if (t < BN + BM + BN - 1) {
@@ -270,59 +229,53 @@ __device__ void frz_item(const FwdParams& p, int h, int chunk, int qt, unsigned 
       treg = (dd >= 0 && dd < T) ? rho[dd] * kLog2e : kNegInf;
     }
   };
-  auto sstore = [&]() {
-#pragma unroll
-    for (int x = 0; x < NVB / NTH; ++x) {
-      const int blk = t + NTH * x, cg = blk % (FCOLS / 8), kg = blk / (FCOLS / 8);
-      u32x2 cols[8];
-      transpose_4x8(vreg[x], cols);
-#pragma unroll
-      for (int c = 0; c < 8; ++c) {
-        const int col = cg * 8 + c;
-        *reinterpret_cast<u32x2*>(sm.vt + col * BN + (((kg >> 1) ^ swz_tr(col)) * 8) + (kg & 1) * 4) = cols[c];
-      }
-    }
+  auto store_tables = [&](FrzStage& sm) {
     if (t < BN) sm.a2[t] = treg;
     else if (t < BN + BM + BN - 1) sm.rw[t - BN] = treg;
   };
 
-  gload(0);
-  sstore();
+  load(0, st[0]);
+  store_tables(st[0]);
+  wait_vm0();
   __syncthreads();
   for (int J = 0; J < n_kt; ++J) {
-    if (J + 1 < n_kt) gload(J + 1);
+    if (J + 1 < n_kt) load(J + 1, st[(J + 1) & 1]);
+    const FrzStage& sm = st[J & 1];
     const int j0 = J * BN;
     if (j0 <= i0w) {
+      // logits alpha(j) + rho(i - j) in log2 units; the distance window index of
+      // (i, j0 + kofs + e) is (i - i0) - (kofs + e) + BN - 1, and entries for j > i hold
+      // -inf, so the causal mask comes for free. They are read twice from LDS (for the
+      // max, then for the exps) rather than held in registers next to 128 accumulators.
+      const int rb0 = (i - i0) + BN - 1 - hh * 8;
+      float mx = kNegInf;
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) mx = fmaxf(mx, sm.a2[ks * 16 + hh * 8 + e] + sm.rw[rb0 - ks * 16 - e]);
+      const float msub = online_rescale<FCOLS / 32>(mx, 1.f, m_used, l, o);
 #pragma unroll
       for (int ks = 0; ks < 4; ++ks) {
-        float pv[8];
         const int kofs = ks * 16 + hh * 8;
-        // distance window index of (i, j0 + kofs + e) is (i - i0) - (kofs + e) + BN - 1;
-        // entries for j > i hold -inf, so the causal mask comes for free.
-        const int rbase = (i - i0) - kofs + BN - 1;
+        float pv[8];
 #pragma unroll
-        for (int e = 0; e < 8; ++e)
-          pv[e] = __builtin_amdgcn_exp2f(sm.a2[kofs + e] + sm.rw[rbase - e] - lz);
-        const bf16x8 pb = pack8(pv);
-#pragma unroll
-        for (int cb = 0; cb < FCOLS / 32; ++cb) {
-          if (cb * 32 < ncols) {
-            const int col = cb * 32 + m;
-            const int ch = 2 * ks + hh;
-            const bf16x8 a = *reinterpret_cast<const bf16x8*>(sm.vt + col * BN + ((ch ^ swz_tr(col)) * 8));
-            o[cb] = mfma32(a, pb, o[cb]);
-          }
+        for (int e = 0; e < 8; ++e) {
+          pv[e] = __builtin_amdgcn_exp2f(sm.a2[kofs + e] + sm.rw[rb0 - ks * 16 - e] - msub);
+          l += pv[e];
         }
+        const bf16x8 pb = pack8(pv);
+        pipelined<FCOLS / 32>([&](int cb) { return lds_tr_operand<CPR>(sm.v, ks * 16, cb * 32, lane); },
+                              [&](int cb, const bf16x8& a) { o[cb] = mfma32(a, pb, o[cb]); });
       }
     }
+    if (J + 1 < n_kt) store_tables(st[(J + 1) & 1]);
+    wait_vm0();
     __syncthreads();
-    if (J + 1 < n_kt) {
-      sstore();
-      __syncthreads();
-    }
   }
 
+  const float lt = l + wave_shfl_xor32(l);
   if (i < T) {
+    const float inv = 1.f / lt;
 #pragma unroll
     for (int cb = 0; cb < FCOLS / 32; ++cb) {
       if (cb * 32 >= ncols) continue;
@@ -331,17 +284,22 @@ __device__ void frz_item(const FwdParams& p, int h, int chunk, int qt, unsigned 
         const int col = col0 + cb * 32 + acc_row(4 * g, hh);
         const int bb = col / D, d = col % D;
         u32x2 pk;
-        pk[0] = pack_bf16x2(o[cb][4 * g], o[cb][4 * g + 1]);
-        pk[1] = pack_bf16x2(o[cb][4 * g + 2], o[cb][4 * g + 3]);
+        pk[0] = pack_bf16x2(o[cb][4 * g] * inv, o[cb][4 * g + 1] * inv);
+        pk[1] = pack_bf16x2(o[cb][4 * g + 2] * inv, o[cb][4 * g + 3] * inv);
         *reinterpret_cast<u32x2*>(p.o + (((size_t)bb * H + h) * T + i) * D + d) = pk;
       }
+    }
+    // log Z(i) is the same for every batch entry; the first column chunk writes it.
+    if (chunk == 0 && hh == 0) {
+      const float lz = (m_used + __log2f(lt)) * kLn2;
+      for (int bb = 0; bb < B; ++bb) p.lse[((size_t)bb * H + h) * T + i] = lz;
     }
   }
 }
 
 template <int D>
 __global__ __launch_bounds__(NTH, 2) void hybrid_fwd_kernel(const FwdParams p) {
-  __shared__ __attribute__((aligned(16))) unsigned char smem[smem_bytes<D>()];
+  __shared__ __attribute__((aligned(16))) unsigned char smem[2 * stage_bytes<D>()];
   const int item = blockIdx.x;
   const int qt = p.n_qt - 1 - item / p.per_qt;
   int rem = item % p.per_qt;
@@ -354,59 +312,7 @@ __global__ __launch_bounds__(NTH, 2) void hybrid_fwd_kernel(const FwdParams p) {
   }
 }
 
-// ---------------------------------------------------------------- log Z prologue
-
-struct LogzParams {
-  const float* alpha;
-  const float* rho;
-  float* lse;
-  int tab_stride, B, H, T;
-  uint8_t frz[kMaxHeads];
-};
-
-// log Z(i) = log sum_{j<=i} exp(alpha(j) + rho(i-j)) (Eq. (3)), max-subtracted, one row per
-// 8 lanes; written to lse[b, h, i] for every b. Batch independent.
-__global__ __launch_bounds__(256) void frozen_logz_kernel(const LogzParams p) {
-  const int h = p.frz[blockIdx.y];
-  const int row = blockIdx.x * 32 + (threadIdx.x >> 3), sub = threadIdx.x & 7;
-  const float* al = p.alpha + (size_t)h * p.tab_stride;
-  const float* rh = p.rho + (size_t)h * p.tab_stride;
-  float mx = kNegInf;
-  if (row < p.T)
-    for (int j = sub; j <= row; j += 8) mx = fmaxf(mx, al[j] + rh[row - j]);
-#pragma unroll
-  for (int o = 1; o < 8; o <<= 1) mx = fmaxf(mx, __shfl_xor(mx, o, 64));
-  float s = 0.f;
-  if (row < p.T)
-    for (int j = sub; j <= row; j += 8) s += exp2f((al[j] + rh[row - j] - mx) * kLog2e);
-#pragma unroll
-  for (int o = 1; o < 8; o <<= 1) s += __shfl_xor(s, o, 64);
-  if (row < p.T && sub == 0) {
-    const float lz = mx + logf(s);
-    for (int b = 0; b < p.B; ++b) p.lse[((size_t)b * p.H + h) * p.T + row] = lz;
-  }
-}
-
 }  // namespace
-
-hipError_t launch_frozen_logz(const AttnArgs& a, const float* alpha, const float* rho,
-                              float* lse, hipStream_t s) {
-  if (a.heads.n_frz == 0) return hipSuccess;
-  LogzParams p;
-  p.alpha = alpha;
-  p.rho = rho;
-  p.lse = lse;
-  p.tab_stride = a.tab_stride;
-  p.B = a.B;
-  p.H = a.H;
-  p.T = a.T;
-  for (int x = 0; x < kMaxHeads; ++x) p.frz[x] = a.heads.frz[x];
-  dim3 grid((a.T + 31) / 32, a.heads.n_frz);
-  prof_begin("frozen_logz", s);
-  hipLaunchKernelGGL(frozen_logz_kernel, grid, dim3(256), 0, s, p);
-  prof_end(s);
-  return hipGetLastError();
-}
 
 hipError_t launch_fwd_bf16(const AttnArgs& a, const void* q, const void* k, const void* v,
                            const float* alpha, const float* rho, void* o, float* lse,

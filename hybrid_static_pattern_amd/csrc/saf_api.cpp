@@ -155,9 +155,7 @@ saf_status saf_attn_fwd(const saf_attn_desc* desc, const void* q, const void* k,
   SAF_TRY(check_ptr(lse, true, "lse"));
   hipStream_t s = static_cast<hipStream_t>(stream);
   (void)hipGetLastError();
-  hipError_t e = saf::launch_frozen_logz(a, alpha, rho, lse, s);
-  if (e != hipSuccess) return hip_fail(e, "frozen_logz launch");
-  e = a.bf16 ? saf::launch_fwd_bf16(a, q, k, v, alpha, rho, o, lse, s)
+  hipError_t e = a.bf16 ? saf::launch_fwd_bf16(a, q, k, v, alpha, rho, o, lse, s)
              : saf::launch_fwd_fp32(a, q, k, v, alpha, rho, o, lse, s);
   if (e != hipSuccess) return hip_fail(e, "hybrid forward launch");
   return SAF_OK;

@@ -36,7 +36,8 @@ __device__ __forceinline__ f32x16 mfma32(const bf16x8& a, const bf16x8& b, const
 }
 
 __device__ __forceinline__ int lane_id() { return threadIdx.x & 63; }
-__device__ __forceinline__ int wave_id() { return threadIdx.x >> 6; }
+// wave index, known to the compiler as wave-uniform (scalar register)
+__device__ __forceinline__ int wave_id() { return __builtin_amdgcn_readfirstlane(threadIdx.x >> 6); }
 
 // bits 2 and 3 of m swapped (an involution on 0..31)
 __device__ __forceinline__ int perm_rows(int m) {
@@ -57,6 +58,107 @@ __device__ __forceinline__ int acc_row(int r, int h) { return ((r >> 2) << 3) + 
 __device__ __forceinline__ int swz_pi(int row) { return (row & 3) | ((row >> 1) & 4); }
 // Rows read consecutively and written 8 apart (transposed staging): bits 0-2 ^ bits 3-5.
 __device__ __forceinline__ int swz_tr(int row) { return (row ^ (row >> 3)) & 7; }
+
+// ---------------------------------------------------------------- LDS tiles
+//
+// A tile is row-major in LDS, CPR 16-byte chunks per row, and chunk c of row r is stored
+// at position c ^ swz<CPR>(r). Two read patterns use the same tiles:
+//   * ds_read_b128 of rows in pi order (an MFMA A operand whose rows are the tile rows):
+//     8 consecutive lanes read rows {0,1,2,3,8,9,10,11} (+4, +16, ...) at one chunk;
+//   * ds_read_b64_tr_b16 (an operand whose rows are the tile columns, see lds_tr_operand):
+//     one instruction reads rows {0..3, 8..11} (+ base) over 64 bytes each.
+// The swizzle gives the 8 rows of the first pattern 8 distinct chunk positions and
+// spreads the second over all banks (each 512-byte read needs two LDS cycles anyway).
+template <int CPR>
+__device__ __forceinline__ int swz(int row) {
+  return CPR >= 16 ? (((row & 3) << 2) | ((row >> 3) & 1)) : ((row & 3) | (((row >> 3) & 1) << 2));
+}
+
+// element offset of (row, col) in a swizzled tile with CPR chunks per row
+template <int CPR>
+__device__ __forceinline__ int tile_off(int row, int col) {
+  return row * (CPR * 8) + ((((col >> 3) ^ swz<CPR>(row))) << 3) + (col & 7);
+}
+
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return (uint32_t)(uintptr_t)((const __attribute__((address_space(3))) void*)p);
+}
+
+// Global -> LDS without registers: lane l's 16 bytes at gsrc land at LDS byte address
+// lds_base + 16 l (lds_base wave-uniform). Issued through inline assembly so that the
+// compiler does not wait for it before unrelated LDS reads; wait_vm0() before the barrier
+// that publishes the tile. M0 holds the LDS base (nothing else in these kernels uses M0).
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+__device__ __forceinline__ void g2lds16(const void* gsrc, uint32_t lds_base) {
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off" ::"s"(lds_base), "v"(gsrc) : "m0");
+}
+#pragma clang diagnostic pop
+
+__device__ __forceinline__ void wait_vm0() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
+// Loads NR rows x CPR chunks into a swizzled tile with all 4 waves of the workgroup.
+// src(row, chunk) returns the global address of logical chunk `chunk` of tile row `row`
+// (callers clamp rows past the end of the data to a valid row).
+template <int CPR, int NR, class Src>
+__device__ __forceinline__ void tile_load(bf16* tile, Src src) {
+  constexpr int NCH = NR * CPR;           // 16-byte chunks
+  constexpr int PERW = NCH / 64 / 4;      // wave-wide loads per wave
+  static_assert(NCH % 256 == 0, "tile must split evenly over 4 waves");
+  const int w = wave_id(), lane = lane_id();
+  const uint32_t base = lds_addr(tile);
+#pragma unroll
+  for (int x = 0; x < PERW; ++x) {
+    const int blk = w * PERW + x;
+    const int pch = blk * 64 + lane;      // physical chunk written by this lane
+    const int row = pch / CPR;
+    const int c = (pch % CPR) ^ swz<CPR>(row);
+    g2lds16(src(row, c), base + blk * 1024);
+  }
+}
+
+// MFMA operand (8 bf16) whose row index runs along the tile's columns: lane l receives
+// tile[row0 + 8 (l / 32) + e][col0 + l % 32] for e = 0..7, read with two
+// ds_read_b64_tr_b16. Within each 16-lane group, the transposing read hands lane i the
+// (i mod 4)-th element of the 8 bytes addressed by lane 4k + i/4 into slot k, so each lane
+// addresses 4 consecutive columns of row row0 + 8 (l / 32) + (l / 4) % 4 (+4 for e = 4..7).
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+template <int CPR>
+__device__ __forceinline__ bf16x8 lds_tr_operand(const bf16* tile, int row0, int col0, int lane) {
+  const int row = row0 + 8 * (lane >> 5) + ((lane >> 2) & 3);
+  const int col = col0 + 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
+  typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+  const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(tile + tile_off<CPR>(row, col)));
+  const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(tile + tile_off<CPR>(row + 4, col)));
+  u32x4 r;
+  r[0] = __builtin_bit_cast(u32x2, lo)[0];
+  r[1] = __builtin_bit_cast(u32x2, lo)[1];
+  r[2] = __builtin_bit_cast(u32x2, hi)[0];
+  r[3] = __builtin_bit_cast(u32x2, hi)[1];
+  return __builtin_bit_cast(bf16x8, r);
+}
+
+// MFMA operand (8 bf16) whose row index is the tile row: lane l receives
+// tile[row][8 * chunk .. 8 * chunk + 7] (one ds_read_b128).
+template <int CPR>
+__device__ __forceinline__ bf16x8 lds_row_operand(const bf16* tile, int row, int chunk) {
+  return *reinterpret_cast<const bf16x8*>(tile + row * (CPR * 8) + ((chunk ^ swz<CPR>(row)) << 3));
+}
+
+// Runs mma(x, operand) for x = 0..N-1 with the LDS read of operand x issued two products
+// ahead (three rotating registers), so each MFMA waits for an operand that was requested
+// while the previous ones executed rather than for a read issued just before it.
+template <int N, class Read, class Mma>
+__device__ __forceinline__ void pipelined(Read read, Mma mma) {
+  bf16x8 buf[3];
+  buf[0] = read(0);
+  if constexpr (N > 1) buf[1] = read(1);
+#pragma unroll
+  for (int x = 0; x < N; ++x) {
+    if (x + 2 < N) buf[(x + 2) % 3] = read(x + 2);
+    mma(x, buf[x % 3]);
+  }
+}
 
 __device__ __forceinline__ float wave_shfl_xor32(float x) {
   return __shfl_xor(x, 32, 64);

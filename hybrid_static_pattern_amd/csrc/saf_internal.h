@@ -27,9 +27,7 @@ struct AttnArgs {
 void prof_begin(const char* name, hipStream_t s);
 void prof_end(hipStream_t s);
 
-// Forward: logZ prologue for frozen heads, then the hybrid forward.
-hipError_t launch_frozen_logz(const AttnArgs& a, const float* alpha, const float* rho,
-                              float* lse, hipStream_t s);
+// Forward (ordinary and frozen heads in one launch).
 hipError_t launch_fwd_bf16(const AttnArgs& a, const void* q, const void* k, const void* v,
                            const float* alpha, const float* rho, void* o, float* lse,
                            hipStream_t s);

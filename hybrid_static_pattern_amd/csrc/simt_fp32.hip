@@ -44,14 +44,11 @@ __global__ __launch_bounds__(R) void fwd_fp32_kernel(const F32Params p) {
   const size_t head = (size_t)bh * T;
   float q[D], o[D];
   for (int d = 0; d < D; ++d) o[d] = 0.f;
-  float m = kNegInf, l = 0.f, lz = 0.f;
+  float m = kNegInf, l = 0.f;
   const float* al = p.alpha + (size_t)h * p.tab_stride;
   const float* rh = p.rho + (size_t)h * p.tab_stride;
-  if (frz) {
-    if (i < T) lz = p.lse[head + i];
-  } else {
+  if (!frz)
     for (int d = 0; d < D; ++d) q[d] = (i < T) ? p.q[(head + i) * D + d] : 0.f;
-  }
   const int jend = min(T, (tile + 1) * R);
   for (int j0 = 0; j0 < jend; j0 += R) {
     __syncthreads();
@@ -65,29 +62,31 @@ __global__ __launch_bounds__(R) void fwd_fp32_kernel(const F32Params p) {
     for (int r = 0; r < R; ++r) {
       const int j = j0 + r;
       if (j > i) break;
-      float w;
+      // logit: scale q.k for an ordinary head, alpha(j) + rho(i - j) for a frozen one (Eq. (3))
+      float s;
       if (frz) {
-        w = expf(al[j] + rh[i - j] - lz);
+        s = al[j] + rh[i - j];
       } else {
-        float s = 0.f;
+        s = 0.f;
         for (int d = 0; d < D; ++d) s = fmaf(q[d], ks[r][d], s);
         s *= p.scale;
-        if (s > m) {
-          const float corr = (m == kNegInf) ? 0.f : expf(m - s);
-          l *= corr;
-          for (int d = 0; d < D; ++d) o[d] *= corr;
-          m = s;
-        }
-        w = expf(s - m);
-        l += w;
       }
+      if (s == kNegInf) continue;  // zero weight
+      if (s > m) {
+        const float corr = (m == kNegInf) ? 0.f : expf(m - s);
+        l *= corr;
+        for (int d = 0; d < D; ++d) o[d] *= corr;
+        m = s;
+      }
+      const float w = expf(s - m);
+      l += w;
       for (int d = 0; d < D; ++d) o[d] = fmaf(w, vs[r][d], o[d]);
     }
   }
   if (i < T) {
-    const float inv = frz ? 1.f : 1.f / l;
+    const float inv = 1.f / l;
     for (int d = 0; d < D; ++d) p.out[(head + i) * D + d] = o[d] * inv;
-    if (!frz) p.lse[head + i] = m + logf(l);
+    p.lse[head + i] = m + logf(l);
   }
 }
 

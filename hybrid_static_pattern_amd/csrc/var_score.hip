@@ -38,59 +38,35 @@ struct VarParams {
 
 template <int D>
 struct KTile {
-  bf16 k[BN * D];
+  bf16 k[BN * D];   // key rows, swizzled (swz<D/8>)
 };
 
 template <int D>
-__device__ __forceinline__ void load_k(const bf16* K, int j0, int T, u32x4 (&reg)[BN * D / 8 / NTH]) {
-  constexpr int CPR = D / 8;
-  const int t = threadIdx.x;
-#pragma unroll
-  for (int x = 0; x < BN * CPR / NTH; ++x) {
-    const int c = t + NTH * x, row = c / CPR, cc = c % CPR;
-    reg[x] = (j0 + row < T) ? *reinterpret_cast<const u32x4*>(K + (size_t)(j0 + row) * D + cc * 8)
-                            : u32x4{0, 0, 0, 0};
-  }
-}
-
-template <int D>
-__device__ __forceinline__ void store_k(const u32x4 (&reg)[BN * D / 8 / NTH], bf16* ks) {
-  constexpr int CPR = D / 8;
-  const int t = threadIdx.x;
-#pragma unroll
-  for (int x = 0; x < BN * CPR / NTH; ++x) {
-    const int c = t + NTH * x, row = c / CPR, cc = c % CPR;
-    *reinterpret_cast<u32x4*>(ks + row * D + ((cc ^ swz_pi(row)) * 8)) = reg[x];
-  }
+__device__ __forceinline__ void load_k(const bf16* K, int j0, int T, KTile<D>& tile) {
+  tile_load<D / 8, BN>(tile.k, [&](int row, int c) { return K + (size_t)min(j0 + row, T - 1) * D + c * 8; });
 }
 
 // S^T tile (64 keys x this lane's query) for the 64-key tile held in LDS.
 template <int D>
 __device__ __forceinline__ void scores(const bf16* ks, const bf16x8 (&qf)[D / 16], int m, int hh,
                                        f32x16 (&s)[2]) {
-#pragma unroll
-  for (int kb = 0; kb < 2; ++kb) {
-    s[kb] = f32x16{};
-    const int krow = kb * 32 + perm_rows(m);
-#pragma unroll
-    for (int kk = 0; kk < D / 16; ++kk) {
-      const int ch = 2 * kk + hh;
-      const bf16x8 a = *reinterpret_cast<const bf16x8*>(ks + krow * D + ((ch ^ swz_pi(krow)) * 8));
-      s[kb] = mfma32(a, qf[kk], s[kb]);
-    }
-  }
+  s[0] = f32x16{};
+  s[1] = f32x16{};
+  pipelined<D / 8>(
+      [&](int x) { return lds_row_operand<D / 8>(ks, (x & 1) * 32 + perm_rows(m), 2 * (x >> 1) + hh); },
+      [&](int x, const bf16x8& a) { s[x & 1] = mfma32(a, qf[x >> 1], s[x & 1]); });
 }
 
 template <int D>
 __device__ __forceinline__ void load_q(const bf16* Q, int i, int T, int hh, bf16x8 (&qf)[D / 16]) {
 #pragma unroll
   for (int kk = 0; kk < D / 16; ++kk)
-    qf[kk] = (i < T) ? *reinterpret_cast<const bf16x8*>(Q + (size_t)i * D + kk * 16 + hh * 8) : bf16x8{};
+    qf[kk] = *reinterpret_cast<const bf16x8*>(Q + (size_t)min(i, T - 1) * D + kk * 16 + hh * 8);
 }
 
 template <int D>
 __global__ __launch_bounds__(NTH, 2) void var_lse_kernel(const VarParams p) {
-  __shared__ __attribute__((aligned(16))) KTile<D> sm;
+  __shared__ __attribute__((aligned(16))) KTile<D> stg[2];
   const int n_qt = p.n_it;
   const int qt = n_qt - 1 - blockIdx.x / (p.N * p.H);
   const int nh = blockIdx.x % (p.N * p.H);
@@ -103,16 +79,15 @@ __global__ __launch_bounds__(NTH, 2) void var_lse_kernel(const VarParams p) {
   const bf16* K = p.k + head * D;
   float mx_run = kNegInf, l = 0.f;
   const int n_kt = min(2 * qt + 2, (T + BN - 1) / BN);
-  u32x4 reg[BN * D / 8 / NTH];
-  load_k<D>(K, 0, T, reg);
-  store_k<D>(reg, sm.k);
+  load_k<D>(K, 0, T, stg[0]);
+  wait_vm0();
   __syncthreads();
   for (int J = 0; J < n_kt; ++J) {
-    if (J + 1 < n_kt) load_k<D>(K, (J + 1) * BN, T, reg);
+    if (J + 1 < n_kt) load_k<D>(K, (J + 1) * BN, T, stg[(J + 1) & 1]);
     const int j0 = J * BN;
     if (j0 <= i0w) {
       f32x16 s[2];
-      scores<D>(sm.k, qf, m, hh, s);
+      scores<D>(stg[J & 1].k, qf, m, hh, s);
       const bool diag = j0 + BN - 1 > i0w;
       float mx = kNegInf;
 #pragma unroll
@@ -133,11 +108,8 @@ __global__ __launch_bounds__(NTH, 2) void var_lse_kernel(const VarParams p) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) l += __builtin_amdgcn_exp2f(s[kb][r] - mx_run);
     }
+    wait_vm0();
     __syncthreads();
-    if (J + 1 < n_kt) {
-      store_k<D>(reg, sm.k);
-      __syncthreads();
-    }
   }
   const float lt = l + wave_shfl_xor32(l);
   if (i < T && hh == 0) p.lse2[head + i] = mx_run + __log2f(lt);
@@ -145,7 +117,7 @@ __global__ __launch_bounds__(NTH, 2) void var_lse_kernel(const VarParams p) {
 
 template <int D>
 __global__ __launch_bounds__(NTH, 2) void var_welford_kernel(const VarParams p) {
-  __shared__ __attribute__((aligned(16))) KTile<D> sm;
+  __shared__ __attribute__((aligned(16))) KTile<D> stg[2];
   __shared__ float red[NTH / 64];
   const int jt = blockIdx.x % p.n_jt;
   const int it = (blockIdx.x / p.n_jt) % p.n_it;
@@ -182,19 +154,18 @@ __global__ __launch_bounds__(NTH, 2) void var_welford_kernel(const VarParams p) 
   const bool active = j0 <= i0w;     // wave has causal entries in this tile
   const bool diag = j0 + BN - 1 > i0w;
   const size_t nh_stride = (size_t)p.H * T;
-  u32x4 reg[BN * D / 8 / NTH];
-  load_k<D>(p.k + ((size_t)h * T) * D, j0, T, reg);
-  store_k<D>(reg, sm.k);
+  load_k<D>(p.k + ((size_t)h * T) * D, j0, T, stg[0]);
+  wait_vm0();
   __syncthreads();
   for (int n = 0; n < p.N; ++n) {
     const size_t head = (size_t)n * nh_stride + (size_t)h * T;
-    if (n + 1 < p.N) load_k<D>(p.k + (head + nh_stride) * D, j0, T, reg);
+    if (n + 1 < p.N) load_k<D>(p.k + (head + nh_stride) * D, j0, T, stg[(n + 1) & 1]);
     if (active) {
       bf16x8 qf[D / 16];
       load_q<D>(p.q + head * D, i, T, hh, qf);
       const float l2 = (i < T) ? p.lse2[head + i] : __builtin_huge_valf();
       f32x16 s[2];
-      scores<D>(sm.k, qf, m, hh, s);
+      scores<D>(stg[n & 1].k, qf, m, hh, s);
       const float rn = 1.f / (float)(n + 1);
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
@@ -208,11 +179,8 @@ __global__ __launch_bounds__(NTH, 2) void var_welford_kernel(const VarParams p) 
           m2[x] = __builtin_fmaf(dlt, a - mean[x], m2[x]);
         }
     }
+    wait_vm0();
     __syncthreads();
-    if (n + 1 < p.N) {
-      store_k<D>(reg, sm.k);
-      __syncthreads();
-    }
   }
 
   float sum = 0.f;
