@@ -22,6 +22,16 @@ sys.path.insert(0, ROOT)
 
 METRIC = "hybrid attn fwd+bwd tokens/s per layer + MFMA util (1B-shape, T=8192, r=25%)"
 PEAK_BF16_TFLOPS = 2516.6  # MI355X dense bf16 MFMA (published)
+# fp32 vector rate without packed instructions (the kernels are built without them):
+# 256 CUs x 4 SIMDs x 16 lanes x 2 FLOP (FMA) x 2.4 GHz
+PEAK_FP32_VALU_TFLOPS = 256 * 4 * 16 * 2 * 2.4e9 / 1e12
+# fp32 operations per (causal pair, sequence) in the Welford pass of the calibration score:
+# logit-to-log2 FMA (2), exp2 (1), delta (1), mean FMA (2), M2 subtract + FMA (3)
+WELFORD_FLOP_PER_SAMPLE = 9
+
+
+def log(msg: str) -> None:
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
 
 
 def causal_pairs(T: int) -> int:
@@ -68,6 +78,7 @@ def cpu_baseline(L, n_dyn, n_frz):
         saf_oracle.attn_fwd(s(L["q"]), s(L["k"]), s(L["v"]), fz, al, rh, scale)
         saf_oracle.attn_bwd(s(L["q"]), s(L["k"]), s(L["v"]), s(L["do"]), fz, al, rh, scale)
         t_head[kind] = time.perf_counter() - t0
+        log(f"oracle {kind} head: {t_head[kind]:.1f} s")
     layer_s = B * n_dyn * t_head.get("dyn", 0.0) + B * n_frz * t_head.get("frz", 0.0)
     return {
         "value": B * T / layer_s, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
@@ -86,9 +97,10 @@ def main():
     ap.add_argument("--workload", default="l1b_fwdbwd")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-sweep", action="store_true", help="skip the r=0 / r=50%% timings")
+    ap.add_argument("--no-calibration", action="store_true", help="skip the calibration-score timing")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
-                    help="first run one plain device copy of this many MiB (a known-size reference "
-                         "for the FETCH_SIZE / WRITE_SIZE counters)")
+                    help="first run one plain elementwise copy (torch.neg) of this many MiB, a "
+                         "known-size reference for the FETCH_SIZE / WRITE_SIZE counters")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU: the layer's heads are independent and this build has no "
@@ -97,7 +109,7 @@ def main():
 
     import torch
 
-    from hybrid_static_pattern_amd import inputs, saf
+    from hybrid_static_pattern_amd import inputs, profiling, saf
 
     saf.load()
     if args.calib_copy_mib:
@@ -105,7 +117,7 @@ def main():
         src = torch.ones(n, dtype=torch.float32, device="cuda:0")
         dst = torch.empty_like(src)
         torch.cuda.synchronize()
-        dst.copy_(src)
+        torch.neg(src, out=dst)  # one elementwise kernel: reads and writes the given MiB
         torch.cuda.synchronize()
         del src, dst
     spec = dict(inputs.WORKLOADS[args.workload])
@@ -144,6 +156,7 @@ def main():
             saf.prof_enable(False)
         return ms, recs
 
+    log(f"timing {args.steps} steps of {args.workload}")
     mask = L["frozen"]
     n_frz = int(mask.sum())
     n_dyn = H - n_frz
@@ -179,7 +192,7 @@ def main():
         "kernels_ms": kern_ms,
         "roofline": {
             "kernel": dominant, "bound": "mfma", "achieved": achieved, "peak": PEAK_BF16_TFLOPS,
-            "unit": "TFLOP/s", "frac": achieved / PEAK_BF16_TFLOPS, "traffic": None,
+            "unit": "TFLOP/s", "frac": achieved / PEAK_BF16_TFLOPS, "traffic": traffic_bytes(profiling, dominant),
         },
     }
     if not args.no_sweep:
@@ -193,8 +206,64 @@ def main():
                              "tflops": layer_flops(B, T, D, H - nf, nf) / (ms2 * 1e-3) / 1e12}
         out["sweep"] = sweep
         out["speedup_vs_r0"] = sweep["r0"]["ms_per_step"] / ms
+    if not args.no_calibration:
+        log("timing the calibration score")
+        out["calibration"] = calibration(torch, inputs, profiling, saf, args.steps, args.warmup)
+    if not args.no_cpu_baseline:
+        log("timing the CPU oracle on a sample of the layer")
     out["cpu_baseline"] = None if args.no_cpu_baseline else cpu_baseline(L, n_dyn, n_frz)
     print(json.dumps(out), flush=True)
+
+
+def traffic_bytes(profiling, prof_name):
+    """HBM bytes per launch of the kernel from the committed counter summary (profiles/), or
+    None when there is none or the kernel's sources changed since it was taken."""
+    k = profiling.PROF_TO_KERNEL.get(prof_name)
+    d = profiling.read_summary(k, os.path.join(ROOT, "profiles")) if k else None
+    return None if d is None else d["fetch_bytes"] + d["write_bytes"]
+
+
+def calibration(torch, inputs, profiling, saf, steps, warmup):
+    """The calibration score (saf_var_score) on its workload: N=64 sequences, 12 heads,
+    T=1024, d_h=64, bf16, per-head temperatures over [0.1, 4]."""
+    C = inputs.make_calibration(**inputs.CALIBRATION)
+    N, H, T, D = C["N"], C["H"], C["T"], C["D"]
+    dev = torch.device("cuda:0")
+    q = torch.from_numpy(C["q"]).to(dev).to(torch.bfloat16)
+    k = torch.from_numpy(C["k"]).to(dev).to(torch.bfloat16)
+    a_hat = torch.empty((H, T, T), dtype=torch.float32, device=dev)
+    s_var = torch.empty((H,), dtype=torch.float64, device=dev)
+    rank = torch.empty((H,), dtype=torch.int32, device=dev)
+    ws = torch.empty(saf.var_workspace_size(N, H, T, D), dtype=torch.uint8, device=dev)
+    run = lambda: saf.var_score(q, k, a_hat=a_hat, s_var=s_var, rank=rank, workspace=ws)
+    for _ in range(warmup):
+        run()
+    torch.cuda.synchronize()
+    saf.prof_enable(True)
+    st = torch.cuda.current_stream()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(st)
+    for _ in range(steps):
+        run()
+    e1.record(st)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+    recs = saf.prof_read()
+    saf.prof_enable(False)
+    per = {}
+    for name, t in recs:
+        per.setdefault(name, []).append(t)
+    kern = {n: float(np.mean(v)) for n, v in per.items()}
+    samples = N * H * causal_pairs(T)
+    wf = WELFORD_FLOP_PER_SAMPLE * samples / (kern["var_welford"] * 1e-3) / 1e12
+    return {
+        "workload": f"calibration: N={N} H={H} T={T} D={D} bf16, tau in [0.1, 4]",
+        "ms": ms, "sample_pairs_per_s": samples / (ms * 1e-3), "kernels_ms": kern,
+        "ranking": [int(x) for x in rank.cpu().numpy()],
+        "roofline": {"kernel": "var_welford", "bound": "alu", "achieved": wf, "peak": PEAK_FP32_VALU_TFLOPS,
+                     "unit": "TFLOP/s", "frac": wf / PEAK_FP32_VALU_TFLOPS,
+                     "traffic": traffic_bytes(profiling, "var_welford")},
+    }
 
 
 if __name__ == "__main__":

@@ -123,7 +123,7 @@ struct FrzBwdSmem {
 };
 
 template <int D>
-constexpr int dkdv_smem_bytes() {
+constexpr int dkdv_smem_bytes() {  // per stage
   return sizeof(DkdvSmem<D>) > sizeof(FrzBwdSmem) ? (int)sizeof(DkdvSmem<D>) : (int)sizeof(FrzBwdSmem);
 }
 
@@ -140,13 +140,22 @@ __device__ void dkdv_dyn(const BwdParams& p, int b, int h, int kt, unsigned char
   const bf16* G = p.dO + head * D;
   const int k0w = kt * BNK + 32 * w;
   const int j = k0w + m;
-
   bf16x8 kf[D / 16], vf[D / 16];
 #pragma unroll
   for (int kk = 0; kk < D / 16; ++kk) {
     const size_t off = (head + min(j, T - 1)) * D + kk * 16 + hh * 8;
     kf[kk] = *reinterpret_cast<const bf16x8*>(p.k + off);
     vf[kk] = *reinterpret_cast<const bf16x8*>(p.v + off);
+  }
+  // per-lane LDS offsets: Q / dO rows in pi order (per k-step), transposed dO^T / Q^T reads
+  // (per d-block); the two tiles share a layout and hence the offsets
+  uint32_t qoff[D / 16], toff[NDB][2];
+#pragma unroll
+  for (int kk = 0; kk < D / 16; ++kk) qoff[kk] = row_off<CPR>(perm_rows(m), 2 * kk + hh);
+#pragma unroll
+  for (int db = 0; db < NDB; ++db) {
+    toff[db][0] = tr_off<CPR>(db * 32, 0, lane);
+    toff[db][1] = tr_off<CPR>(db * 32, 1, lane);
   }
   f32x16 dv[NDB], dk[NDB];
 #pragma unroll
@@ -175,55 +184,70 @@ __device__ void dkdv_dyn(const BwdParams& p, int b, int h, int kt, unsigned char
     }
   };
 
+  // One 32-query block: S and dP for this wave's 32 keys, P and dS in registers, then the
+  // dV and dK products. `diag` masks queries before the key (the block on the diagonal).
+  auto block = [&](const DkdvSmem<D>& sm, int qb, bool diag) {
+    // S = Q K^T and dP = dO V^T, two independent chains interleaved
+    f32x16 sd[2] = {f32x16{}, f32x16{}};
+    pipelined<D / 8>(
+        [&](int x) { return lds_row<CPR>((x & 1) ? sm.gs : sm.qs, qb * 32, qoff[x >> 1]); },
+        [&](int x, const bf16x8& a) { sd[x & 1] = mfma32(a, (x & 1) ? vf[x >> 1] : kf[x >> 1], sd[x & 1]); });
+    float pr[16], dsr[16];
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int qi = qb * 32 + acc_pos(r, hh);
+      float pv = __builtin_amdgcn_exp2f(__builtin_fmaf(sd[0][r], p.c, -sm.ls[qi]));
+      if (diag && acc_pos(r, hh) < m) pv = 0.f;  // query before this lane's key
+      pr[r] = pv;
+      dsr[r] = pv * (sd[1][r] - sm.dl[qi]);
+    }
+    bf16x8 pa[2], da[2];
+#pragma unroll
+    for (int sk = 0; sk < 2; ++sk) {
+      pa[sk] = pack8(pr + 8 * sk);
+      da[sk] = pack8(dsr + 8 * sk);
+    }
+    // dV += P^T dO, dK += dS^T Q; the dO^T / Q^T operands are transposed LDS reads
+    pipelined<4 * NDB>(
+        [&](int x) {
+          const int sk = x / (2 * NDB), db = (x / 2) % NDB;
+          return lds_tr<CPR>((x & 1) ? sm.qs : sm.gs, qb * 32 + sk * 16, toff[db][0], toff[db][1]);
+        },
+        [&](int x, const bf16x8& bop) {
+          const int sk = x / (2 * NDB), db = (x / 2) % NDB;
+          if (x & 1) dk[db] = mfma32(da[sk], bop, dk[db]);
+          else dv[db] = mfma32(pa[sk], bop, dv[db]);
+        });
+  };
+
+  auto step = [&](int st, const DkdvSmem<D>& sm, DkdvSmem<D>& nxt) {
+    if (st + 1 < n_steps) load(st + 1, nxt);
+    if (st * BMQ < BNK) {
+      // steps on the diagonal: query block gq (32 queries) of the key tile meets this
+      // wave's keys (32 w .. 32 w + 31 within the tile) only for gq >= w, and gq == w needs
+      // the causal mask
+#pragma unroll
+      for (int qb = 0; qb < BMQ / 32; ++qb) {
+        const int gq = st * (BMQ / 32) + qb;
+        if (gq < w) continue;
+        block(sm, qb, gq == w);
+      }
+    } else {
+#pragma unroll
+      for (int qb = 0; qb < BMQ / 32; ++qb) block(sm, qb, false);
+    }
+    if (st + 1 < n_steps) store_rows(nxt);
+    wait_vm0();
+    __syncthreads();
+  };
+
   load(0, stg[0]);
   store_rows(stg[0]);
   wait_vm0();
   __syncthreads();
-  for (int st = 0; st < n_steps; ++st) {
-    if (st + 1 < n_steps) load(st + 1, stg[(st + 1) & 1]);
-    const DkdvSmem<D>& sm = stg[st & 1];
-    const int i0 = i_start + st * BMQ;
-#pragma unroll
-    for (int qb = 0; qb < BMQ / 32; ++qb) {
-      const int iq0 = i0 + 32 * qb;
-      if (k0w > iq0) continue;          // all keys of this wave after these queries
-      const int qrow = qb * 32 + perm_rows(m);
-      // S = Q K^T and dP = dO V^T, two independent chains interleaved
-      f32x16 sd[2] = {f32x16{}, f32x16{}};
-      pipelined<D / 8>(
-          [&](int x) { return lds_row_operand<CPR>((x & 1) ? sm.gs : sm.qs, qrow, 2 * (x >> 1) + hh); },
-          [&](int x, const bf16x8& a) { sd[x & 1] = mfma32(a, (x & 1) ? vf[x >> 1] : kf[x >> 1], sd[x & 1]); });
-      float pr[16], dsr[16];
-      const bool diag = (k0w == iq0);
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int qi = qb * 32 + acc_pos(r, hh);
-        float pv = __builtin_amdgcn_exp2f(__builtin_fmaf(sd[0][r], p.c, -sm.ls[qi]));
-        if (diag && acc_pos(r, hh) < m) pv = 0.f;  // query before this lane's key
-        pr[r] = pv;
-        dsr[r] = pv * (sd[1][r] - sm.dl[qi]);
-      }
-      bf16x8 pa[2], da[2];
-#pragma unroll
-      for (int sk = 0; sk < 2; ++sk) {
-        pa[sk] = pack8(pr + 8 * sk);
-        da[sk] = pack8(dsr + 8 * sk);
-      }
-      // dV += P^T dO, dK += dS^T Q; the dO^T / Q^T operands are transposed LDS reads
-      pipelined<4 * NDB>(
-          [&](int x) {
-            const int sk = x / (2 * NDB), db = (x / 2) % NDB;
-            return lds_tr_operand<CPR>((x & 1) ? sm.qs : sm.gs, qb * 32 + sk * 16, db * 32, lane);
-          },
-          [&](int x, const bf16x8& bop) {
-            const int sk = x / (2 * NDB), db = (x / 2) % NDB;
-            if (x & 1) dk[db] = mfma32(da[sk], bop, dk[db]);
-            else dv[db] = mfma32(pa[sk], bop, dv[db]);
-          });
-    }
-    if (st + 1 < n_steps) store_rows(stg[(st + 1) & 1]);
-    wait_vm0();
-    __syncthreads();
+  for (int st = 0; st < n_steps; st += 2) {  // unrolled by two: the LDS stage is a constant
+    step(st, stg[0], stg[1]);
+    if (st + 1 < n_steps) step(st + 1, stg[1], stg[0]);
   }
 
 #pragma unroll
@@ -258,7 +282,9 @@ __device__ void dkdv_frz(const BwdParams& p, int h, int chunk, int kt, unsigned 
   for (int cb = 0; cb < FCOLS / 32; ++cb) dv[cb] = f32x16{};
 
   const int n_steps = (T - kbase + BMQ - 1) / BMQ;
-  float treg = 0.f;
+  // per step: lz for BMQ queries, then the rho window of BMQ + BNK - 1 distances
+  constexpr int NTAB = BMQ + BMQ + BNK - 1;
+  float treg[(NTAB + NTH - 1) / NTH];
   auto load = [&](int st, FrzBwdSmem& sm) {
     const int i0 = kbase + st * BMQ;
     tile_load<CPR, BMQ>(sm.gs, [&](int row, int c) {
@@ -266,26 +292,36 @@ __device__ void dkdv_frz(const BwdParams& p, int h, int chunk, int kt, unsigned 
       const int bb = min(col / D, B - 1), d = col % D;
       return p.dO + (((size_t)bb * H + h) * T + min(i0 + row, T - 1)) * D + d;
     });
-    if (t < BMQ) {
-      const int i = i0 + t;
-      treg = (i < T) ? p.lse[(size_t)h * T + i] * kLog2e : __builtin_huge_valf();
-    } else if (t < BMQ + BMQ + BNK - 1) {
-      const int dd = i0 - kbase - (BNK - 1) + (t - BMQ);
-      treg = (dd >= 0 && dd < T) ? rho[dd] * kLog2e : kNegInf;
+#pragma unroll
+    for (int y = 0; y < (NTAB + NTH - 1) / NTH; ++y) {
+      const int x = t + y * NTH;
+      if (x < BMQ) {
+        const int i = i0 + x;
+        treg[y] = (i < T) ? p.lse[(size_t)h * T + i] * kLog2e : __builtin_huge_valf();
+      } else if (x < NTAB) {
+        const int dd = i0 - kbase - (BNK - 1) + (x - BMQ);
+        treg[y] = (dd >= 0 && dd < T) ? rho[dd] * kLog2e : kNegInf;
+      }
     }
   };
   auto store_tables = [&](FrzBwdSmem& sm) {
-    if (t < BMQ) sm.lz[t] = treg;
-    else if (t < BMQ + BMQ + BNK - 1) sm.rw[t - BMQ] = treg;
+#pragma unroll
+    for (int y = 0; y < (NTAB + NTH - 1) / NTH; ++y) {
+      const int x = t + y * NTH;
+      if (x < BMQ) sm.lz[x] = treg[y];
+      else if (x < NTAB) sm.rw[x - BMQ] = treg[y];
+    }
   };
 
-  load(0, stg[0]);
-  store_tables(stg[0]);
-  wait_vm0();
-  __syncthreads();
-  for (int st = 0; st < n_steps; ++st) {
-    if (st + 1 < n_steps) load(st + 1, stg[(st + 1) & 1]);
-    const FrzBwdSmem& sm = stg[st & 1];
+  uint32_t goff[FCOLS / 32][2];
+#pragma unroll
+  for (int cb = 0; cb < FCOLS / 32; ++cb) {
+    goff[cb][0] = tr_off<CPR>(cb * 32, 0, lane);
+    goff[cb][1] = tr_off<CPR>(cb * 32, 1, lane);
+  }
+
+  auto step = [&](int st, const FrzBwdSmem& sm, FrzBwdSmem& nxt) {
+    if (st + 1 < n_steps) load(st + 1, nxt);
     const int i0 = kbase + st * BMQ;
 #pragma unroll
     for (int qb = 0; qb < BMQ / 32; ++qb) {
@@ -306,16 +342,25 @@ __device__ void dkdv_frz(const BwdParams& p, int h, int chunk, int kt, unsigned 
         }
         const bf16x8 ahi = pack8(ph);
         const bf16x8 alo = pack8(pl);
-        pipelined<FCOLS / 32>([&](int cb) { return lds_tr_operand<CPR>(sm.gs, qb * 32 + sk * 16, cb * 32, lane); },
+        pipelined<FCOLS / 32>([&](int cb) { return lds_tr<CPR>(sm.gs, qb * 32 + sk * 16, goff[cb][0], goff[cb][1]); },
                               [&](int cb, const bf16x8& bg) {
                                 dv[cb] = mfma32(ahi, bg, dv[cb]);
                                 dv[cb] = mfma32(alo, bg, dv[cb]);
                               });
       }
     }
-    if (st + 1 < n_steps) store_tables(stg[(st + 1) & 1]);
+    if (st + 1 < n_steps) store_tables(nxt);
     wait_vm0();
     __syncthreads();
+  };
+
+  load(0, stg[0]);
+  store_tables(stg[0]);
+  wait_vm0();
+  __syncthreads();
+  for (int st = 0; st < n_steps; st += 2) {  // unrolled by two: the LDS stage is a constant
+    step(st, stg[0], stg[1]);
+    if (st + 1 < n_steps) step(st + 1, stg[1], stg[0]);
   }
 
 #pragma unroll
@@ -393,46 +438,53 @@ __global__ __launch_bounds__(NTH, 2) void dq_kernel(const BwdParams p) {
     tile_load<CPR, BND>(sm.v, [&](int row, int c) { return V + (size_t)min(j0 + row, T - 1) * D + c * 8; });
   };
 
-  load(0, stg[0]);
-  wait_vm0();
-  __syncthreads();
-  for (int J = 0; J < n_kt; ++J) {
-    if (J + 1 < n_kt) load(J + 1, stg[(J + 1) & 1]);
-    const DqSmem<D>& sm = stg[J & 1];
+  uint32_t koff[D / 16], toff[NDB][2];
+#pragma unroll
+  for (int kk = 0; kk < D / 16; ++kk) koff[kk] = row_off<CPR>(perm_rows(m), 2 * kk + hh);
+#pragma unroll
+  for (int db = 0; db < NDB; ++db) {
+    toff[db][0] = tr_off<CPR>(db * 32, 0, lane);
+    toff[db][1] = tr_off<CPR>(db * 32, 1, lane);
+  }
+
+  auto tile = [&](int J, const DqSmem<D>& sm, DqSmem<D>& nxt) {
+    if (J + 1 < n_kt) load(J + 1, nxt);
     const int j0 = J * BND;
     if (j0 <= i0w) {
-      // S^T = K Q^T and dP^T = V dO^T for two 32-key blocks: four independent chains
-      f32x16 sd[4] = {f32x16{}, f32x16{}, f32x16{}, f32x16{}};   // [kb * 2 + (0: S, 1: dP)]
-      pipelined<4 * (D / 16)>(
-          [&](int x) {
-            const int kk = x >> 2, kb = (x >> 1) & 1;
-            return lds_row_operand<CPR>((x & 1) ? sm.v : sm.k, kb * 32 + perm_rows(m), 2 * kk + hh);
-          },
-          [&](int x, const bf16x8& a) {
-            const int kk = x >> 2;
-            sd[x & 3] = mfma32(a, (x & 1) ? gf[kk] : qf[kk], sd[x & 3]);
-          });
+      // per 32-key block: S^T = K Q^T and dP^T = V dO^T (two independent chains), then dS^T
       const bool diag = (j0 + BND - 1 > i0w);
       const int lim = i - j0 - 8 * hh;
       bf16x8 dsb[4];
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) {
+        f32x16 sd[2] = {f32x16{}, f32x16{}};   // 0: S^T, 1: dP^T
+        pipelined<D / 8>(
+            [&](int x) { return lds_row<CPR>((x & 1) ? sm.v : sm.k, kb * 32, koff[x >> 1]); },
+            [&](int x, const bf16x8& a) { sd[x & 1] = mfma32(a, (x & 1) ? gf[x >> 1] : qf[x >> 1], sd[x & 1]); });
         float dsr[16];
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          float pv = __builtin_amdgcn_exp2f(__builtin_fmaf(sd[2 * kb][r], p.c, -lse2));
+          float pv = __builtin_amdgcn_exp2f(__builtin_fmaf(sd[0][r], p.c, -lse2));
           if (diag && kb * 32 + ((r >> 3) << 4) + (r & 7) > lim) pv = 0.f;
-          dsr[r] = pv * (sd[2 * kb + 1][r] - dlt);
+          dsr[r] = pv * (sd[1][r] - dlt);
         }
         dsb[2 * kb] = pack8(dsr);
         dsb[2 * kb + 1] = pack8(dsr + 8);
       }
       // dQ^T += K^T dS^T, K^T read transposed from the key tile
-      pipelined<4 * NDB>([&](int x) { return lds_tr_operand<CPR>(sm.k, (x / NDB) * 16, (x % NDB) * 32, lane); },
+      pipelined<4 * NDB>([&](int x) { return lds_tr<CPR>(sm.k, (x / NDB) * 16, toff[x % NDB][0], toff[x % NDB][1]); },
                          [&](int x, const bf16x8& a) { acc[x % NDB] = mfma32(a, dsb[x / NDB], acc[x % NDB]); });
     }
     wait_vm0();
     __syncthreads();
+  };
+
+  load(0, stg[0]);
+  wait_vm0();
+  __syncthreads();
+  for (int J = 0; J < n_kt; J += 2) {  // unrolled by two: the LDS stage is a constant
+    tile(J, stg[0], stg[1]);
+    if (J + 1 < n_kt) tile(J + 1, stg[1], stg[0]);
   }
 
   if (i < T) {

@@ -126,19 +126,25 @@ __device__ void dyn_item(const FwdParams& p, int b, int h, int qt, unsigned char
     tile_load<CPR, BN>(sm.v, [&](int row, int c) { return V + (size_t)min(j0 + row, T - 1) * D + c * 8; });
   };
 
-  load(0, st[0]);
-  wait_vm0();
-  __syncthreads();
-  for (int J = 0; J < n_kt; ++J) {
-    if (J + 1 < n_kt) load(J + 1, st[(J + 1) & 1]);
-    const DynStage<D>& sm = st[J & 1];
+  // per-lane LDS offsets: K rows in pi order (one per k-step), V^T reads (per d-block)
+  constexpr int NDB = D / 32;
+  uint32_t koff[D / 16], voff[NDB][2];
+#pragma unroll
+  for (int kk = 0; kk < D / 16; ++kk) koff[kk] = row_off<CPR>(perm_rows(m), 2 * kk + hh);
+#pragma unroll
+  for (int db = 0; db < NDB; ++db) {
+    voff[db][0] = tr_off<CPR>(db * 32, 0, lane);
+    voff[db][1] = tr_off<CPR>(db * 32, 1, lane);
+  }
+
+  auto tile = [&](int J, const DynStage<D>& sm, DynStage<D>& nxt) {
+    if (J + 1 < n_kt) load(J + 1, nxt);
     const int j0 = J * BN;
     if (j0 <= i0w) {  // tile meets this wave's causal region
       // S^T for keys j0 .. j0+63: two independent 32-key chains, interleaved
       f32x16 s[2] = {f32x16{}, f32x16{}};
-      pipelined<D / 8>(
-          [&](int x) { return lds_row_operand<CPR>(sm.k, (x & 1) * 32 + perm_rows(m), 2 * (x >> 1) + hh); },
-          [&](int x, const bf16x8& a) { s[x & 1] = mfma32(a, qf[x >> 1], s[x & 1]); });
+      pipelined<D / 8>([&](int x) { return lds_row<CPR>(sm.k, (x & 1) * 32, koff[x >> 1]); },
+                       [&](int x, const bf16x8& a) { s[x & 1] = mfma32(a, qf[x >> 1], s[x & 1]); });
       if (j0 + BN - 1 > i0w) {  // diagonal tile: keys after the query get -inf
         const int lim = i - j0 - 8 * hh;  // key offset kb*32 + acc_pos(r, hh) > i - j0
 #pragma unroll
@@ -152,7 +158,7 @@ __device__ void dyn_item(const FwdParams& p, int b, int h, int qt, unsigned char
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
         for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb][r]);
-      const float msub = online_rescale<D / 32>(mx, p.c, m_used, l, o);
+      const float msub = online_rescale<NDB>(mx, p.c, m_used, l, o);
       bf16x8 pb[4];
 #pragma unroll
       for (int ks = 0; ks < 4; ++ks) {
@@ -164,14 +170,21 @@ __device__ void dyn_item(const FwdParams& p, int b, int h, int qt, unsigned char
         }
         pb[ks] = pack8(pv);
       }
-      // O^T += V^T P^T: the four d-blocks are independent accumulators
-      constexpr int NDB = D / 32;
+      // O^T += V^T P^T: the d-blocks are independent accumulators
       pipelined<4 * NDB>(
-          [&](int x) { return lds_tr_operand<CPR>(sm.v, (x / NDB) * 16, (x % NDB) * 32, lane); },
+          [&](int x) { return lds_tr<CPR>(sm.v, (x / NDB) * 16, voff[x % NDB][0], voff[x % NDB][1]); },
           [&](int x, const bf16x8& a) { o[x % NDB] = mfma32(a, pb[x / NDB], o[x % NDB]); });
     }
     wait_vm0();
     __syncthreads();
+  };
+
+  load(0, st[0]);
+  wait_vm0();
+  __syncthreads();
+  for (int J = 0; J < n_kt; J += 2) {  // unrolled by two: the LDS stage is a constant
+    tile(J, st[0], st[1]);
+    if (J + 1 < n_kt) tile(J + 1, st[1], st[0]);
   }
 
   const float lt = l + wave_shfl_xor32(l);
@@ -234,13 +247,15 @@ __device__ void frz_item(const FwdParams& p, int h, int chunk, int qt, unsigned 
     else if (t < BN + BM + BN - 1) sm.rw[t - BN] = treg;
   };
 
-  load(0, st[0]);
-  store_tables(st[0]);
-  wait_vm0();
-  __syncthreads();
-  for (int J = 0; J < n_kt; ++J) {
-    if (J + 1 < n_kt) load(J + 1, st[(J + 1) & 1]);
-    const FrzStage& sm = st[J & 1];
+  uint32_t voff[FCOLS / 32][2];
+#pragma unroll
+  for (int cb = 0; cb < FCOLS / 32; ++cb) {
+    voff[cb][0] = tr_off<CPR>(cb * 32, 0, lane);
+    voff[cb][1] = tr_off<CPR>(cb * 32, 1, lane);
+  }
+
+  auto tile = [&](int J, const FrzStage& sm, FrzStage& nxt) {
+    if (J + 1 < n_kt) load(J + 1, nxt);
     const int j0 = J * BN;
     if (j0 <= i0w) {
       // logits alpha(j) + rho(i - j) in log2 units; the distance window index of
@@ -264,13 +279,22 @@ __device__ void frz_item(const FwdParams& p, int h, int chunk, int qt, unsigned 
           l += pv[e];
         }
         const bf16x8 pb = pack8(pv);
-        pipelined<FCOLS / 32>([&](int cb) { return lds_tr_operand<CPR>(sm.v, ks * 16, cb * 32, lane); },
+        pipelined<FCOLS / 32>([&](int cb) { return lds_tr<CPR>(sm.v, ks * 16, voff[cb][0], voff[cb][1]); },
                               [&](int cb, const bf16x8& a) { o[cb] = mfma32(a, pb, o[cb]); });
       }
     }
-    if (J + 1 < n_kt) store_tables(st[(J + 1) & 1]);
+    if (J + 1 < n_kt) store_tables(nxt);
     wait_vm0();
     __syncthreads();
+  };
+
+  load(0, st[0]);
+  store_tables(st[0]);
+  wait_vm0();
+  __syncthreads();
+  for (int J = 0; J < n_kt; J += 2) {  // unrolled by two: the LDS stage is a constant
+    tile(J, st[0], st[1]);
+    if (J + 1 < n_kt) tile(J + 1, st[1], st[0]);
   }
 
   const float lt = l + wave_shfl_xor32(l);

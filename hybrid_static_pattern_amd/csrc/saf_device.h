@@ -64,14 +64,17 @@ __device__ __forceinline__ int swz_tr(int row) { return (row ^ (row >> 3)) & 7; 
 // A tile is row-major in LDS, CPR 16-byte chunks per row, and chunk c of row r is stored
 // at position c ^ swz<CPR>(r). Two read patterns use the same tiles:
 //   * ds_read_b128 of rows in pi order (an MFMA A operand whose rows are the tile rows):
-//     8 consecutive lanes read rows {0,1,2,3,8,9,10,11} (+4, +16, ...) at one chunk;
+//     16 consecutive lanes read rows {0,1,2,3,8,9,10,11,4,5,6,7,12,13,14,15} (+16) at one
+//     logical chunk;
 //   * ds_read_b64_tr_b16 (an operand whose rows are the tile columns, see lds_tr_operand):
-//     one instruction reads rows {0..3, 8..11} (+ base) over 64 bytes each.
-// The swizzle gives the 8 rows of the first pattern 8 distinct chunk positions and
-// spreads the second over all banks (each 512-byte read needs two LDS cycles anyway).
+//     lanes 0-31 read rows 0..3 and lanes 32-63 rows 8..11 (+ base), 64 bytes each.
+// With 64 four-byte banks (256 bytes per cycle) the swizzle puts the 16 rows of the first
+// pattern on 16 distinct chunk positions, and the four rows of each half-wave of the second
+// on four distinct 64-byte groups. 256-byte rows (CPR 16) all start at bank 0; 128-byte
+// rows (CPR 8) alternate between the two bank halves.
 template <int CPR>
 __device__ __forceinline__ int swz(int row) {
-  return CPR >= 16 ? (((row & 3) << 2) | ((row >> 3) & 1)) : ((row & 3) | (((row >> 3) & 1) << 2));
+  return CPR >= 16 ? (((row & 3) << 2) | ((row >> 2) & 3)) : ((((row >> 1) & 1) << 2) | ((row >> 2) & 3));
 }
 
 // element offset of (row, col) in a swizzled tile with CPR chunks per row
@@ -117,19 +120,32 @@ __device__ __forceinline__ void tile_load(bf16* tile, Src src) {
   }
 }
 
-// MFMA operand (8 bf16) whose row index runs along the tile's columns: lane l receives
-// tile[row0 + 8 (l / 32) + e][col0 + l % 32] for e = 0..7, read with two
-// ds_read_b64_tr_b16. Within each 16-lane group, the transposing read hands lane i the
-// (i mod 4)-th element of the 8 bytes addressed by lane 4k + i/4 into slot k, so each lane
-// addresses 4 consecutive columns of row row0 + 8 (l / 32) + (l / 4) % 4 (+4 for e = 4..7).
+// Transposed operand reads. An MFMA operand (8 bf16) whose row index runs along the
+// tile's columns: lane l receives tile[row0 + 8 (l / 32) + e][col0 + l % 32] for e = 0..7,
+// read with two ds_read_b64_tr_b16. Within each 16-lane group, the transposing read hands
+// lane i the (i mod 4)-th element of the 8 bytes addressed by lane 4k + i/4 into slot k, so
+// each lane addresses 4 consecutive columns of row row0 + 8 (l / 32) + (l / 4) % 4 (+4 for
+// e = 4..7).
+//
+// The swizzle depends on row & 15 only, so for row0 a multiple of 16 the address is a
+// per-lane offset (for row0 = 0; tr_off) plus the constant row0 * row bytes, which the
+// reads take as an immediate. Callers compute tr_off once per column block.
 typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+
 template <int CPR>
-__device__ __forceinline__ bf16x8 lds_tr_operand(const bf16* tile, int row0, int col0, int lane) {
-  const int row = row0 + 8 * (lane >> 5) + ((lane >> 2) & 3);
+__device__ __forceinline__ uint32_t tr_off(int col0, int half, int lane) {
+  const int row = 8 * (lane >> 5) + ((lane >> 2) & 3) + 4 * half;
   const int col = col0 + 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
-  typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
-  const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(tile + tile_off<CPR>(row, col)));
-  const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(tile + tile_off<CPR>(row + 4, col)));
+  return 2u * (uint32_t)tile_off<CPR>(row, col);
+}
+
+// tile: LDS tile base; row0: multiple of 16; off_lo / off_hi: tr_off(col0, 0 / 1, lane)
+template <int CPR>
+__device__ __forceinline__ bf16x8 lds_tr(const bf16* tile, int row0, uint32_t off_lo, uint32_t off_hi) {
+  const char* base = reinterpret_cast<const char*>(tile) + row0 * (CPR * 16);
+  const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(base + off_lo));
+  const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(base + off_hi));
   u32x4 r;
   r[0] = __builtin_bit_cast(u32x2, lo)[0];
   r[1] = __builtin_bit_cast(u32x2, lo)[1];
@@ -138,11 +154,18 @@ __device__ __forceinline__ bf16x8 lds_tr_operand(const bf16* tile, int row0, int
   return __builtin_bit_cast(bf16x8, r);
 }
 
-// MFMA operand (8 bf16) whose row index is the tile row: lane l receives
-// tile[row][8 * chunk .. 8 * chunk + 7] (one ds_read_b128).
+// Row operand reads: lane l receives tile[row][8 chunk .. 8 chunk + 7] (one ds_read_b128).
+// For rows row0 + r with r < 16... the swizzle again depends on the row's low 4 bits only:
+// row_off(r, chunk) is the per-lane offset for row0 = 0, and row0 (a multiple of 16) adds a
+// constant.
 template <int CPR>
-__device__ __forceinline__ bf16x8 lds_row_operand(const bf16* tile, int row, int chunk) {
-  return *reinterpret_cast<const bf16x8*>(tile + row * (CPR * 8) + ((chunk ^ swz<CPR>(row)) << 3));
+__device__ __forceinline__ uint32_t row_off(int row, int chunk) {
+  return 16u * (uint32_t)(row * CPR + (chunk ^ swz<CPR>(row)));
+}
+
+template <int CPR>
+__device__ __forceinline__ bf16x8 lds_row(const bf16* tile, int row0, uint32_t off) {
+  return *reinterpret_cast<const bf16x8*>(reinterpret_cast<const char*>(tile) + row0 * (CPR * 16) + off);
 }
 
 // Runs mma(x, operand) for x = 0..N-1 with the LDS read of operand x issued two products

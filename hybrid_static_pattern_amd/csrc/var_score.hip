@@ -46,15 +46,21 @@ __device__ __forceinline__ void load_k(const bf16* K, int j0, int T, KTile<D>& t
   tile_load<D / 8, BN>(tile.k, [&](int row, int c) { return K + (size_t)min(j0 + row, T - 1) * D + c * 8; });
 }
 
-// S^T tile (64 keys x this lane's query) for the 64-key tile held in LDS.
+// S^T tile (64 keys x this lane's query) for the 64-key tile held in LDS; koff: per-lane
+// offsets of the pi-ordered key rows, one per k-step.
 template <int D>
-__device__ __forceinline__ void scores(const bf16* ks, const bf16x8 (&qf)[D / 16], int m, int hh,
+__device__ __forceinline__ void scores(const bf16* ks, const bf16x8 (&qf)[D / 16], const uint32_t (&koff)[D / 16],
                                        f32x16 (&s)[2]) {
   s[0] = f32x16{};
   s[1] = f32x16{};
-  pipelined<D / 8>(
-      [&](int x) { return lds_row_operand<D / 8>(ks, (x & 1) * 32 + perm_rows(m), 2 * (x >> 1) + hh); },
-      [&](int x, const bf16x8& a) { s[x & 1] = mfma32(a, qf[x >> 1], s[x & 1]); });
+  pipelined<D / 8>([&](int x) { return lds_row<D / 8>(ks, (x & 1) * 32, koff[x >> 1]); },
+                   [&](int x, const bf16x8& a) { s[x & 1] = mfma32(a, qf[x >> 1], s[x & 1]); });
+}
+
+template <int D>
+__device__ __forceinline__ void key_offsets(int m, int hh, uint32_t (&koff)[D / 16]) {
+#pragma unroll
+  for (int kk = 0; kk < D / 16; ++kk) koff[kk] = row_off<D / 8>(perm_rows(m), 2 * kk + hh);
 }
 
 template <int D>
@@ -76,6 +82,8 @@ __global__ __launch_bounds__(NTH, 2) void var_lse_kernel(const VarParams p) {
   const int i0w = qt * BM + 32 * w, i = i0w + m;
   bf16x8 qf[D / 16];
   load_q<D>(p.q + head * D, i, T, hh, qf);
+  uint32_t koff[D / 16];
+  key_offsets<D>(m, hh, koff);
   const bf16* K = p.k + head * D;
   float mx_run = kNegInf, l = 0.f;
   const int n_kt = min(2 * qt + 2, (T + BN - 1) / BN);
@@ -87,7 +95,7 @@ __global__ __launch_bounds__(NTH, 2) void var_lse_kernel(const VarParams p) {
     const int j0 = J * BN;
     if (j0 <= i0w) {
       f32x16 s[2];
-      scores<D>(stg[J & 1].k, qf, m, hh, s);
+      scores<D>(stg[J & 1].k, qf, koff, s);
       const bool diag = j0 + BN - 1 > i0w;
       float mx = kNegInf;
 #pragma unroll
@@ -154,6 +162,8 @@ __global__ __launch_bounds__(NTH, 2) void var_welford_kernel(const VarParams p) 
   const bool active = j0 <= i0w;     // wave has causal entries in this tile
   const bool diag = j0 + BN - 1 > i0w;
   const size_t nh_stride = (size_t)p.H * T;
+  uint32_t koff[D / 16];
+  key_offsets<D>(m, hh, koff);
   load_k<D>(p.k + ((size_t)h * T) * D, j0, T, stg[0]);
   wait_vm0();
   __syncthreads();
@@ -165,7 +175,7 @@ __global__ __launch_bounds__(NTH, 2) void var_welford_kernel(const VarParams p) 
       load_q<D>(p.q + head * D, i, T, hh, qf);
       const float l2 = (i < T) ? p.lse2[head + i] : __builtin_huge_valf();
       f32x16 s[2];
-      scores<D>(stg[n & 1].k, qf, m, hh, s);
+      scores<D>(stg[n & 1].k, qf, koff, s);
       const float rn = 1.f / (float)(n + 1);
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)

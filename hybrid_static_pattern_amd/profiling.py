@@ -1,0 +1,140 @@
+"""Turns rocprofv3 counter dumps into the HBM-traffic summaries kept under profiles/.
+
+    python -m hybrid_static_pattern_amd.profiling traffic \
+        --fetch gpurun_out/pmc_C/run_counter_collection.csv \
+        --write gpurun_out/pmc_D/run_counter_collection.csv \
+        --copy-mib 256 --command "<the rocprofv3 command lines>" --out profiles/
+
+FETCH_SIZE and WRITE_SIZE are read per dispatch (KiB) for every libsaf kernel and scaled by
+the factor that makes the same counters match a plain elementwise copy of known size (the
+bench's --calib-copy-mib torch.neg kernel, which reads and writes copy-mib MiB). Each summary records a
+hash of the kernel's sources, so a reader can tell when the kernel has changed since the
+counters were taken (bench.py then reports the traffic as unknown).
+"""
+from __future__ import annotations
+
+import argparse
+import collections
+import csv
+import hashlib
+import os
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+CSRC = os.path.join(PKG, "csrc")
+
+# kernel (short name) -> source files whose text determines it
+KERNEL_SOURCES = {
+    "hybrid_fwd_kernel": ["fwd_bf16.hip", "saf_device.h"],
+    "dkdv_kernel": ["bwd_bf16.hip", "saf_device.h"],
+    "dq_kernel": ["bwd_bf16.hip", "saf_device.h"],
+    "bwd_delta_kernel": ["bwd_bf16.hip", "saf_device.h"],
+    "var_lse_kernel": ["var_score.hip", "saf_device.h"],
+    "var_welford_kernel": ["var_score.hip", "saf_device.h"],
+}
+# workload each kernel's counters are taken on (part of the summary's file name)
+KERNEL_WORKLOAD = {"var_lse_kernel": "calibration_N64_H12_T1024", "var_welford_kernel": "calibration_N64_H12_T1024"}
+DEFAULT_WORKLOAD = "1b_T8192_r25"
+# bench/prof names -> kernel short names
+PROF_TO_KERNEL = {"hybrid_fwd": "hybrid_fwd_kernel", "dkdv": "dkdv_kernel", "dq": "dq_kernel",
+                  "bwd_delta": "bwd_delta_kernel", "var_lse": "var_lse_kernel",
+                  "var_welford": "var_welford_kernel"}
+
+
+def source_hash(kernel: str) -> str:
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES[kernel]:
+        with open(os.path.join(CSRC, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def short_name(full: str) -> str:
+    if "at::native" in full:
+        return "torch_copy" if "neg" in full.lower() else "torch_other"
+    name = full.split("(")[0] if "(anonymous" not in full.split("<")[0] else full
+    for k in KERNEL_SOURCES:
+        if k in full:
+            return k
+    return name.replace("void ", "")
+
+
+def per_dispatch(path: str, counter: str):
+    """Mean counter value per dispatch for each kernel in a rocprofv3 counter CSV."""
+    tot = collections.defaultdict(float)
+    disp = collections.defaultdict(set)
+    with open(path) as f:
+        for r in csv.DictReader(f):
+            if r["Counter_Name"] != counter:
+                continue
+            k = short_name(r["Kernel_Name"])
+            tot[k] += float(r["Counter_Value"])
+            disp[k].add(r["Dispatch_Id"])
+    return {k: tot[k] / len(disp[k]) for k in tot}
+
+
+def traffic(fetch_csv: str, write_csv: str, copy_mib: int):
+    fetch = per_dispatch(fetch_csv, "FETCH_SIZE")
+    write = per_dispatch(write_csv, "WRITE_SIZE")
+    copy_kib = copy_mib * 1024.0
+    f_scale = copy_kib / fetch["torch_copy"]
+    w_scale = copy_kib / write["torch_copy"]
+    out = {}
+    for k in KERNEL_SOURCES:
+        if k in fetch and k in write:
+            out[k] = dict(fetch_bytes=fetch[k] * 1024 * f_scale, write_bytes=write[k] * 1024 * w_scale,
+                          fetch_kib_raw=fetch[k], write_kib_raw=write[k], fetch_scale=f_scale,
+                          write_scale=w_scale, source_hash=source_hash(k))
+    return out
+
+
+def summary_path(outdir: str, kernel: str) -> str:
+    return os.path.join(outdir, f"traffic_{kernel}_{KERNEL_WORKLOAD.get(kernel, DEFAULT_WORKLOAD)}.txt")
+
+
+def write_summaries(data: dict, outdir: str, command: str) -> None:
+    for k, d in data.items():
+        with open(summary_path(outdir, k), "w") as f:
+            wl = KERNEL_WORKLOAD.get(k, DEFAULT_WORKLOAD)
+            f.write(f"# HBM traffic of {k} per launch, workload {wl}\n")
+            f.write("# FETCH_SIZE and WRITE_SIZE (KiB per dispatch) scaled by the factor that makes the\n")
+            f.write("# same counters read a plain device copy of known size correctly.\n")
+            f.write(f"# command: {command}\n")
+            for key, val in d.items():
+                f.write(f"{key}: {val}\n")
+
+
+def read_summary(kernel: str, outdir: str):
+    """The committed traffic summary for `kernel`, or None if absent or taken on other sources."""
+    path = summary_path(outdir, kernel)
+    if not os.path.exists(path):
+        return None
+    d = {}
+    with open(path) as f:
+        for line in f:
+            if line.startswith("#") or ":" not in line:
+                continue
+            key, val = line.split(":", 1)
+            d[key.strip()] = val.strip()
+    if d.get("source_hash") != source_hash(kernel):
+        return None
+    return {k: (v if k == "source_hash" else float(v)) for k, v in d.items()}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    sub = ap.add_subparsers(dest="cmd", required=True)
+    t = sub.add_parser("traffic")
+    t.add_argument("--fetch", required=True)
+    t.add_argument("--write", required=True)
+    t.add_argument("--copy-mib", type=int, required=True)
+    t.add_argument("--command", default="")
+    t.add_argument("--out", default=os.path.join(os.path.dirname(PKG), "profiles"))
+    a = ap.parse_args()
+    data = traffic(a.fetch, a.write, a.copy_mib)
+    write_summaries(data, a.out, a.command)
+    for k, d in data.items():
+        print(f"{k}: fetch {d['fetch_bytes'] / 1e6:.1f} MB, write {d['write_bytes'] / 1e6:.1f} MB per launch")
+
+
+if __name__ == "__main__":
+    main()
