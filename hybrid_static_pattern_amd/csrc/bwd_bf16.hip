@@ -10,8 +10,8 @@
 //
 // Kernels, in launch order:
 //   bwd_delta   delta for ordinary heads (one 8-lane group per row);
-//   dkdv        one launch holding two kinds of work items:
-//       ordinary (b, h, 128-key tile): each wave keeps 32 keys (K, V fragments and the
+//   dkdv        one launch of 8-wave workgroups on 16x16x32 MFMAs, two kinds of items:
+//       ordinary (b, h, 128-key tile): each wave keeps 16 keys (K, V fragments and the
 //           fp32 dK, dV tiles) in registers and walks the 64-query steps from the
 //           diagonal down; S and dP are computed with the key as the lane index so P
 //           and dS feed the dV and dK products straight from registers;
@@ -108,129 +108,312 @@ __global__ __launch_bounds__(256) void bwd_delta_kernel(const DeltaParams p) {
 
 // ---------------------------------------------------------------- dK / dV
 
+// ---------------------------------------------------------------- dK / dV, ordinary heads
+//
+// 8 waves x 16 keys per 128-key workgroup on v_mfma_f32_16x16x32_bf16, so that a wave's
+// fp32 dK and dV tiles (16 keys x D) take 64 registers and two waves fit on each SIMD: while
+// one wave runs its softmax arithmetic the other keeps the matrix cores busy.
+//   16x16x32 operand layout: A (16 x 32): lane l holds A[l % 16][8 (l / 16) + e];
+//   B (32 x 16): lane l holds B[8 (l / 16) + e][l % 16]; C (16 x 16): lane l, register r
+//   holds C[4 (l / 16) + r][l % 16].
+// S = Q K^T is computed in two 16-query halves h whose A rows are the step's Q rows
+// 8 (rho / 4) + 4 h + rho % 4 (rho = MFMA row): then register r of half h in lane group g
+// holds query 8 g + 4 h + r, and the 8 values of lane group g are exactly the 8 consecutive
+// queries 8 g .. 8 g + 7 that the P^T operand of the dV product needs (k index e = 4 h + r).
+
+constexpr int NW16 = 8;            // waves per ordinary dK/dV workgroup
+constexpr int NTH16 = 64 * NW16;
+
+__device__ __forceinline__ f32x4 mfma16(const bf16x8& a, const bf16x8& b, const f32x4& c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+// Chunk swizzle for the 16-lane read patterns of this kernel (period 32 in the row):
+//   A rows: each 16-lane group reads rows {0..3, 8..11, 16..19, 24..27} (+4, +32) at one chunk;
+//   B via ds_read_b64_tr_b16: each half-wave reads rows {0..3, 8..11} (+16, +4, +32) over
+//   32 bytes. Both map to distinct banks with 64 four-byte banks.
+template <int CPR>
+__device__ __forceinline__ int swz16(int r) {
+  return CPR >= 16 ? (((r & 3) << 1) | (((r >> 3) & 1) << 3) | ((r >> 4) & 1))
+                   : (((r >> 4) & 1) | (((r >> 1) & 1) << 1) | (((r >> 3) & 1) << 2));
+}
+
+template <int CPR, int NR, class Src>
+__device__ __forceinline__ void tile_load16(bf16* tile, Src src) {
+  constexpr int NCH = NR * CPR;
+  constexpr int PERW = NCH / 64 / NW16;
+  static_assert(NCH % (64 * NW16) == 0, "tile must split evenly over the waves");
+  const int w = wave_id(), lane = lane_id();
+  const uint32_t base = lds_addr(tile);
+#pragma unroll
+  for (int x = 0; x < PERW; ++x) {
+    const int blk = w * PERW + x;
+    const int pch = blk * 64 + lane;
+    const int row = pch / CPR;
+    const int c = (pch % CPR) ^ swz16<CPR>(row);
+    g2lds16(src(row, c), base + blk * 1024);
+  }
+}
+
 template <int D>
-struct DkdvSmem {
-  bf16 qs[BMQ * D];   // Q rows of the step, swizzled (swz<D/8>); also read transposed
-  bf16 gs[BMQ * D];   // dO rows of the step; also read transposed
+struct Dkdv16Stage {
+  bf16 qs[BMQ * D];   // Q rows of the step, swizzled (swz16)
+  bf16 gs[BMQ * D];   // dO rows of the step
   float ls[BMQ];      // lse * log2(e) (+inf past T)
   float dl[BMQ];      // delta
 };
 
-struct FrzBwdSmem {
-  bf16 gs[BMQ * FCOLS];   // folded dO [q][column], swizzled; read transposed
+struct Frz16Stage {
+  bf16 gs[BMQ * FCOLS];   // folded dO [q][column], swizzled (swz16); read transposed
   float lz[BMQ];          // log Z * log2(e) (+inf past T)
   float rw[BMQ + BNK];    // rho * log2(e) over the step's distance window
 };
 
 template <int D>
-constexpr int dkdv_smem_bytes() {  // per stage
-  return sizeof(DkdvSmem<D>) > sizeof(FrzBwdSmem) ? (int)sizeof(DkdvSmem<D>) : (int)sizeof(FrzBwdSmem);
+constexpr int dkdv16_smem_bytes() {
+  return 2 * (sizeof(Dkdv16Stage<D>) > sizeof(Frz16Stage) ? (int)sizeof(Dkdv16Stage<D>) : (int)sizeof(Frz16Stage));
+}
+
+// Frozen item (h, 128-key tile, column chunk): dV_b[j] = sum_{i>=j} P(i,j) dO_b[i] for the
+// batch folded into up to 256 columns. Each wave keeps 16 keys x 256 columns of fp32 dV;
+// P^T is regenerated per lane from alpha, rho and log Z (entries for j > i come out as 0 from
+// the -inf distances of the window) and split into bf16 high and low parts.
+template <int D>
+__device__ void dv_frz16(const BwdParams& p, int h, int chunk, int kt, unsigned char* smem_raw) {
+  constexpr int CPR = FCOLS / 8;
+  constexpr int NCB = FCOLS / 16;
+  Frz16Stage* stg = reinterpret_cast<Frz16Stage*>(smem_raw);
+  const int t = threadIdx.x, lane = lane_id(), w = wave_id();
+  const int n = lane & 15, g = lane >> 4;
+  const int T = p.T, H = p.H, B = p.B;
+  const int col0 = chunk * FCOLS;
+  const int ncols = min(FCOLS, B * D - col0);
+  const int kbase = kt * BNK, k0w = kbase + 16 * w, j = k0w + n;
+  const float a2 = (j < T) ? p.alpha[(size_t)h * p.tab_stride + j] * kLog2e : kNegInf;
+  const float* rho = p.rho + (size_t)h * p.tab_stride;
+
+  f32x4 dv[NCB];
+#pragma unroll
+  for (int cb = 0; cb < NCB; ++cb) dv[cb] = f32x4{0.f, 0.f, 0.f, 0.f};
+  uint32_t goff[NCB][2];
+#pragma unroll
+  for (int cb = 0; cb < NCB; ++cb)
+#pragma unroll
+    for (int hf = 0; hf < 2; ++hf) {
+      const int row = 8 * g + ((lane >> 2) & 3) + 4 * hf, col = 16 * cb + 4 * (lane & 3);
+      goff[cb][hf] = 2u * (uint32_t)(row * FCOLS + (((col >> 3) ^ swz16<CPR>(row)) << 3) + (col & 7));
+    }
+
+  const int n_steps = (T - kbase + BMQ - 1) / BMQ;
+  constexpr int NTAB = BMQ + BMQ + BNK - 1;   // lz for the step's queries, then the rho window
+  static_assert(NTAB <= NTH16, "one table entry per thread");
+  float treg = 0.f;
+  auto load = [&](int st, Frz16Stage& sm) {
+    const int i0 = kbase + st * BMQ;
+    tile_load16<CPR, BMQ>(sm.gs, [&](int row, int c) {
+      const int col = col0 + c * 8;
+      const int bb = min(col / D, B - 1), d = col % D;
+      return p.dO + (((size_t)bb * H + h) * T + min(i0 + row, T - 1)) * D + d;
+    });
+    if (t < BMQ) {
+      const int i = i0 + t;
+      treg = (i < T) ? p.lse[(size_t)h * T + i] * kLog2e : __builtin_huge_valf();
+    } else if (t < NTAB) {
+      const int dd = i0 - kbase - (BNK - 1) + (t - BMQ);
+      treg = (dd >= 0 && dd < T) ? rho[dd] * kLog2e : kNegInf;
+    }
+  };
+  auto store_tables = [&](Frz16Stage& sm) {
+    if (t < BMQ) sm.lz[t] = treg;
+    else if (t < NTAB) sm.rw[t - BMQ] = treg;
+  };
+
+  auto step = [&](int st, const Frz16Stage& sm, Frz16Stage& nxt) {
+    if (st + 1 < n_steps) load(st + 1, nxt);
+#pragma unroll
+    for (int qb = 0; qb < BMQ / 32; ++qb) {
+      if (st * (BMQ / 32) + qb < (w >> 1)) continue;   // every query before this wave's keys
+      // queries i0 + qb*32 + 8 g + e; window index of distance i - j is
+      // (qb*32 + 8 g + e) - (16 w + n) + BNK - 1
+      const int qofs = qb * 32 + 8 * g;
+      const int rbase = qofs - (16 * w + n) + BNK - 1;
+      float ph[8], pl[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const float pv = __builtin_amdgcn_exp2f(a2 + sm.rw[rbase + e] - sm.lz[qofs + e]);
+        const bf16 hi = (bf16)pv;
+        ph[e] = (float)hi;
+        pl[e] = pv - ph[e];
+      }
+      const bf16x8 ahi = pack8(ph), alo = pack8(pl);
+      pipelined<NCB>(
+          [&](int cb) {
+            const char* base = reinterpret_cast<const char*>(sm.gs) + qb * 32 * (CPR * 16);
+            const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(base + goff[cb][0]));
+            const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(base + goff[cb][1]));
+            u32x4 r;
+            r[0] = __builtin_bit_cast(u32x2, lo)[0];
+            r[1] = __builtin_bit_cast(u32x2, lo)[1];
+            r[2] = __builtin_bit_cast(u32x2, hi)[0];
+            r[3] = __builtin_bit_cast(u32x2, hi)[1];
+            return __builtin_bit_cast(bf16x8, r);
+          },
+          [&](int cb, const bf16x8& bg) {
+            dv[cb] = mfma16(ahi, bg, dv[cb]);
+            dv[cb] = mfma16(alo, bg, dv[cb]);
+          });
+    }
+    if (st + 1 < n_steps) store_tables(nxt);
+    wait_vm0();
+    __syncthreads();
+  };
+
+  load(0, stg[0]);
+  store_tables(stg[0]);
+  wait_vm0();
+  __syncthreads();
+  for (int st = 0; st < n_steps; st += 2) {  // unrolled by two: the LDS stage is a constant
+    step(st, stg[0], stg[1]);
+    if (st + 1 < n_steps) step(st + 1, stg[1], stg[0]);
+  }
+
+#pragma unroll
+  for (int cb = 0; cb < NCB; ++cb) {
+    const int col = col0 + 16 * cb + n;
+    if (16 * cb >= ncols) continue;
+    const int bb = col / D, d = col % D;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int key = k0w + 4 * g + r;
+      if (key < T) p.dv[(((size_t)bb * H + h) * T + key) * D + d] = dv[cb][r];
+    }
+  }
 }
 
 template <int D>
-__device__ void dkdv_dyn(const BwdParams& p, int b, int h, int kt, unsigned char* smem_raw) {
+__device__ void dkdv_dyn16(const BwdParams& p, int b, int h, int kt, unsigned char* smem_raw) {
   constexpr int CPR = D / 8;
-  constexpr int NDB = D / 32;
-  DkdvSmem<D>* stg = reinterpret_cast<DkdvSmem<D>*>(smem_raw);
+  constexpr int NKS = D / 32;   // 32-wide k-steps over d
+  constexpr int NDB = D / 16;   // 16-wide d blocks of dK, dV
+  Dkdv16Stage<D>* stg = reinterpret_cast<Dkdv16Stage<D>*>(smem_raw);
   const int t = threadIdx.x, lane = lane_id(), w = wave_id();
-  const int m = lane & 31, hh = lane >> 5;
+  const int n = lane & 15, g = lane >> 4;
   const int T = p.T;
   const size_t head = ((size_t)b * p.H + h) * (size_t)T;
   const bf16* Q = p.q + head * D;
   const bf16* G = p.dO + head * D;
-  const int k0w = kt * BNK + 32 * w;
-  const int j = k0w + m;
-  bf16x8 kf[D / 16], vf[D / 16];
+  const int k0w = kt * BNK + 16 * w;
+  const int j = k0w + n;
+
+  bf16x8 kf[NKS], vf[NKS];   // B operands: K[j][32 ks + 8 g + e], V likewise
 #pragma unroll
-  for (int kk = 0; kk < D / 16; ++kk) {
-    const size_t off = (head + min(j, T - 1)) * D + kk * 16 + hh * 8;
-    kf[kk] = *reinterpret_cast<const bf16x8*>(p.k + off);
-    vf[kk] = *reinterpret_cast<const bf16x8*>(p.v + off);
+  for (int ks = 0; ks < NKS; ++ks) {
+    const size_t off = (head + min(j, T - 1)) * D + 32 * ks + 8 * g;
+    kf[ks] = *reinterpret_cast<const bf16x8*>(p.k + off);
+    vf[ks] = *reinterpret_cast<const bf16x8*>(p.v + off);
   }
-  // per-lane LDS offsets: Q / dO rows in pi order (per k-step), transposed dO^T / Q^T reads
-  // (per d-block); the two tiles share a layout and hence the offsets
-  uint32_t qoff[D / 16], toff[NDB][2];
-#pragma unroll
-  for (int kk = 0; kk < D / 16; ++kk) qoff[kk] = row_off<CPR>(perm_rows(m), 2 * kk + hh);
+  f32x4 dv[NDB], dk[NDB];
 #pragma unroll
   for (int db = 0; db < NDB; ++db) {
-    toff[db][0] = tr_off<CPR>(db * 32, 0, lane);
-    toff[db][1] = tr_off<CPR>(db * 32, 1, lane);
+    dv[db] = f32x4{0.f, 0.f, 0.f, 0.f};
+    dk[db] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
-  f32x16 dv[NDB], dk[NDB];
+  // per-lane byte offsets within a 32-row block of a tile (constant multiples of 32 rows
+  // keep the swizzle): A-row reads per (half, k-step), transposed B reads per (d-block, half)
+  uint32_t roff[2][NKS], toff[NDB][2];
 #pragma unroll
-  for (int db = 0; db < NDB; ++db) {
-    dv[db] = f32x16{};
-    dk[db] = f32x16{};
-  }
+  for (int hf = 0; hf < 2; ++hf)
+#pragma unroll
+    for (int ks = 0; ks < NKS; ++ks) {
+      const int row = 8 * (n >> 2) + 4 * hf + (n & 3), chunk = 4 * ks + g;
+      roff[hf][ks] = 16u * (uint32_t)(row * CPR + (chunk ^ swz16<CPR>(row)));
+    }
+#pragma unroll
+  for (int db = 0; db < NDB; ++db)
+#pragma unroll
+    for (int hf = 0; hf < 2; ++hf) {
+      const int row = 8 * g + ((lane >> 2) & 3) + 4 * hf, col = 16 * db + 4 * (lane & 3);
+      toff[db][hf] = 2u * (uint32_t)(row * D + (((col >> 3) ^ swz16<CPR>(row)) << 3) + (col & 7));
+    }
 
   const int i_start = kt * BNK;
   const int n_steps = (T - i_start + BMQ - 1) / BMQ;
   float lreg = 0.f, dreg = 0.f;
-  auto load = [&](int st, DkdvSmem<D>& sm) {
+  auto load = [&](int st, Dkdv16Stage<D>& sm) {
     const int i0 = i_start + st * BMQ;
-    tile_load<CPR, BMQ>(sm.qs, [&](int row, int c) { return Q + (size_t)min(i0 + row, T - 1) * D + c * 8; });
-    tile_load<CPR, BMQ>(sm.gs, [&](int row, int c) { return G + (size_t)min(i0 + row, T - 1) * D + c * 8; });
+    tile_load16<CPR, BMQ>(sm.qs, [&](int row, int c) { return Q + (size_t)min(i0 + row, T - 1) * D + c * 8; });
+    tile_load16<CPR, BMQ>(sm.gs, [&](int row, int c) { return G + (size_t)min(i0 + row, T - 1) * D + c * 8; });
     if (t < BMQ) {
       const int i = i0 + t;
       lreg = (i < T) ? p.lse[head + i] * kLog2e : __builtin_huge_valf();
       dreg = (i < T) ? p.delta[head + i] : 0.f;
     }
   };
-  auto store_rows = [&](DkdvSmem<D>& sm) {
+  auto store_rows = [&](Dkdv16Stage<D>& sm) {
     if (t < BMQ) {
       sm.ls[t] = lreg;
       sm.dl[t] = dreg;
     }
   };
-
-  // One 32-query block: S and dP for this wave's 32 keys, P and dS in registers, then the
-  // dV and dK products. `diag` masks queries before the key (the block on the diagonal).
-  auto block = [&](const DkdvSmem<D>& sm, int qb, bool diag) {
-    // S = Q K^T and dP = dO V^T, two independent chains interleaved
-    f32x16 sd[2] = {f32x16{}, f32x16{}};
-    pipelined<D / 8>(
-        [&](int x) { return lds_row<CPR>((x & 1) ? sm.gs : sm.qs, qb * 32, qoff[x >> 1]); },
-        [&](int x, const bf16x8& a) { sd[x & 1] = mfma32(a, (x & 1) ? vf[x >> 1] : kf[x >> 1], sd[x & 1]); });
-    float pr[16], dsr[16];
-#pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int qi = qb * 32 + acc_pos(r, hh);
-      float pv = __builtin_amdgcn_exp2f(__builtin_fmaf(sd[0][r], p.c, -sm.ls[qi]));
-      if (diag && acc_pos(r, hh) < m) pv = 0.f;  // query before this lane's key
-      pr[r] = pv;
-      dsr[r] = pv * (sd[1][r] - sm.dl[qi]);
-    }
-    bf16x8 pa[2], da[2];
-#pragma unroll
-    for (int sk = 0; sk < 2; ++sk) {
-      pa[sk] = pack8(pr + 8 * sk);
-      da[sk] = pack8(dsr + 8 * sk);
-    }
-    // dV += P^T dO, dK += dS^T Q; the dO^T / Q^T operands are transposed LDS reads
-    pipelined<4 * NDB>(
-        [&](int x) {
-          const int sk = x / (2 * NDB), db = (x / 2) % NDB;
-          return lds_tr<CPR>((x & 1) ? sm.qs : sm.gs, qb * 32 + sk * 16, toff[db][0], toff[db][1]);
-        },
-        [&](int x, const bf16x8& bop) {
-          const int sk = x / (2 * NDB), db = (x / 2) % NDB;
-          if (x & 1) dk[db] = mfma32(da[sk], bop, dk[db]);
-          else dv[db] = mfma32(pa[sk], bop, dv[db]);
-        });
+  auto lds_a = [](const bf16* tile, int qb, uint32_t off) {
+    return *reinterpret_cast<const bf16x8*>(reinterpret_cast<const char*>(tile) + qb * 32 * (CPR * 16) + off);
+  };
+  auto lds_b = [](const bf16* tile, int qb, uint32_t off_lo, uint32_t off_hi) {
+    const char* base = reinterpret_cast<const char*>(tile) + qb * 32 * (CPR * 16);
+    const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(base + off_lo));
+    const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(base + off_hi));
+    u32x4 r;
+    r[0] = __builtin_bit_cast(u32x2, lo)[0];
+    r[1] = __builtin_bit_cast(u32x2, lo)[1];
+    r[2] = __builtin_bit_cast(u32x2, hi)[0];
+    r[3] = __builtin_bit_cast(u32x2, hi)[1];
+    return __builtin_bit_cast(bf16x8, r);
   };
 
-  auto step = [&](int st, const DkdvSmem<D>& sm, DkdvSmem<D>& nxt) {
+  // one 32-query block: S, dP (two halves each), P and dS in registers, dV and dK.
+  // `diag` marks the block on the diagonal: a query before this lane's key (query offset
+  // 8 g + 4 h + r in the block, key offset 16 (w & 1) + n) gets zero weight.
+  const int kdiag = 16 * (w & 1) + n;
+  auto block = [&](const Dkdv16Stage<D>& sm, int qb, bool diag) {
+    f32x4 sc[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
+    f32x4 dp[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
+    pipelined<4 * NKS>(
+        [&](int x) { return lds_a((x & 1) ? sm.gs : sm.qs, qb, roff[(x >> 1) & 1][x >> 2]); },
+        [&](int x, const bf16x8& a) {
+          const int hf = (x >> 1) & 1, ks = x >> 2;
+          if (x & 1) dp[hf] = mfma16(a, vf[ks], dp[hf]);
+          else sc[hf] = mfma16(a, kf[ks], sc[hf]);
+        });
+    float pr[8], dsr[8];
+#pragma unroll
+    for (int hf = 0; hf < 2; ++hf)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int qi = qb * 32 + 8 * g + 4 * hf + r;
+        float pv = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[hf][r], p.c, -sm.ls[qi]));
+        if (diag && 8 * g + 4 * hf + r < kdiag) pv = 0.f;
+        pr[4 * hf + r] = pv;
+        dsr[4 * hf + r] = pv * (dp[hf][r] - sm.dl[qi]);
+      }
+    const bf16x8 pa = pack8(pr), da = pack8(dsr);
+    // dV += P^T dO, dK += dS^T Q over the block's 32 queries (one 16x16x32 product each)
+    pipelined<2 * NDB>([&](int x) { return lds_b((x & 1) ? sm.qs : sm.gs, qb, toff[x >> 1][0], toff[x >> 1][1]); },
+                       [&](int x, const bf16x8& bop) {
+                         if (x & 1) dk[x >> 1] = mfma16(da, bop, dk[x >> 1]);
+                         else dv[x >> 1] = mfma16(pa, bop, dv[x >> 1]);
+                       });
+  };
+
+  auto step = [&](int st, const Dkdv16Stage<D>& sm, Dkdv16Stage<D>& nxt) {
     if (st + 1 < n_steps) load(st + 1, nxt);
     if (st * BMQ < BNK) {
-      // steps on the diagonal: query block gq (32 queries) of the key tile meets this
-      // wave's keys (32 w .. 32 w + 31 within the tile) only for gq >= w, and gq == w needs
-      // the causal mask
+      // steps on the diagonal: 32-query block gq of the key tile meets this wave's keys
+      // (16 w .. 16 w + 15 within the tile) for gq >= w / 2, and gq == w / 2 needs the mask
 #pragma unroll
       for (int qb = 0; qb < BMQ / 32; ++qb) {
         const int gq = st * (BMQ / 32) + qb;
-        if (gq < w) continue;
-        block(sm, qb, gq == w);
+        if (gq < (w >> 1)) continue;
+        block(sm, qb, gq == (w >> 1));
       }
     } else {
 #pragma unroll
@@ -253,141 +436,29 @@ __device__ void dkdv_dyn(const BwdParams& p, int b, int h, int kt, unsigned char
 #pragma unroll
   for (int db = 0; db < NDB; ++db)
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int key = k0w + acc_row(r, hh);
+    for (int r = 0; r < 4; ++r) {
+      const int key = k0w + 4 * g + r;
       if (key < T) {
-        const size_t off = (head + key) * D + db * 32 + m;
+        const size_t off = (head + key) * D + 16 * db + n;
         p.dv[off] = dv[db][r];
         p.dk[off] = dk[db][r] * p.scale;
       }
     }
 }
 
+// Both item kinds in one launch, heaviest key tile first: per key tile, the ordinary
+// (b, h) items, then the frozen (h, column chunk) items.
 template <int D>
-__device__ void dkdv_frz(const BwdParams& p, int h, int chunk, int kt, unsigned char* smem_raw) {
-  constexpr int CPR = FCOLS / 8;
-  FrzBwdSmem* stg = reinterpret_cast<FrzBwdSmem*>(smem_raw);
-  const int t = threadIdx.x, lane = lane_id(), w = wave_id();
-  const int m = lane & 31, hh = lane >> 5;
-  const int T = p.T, H = p.H, B = p.B;
-  const int col0 = chunk * FCOLS;
-  const int ncols = min(FCOLS, B * D - col0);
-  const int kbase = kt * BNK, k0w = kbase + 32 * w, j = k0w + m;
-  const float a2 = (j < T) ? p.alpha[(size_t)h * p.tab_stride + j] * kLog2e : kNegInf;
-  const float* rho = p.rho + (size_t)h * p.tab_stride;
-
-  // Columns past B*D (a partial last chunk) read clamped, valid data and are not stored.
-  f32x16 dv[FCOLS / 32];
-#pragma unroll
-  for (int cb = 0; cb < FCOLS / 32; ++cb) dv[cb] = f32x16{};
-
-  const int n_steps = (T - kbase + BMQ - 1) / BMQ;
-  // per step: lz for BMQ queries, then the rho window of BMQ + BNK - 1 distances
-  constexpr int NTAB = BMQ + BMQ + BNK - 1;
-  float treg[(NTAB + NTH - 1) / NTH];
-  auto load = [&](int st, FrzBwdSmem& sm) {
-    const int i0 = kbase + st * BMQ;
-    tile_load<CPR, BMQ>(sm.gs, [&](int row, int c) {
-      const int col = col0 + c * 8;
-      const int bb = min(col / D, B - 1), d = col % D;
-      return p.dO + (((size_t)bb * H + h) * T + min(i0 + row, T - 1)) * D + d;
-    });
-#pragma unroll
-    for (int y = 0; y < (NTAB + NTH - 1) / NTH; ++y) {
-      const int x = t + y * NTH;
-      if (x < BMQ) {
-        const int i = i0 + x;
-        treg[y] = (i < T) ? p.lse[(size_t)h * T + i] * kLog2e : __builtin_huge_valf();
-      } else if (x < NTAB) {
-        const int dd = i0 - kbase - (BNK - 1) + (x - BMQ);
-        treg[y] = (dd >= 0 && dd < T) ? rho[dd] * kLog2e : kNegInf;
-      }
-    }
-  };
-  auto store_tables = [&](FrzBwdSmem& sm) {
-#pragma unroll
-    for (int y = 0; y < (NTAB + NTH - 1) / NTH; ++y) {
-      const int x = t + y * NTH;
-      if (x < BMQ) sm.lz[x] = treg[y];
-      else if (x < NTAB) sm.rw[x - BMQ] = treg[y];
-    }
-  };
-
-  uint32_t goff[FCOLS / 32][2];
-#pragma unroll
-  for (int cb = 0; cb < FCOLS / 32; ++cb) {
-    goff[cb][0] = tr_off<CPR>(cb * 32, 0, lane);
-    goff[cb][1] = tr_off<CPR>(cb * 32, 1, lane);
-  }
-
-  auto step = [&](int st, const FrzBwdSmem& sm, FrzBwdSmem& nxt) {
-    if (st + 1 < n_steps) load(st + 1, nxt);
-    const int i0 = kbase + st * BMQ;
-#pragma unroll
-    for (int qb = 0; qb < BMQ / 32; ++qb) {
-      if (k0w > i0 + 32 * qb) continue;
-#pragma unroll
-      for (int sk = 0; sk < 2; ++sk) {
-        const int qofs = qb * 32 + sk * 16 + hh * 8;   // query offset within the step
-        // window index of distance (i0 + qofs + e) - j is qofs + e - (j - kbase) + BNK - 1;
-        // entries for j > i hold -inf, which masks the future for free.
-        const int rbase = qofs - (32 * w + m) + BNK - 1;
-        float ph[8], pl[8];
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const float pv = __builtin_amdgcn_exp2f(a2 + sm.rw[rbase + e] - sm.lz[qofs + e]);
-          const bf16 hi = (bf16)pv;
-          ph[e] = (float)hi;
-          pl[e] = pv - ph[e];
-        }
-        const bf16x8 ahi = pack8(ph);
-        const bf16x8 alo = pack8(pl);
-        pipelined<FCOLS / 32>([&](int cb) { return lds_tr<CPR>(sm.gs, qb * 32 + sk * 16, goff[cb][0], goff[cb][1]); },
-                              [&](int cb, const bf16x8& bg) {
-                                dv[cb] = mfma32(ahi, bg, dv[cb]);
-                                dv[cb] = mfma32(alo, bg, dv[cb]);
-                              });
-      }
-    }
-    if (st + 1 < n_steps) store_tables(nxt);
-    wait_vm0();
-    __syncthreads();
-  };
-
-  load(0, stg[0]);
-  store_tables(stg[0]);
-  wait_vm0();
-  __syncthreads();
-  for (int st = 0; st < n_steps; st += 2) {  // unrolled by two: the LDS stage is a constant
-    step(st, stg[0], stg[1]);
-    if (st + 1 < n_steps) step(st + 1, stg[1], stg[0]);
-  }
-
-#pragma unroll
-  for (int cb = 0; cb < FCOLS / 32; ++cb) {
-    const int col = col0 + cb * 32 + m;
-    if (cb * 32 >= ncols) continue;
-    const int bb = col / D, d = col % D;
-#pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int key = k0w + acc_row(r, hh);
-      if (key < T) p.dv[(((size_t)bb * H + h) * T + key) * D + d] = dv[cb][r];
-    }
-  }
-}
-
-template <int D>
-__global__ __launch_bounds__(NTH, 1) void dkdv_kernel(const BwdParams p) {
-  __shared__ __attribute__((aligned(16))) unsigned char smem[2 * dkdv_smem_bytes<D>()];
-  const int item = blockIdx.x;
-  const int kt = item / p.per_tile;  // key tile 0 has the most queries: heaviest first
-  int rem = item % p.per_tile;
+__global__ __launch_bounds__(NTH16, 2) void dkdv_kernel(const BwdParams p) {
+  __shared__ __attribute__((aligned(16))) unsigned char smem[dkdv16_smem_bytes<D>()];
+  const int kt = blockIdx.x / p.per_tile;
+  int rem = blockIdx.x % p.per_tile;
   const int nd = p.B * p.n_dyn;
   if (rem < nd) {
-    dkdv_dyn<D>(p, rem / p.n_dyn, p.dyn[rem % p.n_dyn], kt, smem);
+    dkdv_dyn16<D>(p, rem / p.n_dyn, p.dyn[rem % p.n_dyn], kt, smem);
   } else {
     rem -= nd;
-    dkdv_frz<D>(p, p.frz[rem / p.n_chunks], rem % p.n_chunks, kt, smem);
+    dv_frz16<D>(p, p.frz[rem / p.n_chunks], rem % p.n_chunks, kt, smem);
   }
 }
 
@@ -563,16 +634,16 @@ hipError_t launch_bwd_bf16(const AttnArgs& a, const void* q, const void* k, cons
   hipError_t e = launch_delta(a, o, dO, delta, s);
   if (e != hipSuccess) return e;
   BwdParams p = make_params(a, q, k, v, dO, lse, delta, alpha, rho, dq, dk, dv);
+  p.n_tiles = (a.T + BNK - 1) / BNK;
   p.n_chunks = (a.B * a.D + FCOLS - 1) / FCOLS;
   p.per_tile = a.B * p.n_dyn + p.n_frz * p.n_chunks;
-  p.n_tiles = (a.T + BNK - 1) / BNK;
   const int n_items = p.n_tiles * p.per_tile;
   if (n_items > 0) {
     prof_begin("dkdv", s);
     if (a.D == 64)
-      hipLaunchKernelGGL(dkdv_kernel<64>, dim3(n_items), dim3(NTH), 0, s, p);
+      hipLaunchKernelGGL(dkdv_kernel<64>, dim3(n_items), dim3(NTH16), 0, s, p);
     else
-      hipLaunchKernelGGL(dkdv_kernel<128>, dim3(n_items), dim3(NTH), 0, s, p);
+      hipLaunchKernelGGL(dkdv_kernel<128>, dim3(n_items), dim3(NTH16), 0, s, p);
     prof_end(s);
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
