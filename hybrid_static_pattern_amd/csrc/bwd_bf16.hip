@@ -32,8 +32,8 @@ namespace saf {
 namespace {
 
 constexpr int NTH = 256;
-constexpr int BNK = 128;   // keys per dK/dV workgroup
-constexpr int BMQ = 64;    // queries per dK/dV step
+constexpr int BNK = 256;   // keys per dK/dV workgroup
+constexpr int BMQ = 32;    // queries per dK/dV step
 constexpr int BMD = 128;   // queries per dQ workgroup
 constexpr int BND = 64;    // keys per dQ step
 constexpr int FCOLS = 256;
@@ -45,6 +45,7 @@ struct BwdParams {
   const bf16* dO;
   const float* lse;
   const float* delta;
+  const float* ls2;     // lse * log2(e) of ordinary heads
   const float* alpha;
   const float* rho;
   float* dq;
@@ -64,6 +65,8 @@ struct DeltaParams {
   const void* o;
   const void* dO;
   float* delta;
+  const float* lse;
+  float* ls2;   // lse * log2(e) (null: not written)
   int H, T, D, n_rows;  // n_rows = B * n_dyn * T
   int n_dyn;
   bool bf16;
@@ -103,362 +106,440 @@ __global__ __launch_bounds__(256) void bwd_delta_kernel(const DeltaParams p) {
   }
 #pragma unroll
   for (int o = 1; o < 8; o <<= 1) acc += __shfl_xor(acc, o, 64);
-  if (row < p.n_rows && sub == 0) p.delta[r] = acc;
+  if (row < p.n_rows && sub == 0) {
+    p.delta[r] = acc;
+    if (p.ls2) p.ls2[r] = p.lse[r] * kLog2e;
+  }
 }
 
 // ---------------------------------------------------------------- dK / dV
-
-// ---------------------------------------------------------------- dK / dV, ordinary heads
 //
-// 8 waves x 16 keys per 128-key workgroup on v_mfma_f32_16x16x32_bf16, so that a wave's
-// fp32 dK and dV tiles (16 keys x D) take 64 registers and two waves fit on each SIMD: while
-// one wave runs its softmax arithmetic the other keeps the matrix cores busy.
-//   16x16x32 operand layout: A (16 x 32): lane l holds A[l % 16][8 (l / 16) + e];
-//   B (32 x 16): lane l holds B[8 (l / 16) + e][l % 16]; C (16 x 16): lane l, register r
-//   holds C[4 (l / 16) + r][l % 16].
-// S = Q K^T is computed in two 16-query halves h whose A rows are the step's Q rows
-// 8 (rho / 4) + 4 h + rho % 4 (rho = MFMA row): then register r of half h in lane group g
+// v_mfma_f32_16x16x32_bf16 throughout. Operand layout: A (16 x 32): lane l holds
+// A[l % 16][8 (l / 16) + e]; B (32 x 16): lane l holds B[8 (l / 16) + e][l % 16]; C (16 x 16):
+// lane l, register r holds C[4 (l / 16) + r][l % 16]. Below n = l % 16 and g = l / 16.
+//
+// One workgroup of 8 waves per 256-key tile; wave w owns keys 32 w .. 32 w + 31 (two 16-key
+// groups kg) and keeps their K fragments and fp32 dK and dV tiles in registers, while the
+// tile's V rows sit in LDS for the whole item. Every Q and dO byte a wave reads from LDS
+// feeds two MFMAs. Steps are 32-query blocks whose Q / dO rows (and per-wave tables) go from
+// HBM straight into one of NSK LDS stages, NSK - 1 steps ahead of their use.
+//
+// S = Q K^T is computed in two 16-query halves h whose A rows are the block's Q rows
+// 8 (rho / 4) + 4 h + rho % 4 (rho = MFMA row): register r of half h in lane group g then
 // holds query 8 g + 4 h + r, and the 8 values of lane group g are exactly the 8 consecutive
 // queries 8 g .. 8 g + 7 that the P^T operand of the dV product needs (k index e = 4 h + r).
 
-constexpr int NW16 = 8;            // waves per ordinary dK/dV workgroup
-constexpr int NTH16 = 64 * NW16;
+constexpr int NWK = 8;                   // waves per dK/dV workgroup
+constexpr int NTK = 64 * NWK;
+constexpr int KPW = BNK / NWK;           // keys per wave
+constexpr int NKG = KPW / 16;            // 16-key groups per wave
+constexpr int NSK = 4;                   // LDS stages
+constexpr int DIAG_STEPS = BNK / BMQ;    // steps over the tile's own queries
+static_assert(KPW == 32 && DIAG_STEPS % NSK == 0, "tile layout");
+
+// Values read in place of rows past the data: +inf (a log-normaliser that zeroes its row's
+// weights) and -inf (a distance table entry of a key after its query).
+__device__ float kSentinel[2] = {__builtin_huge_valf(), -__builtin_huge_valf()};
 
 __device__ __forceinline__ f32x4 mfma16(const bf16x8& a, const bf16x8& b, const f32x4& c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
 
-// Chunk swizzle for the 16-lane read patterns of this kernel (period 32 in the row):
-//   A rows: each 16-lane group reads rows {0..3, 8..11, 16..19, 24..27} (+4, +32) at one chunk;
-//   B via ds_read_b64_tr_b16: each half-wave reads rows {0..3, 8..11} (+16, +4, +32) over
-//   32 bytes. Both map to distinct banks with 64 four-byte banks.
+// Chunk swizzles. gfx950 serves ds_read_b128 in four groups of 16 lanes (the half-wave, and
+// within it the parity of the lane's quad index (lane / 4) & 7) and ds_read_b64 /
+// ds_read_b64_tr_b16 in half-waves, each group over 64 four-byte banks. hq = 0, 2, 3, 1 maps
+// a 2-bit quad index so that the four quads of a b128 group get distinct values of
+// g ^ hq(quad) and quads 2 m, 2 m + 1 differ in bit 1.
+__device__ __forceinline__ int swz16_hq(int q) { return (((q ^ (q >> 1)) & 1) << 1) | (q >> 1); }
+// Q and dO tiles (query rows), period 32 in the row. Reads:
+//   A rows (b128): lane (n, g) reads row 8 (n / 4) + 4 h + n % 4, chunk 4 k + g;
+//   B via ds_read_b64_tr_b16: lane l reads row 8 g + (l / 4) % 4 + 4 h, 8 bytes at
+//   column 16 b + 4 (l % 4).
+// Position bits 2-3 separate the four rows of a quad (row bits 0-1; for 128-byte rows, where
+// row bit 0 already picks the bank half, row bit 1), and bits 0-1 take hq(row bits 3-4): the
+// four quads of a b128 group then differ in chunk bits 0-1, and the two row blocks of a
+// transposed half-wave in chunk bit 1. Row bit 2 is not used, so rows r and r + 4 share the
+// swizzle, and k (bits 2-3 of the chunk) and b (bits 1-3) enter the byte offset as an XOR
+// with 64 k and 32 b: a lane's offsets are one base XOR a constant.
 template <int CPR>
 __device__ __forceinline__ int swz16(int r) {
-  return CPR >= 16 ? (((r & 3) << 1) | (((r >> 3) & 1) << 3) | ((r >> 4) & 1))
-                   : (((r >> 4) & 1) | (((r >> 1) & 1) << 1) | (((r >> 3) & 1) << 2));
+  return CPR >= 16 ? (((r & 3) << 2) | swz16_hq((r >> 3) & 3)) : ((((r >> 1) & 1) << 2) | swz16_hq((r >> 3) & 3));
+}
+// V tile (key rows), read as the B operand of dP = dO V^T: lane (n, g) reads row
+// 16 m + n, chunk 4 k + g (b128). Same construction with hq taken from row bits 2-3.
+template <int CPR>
+__device__ __forceinline__ int swzv(int r) {
+  return CPR >= 16 ? (((r & 3) << 2) | swz16_hq((r >> 2) & 3)) : ((((r >> 1) & 1) << 2) | swz16_hq((r >> 2) & 3));
 }
 
-template <int CPR, int NR, class Src>
-__device__ __forceinline__ void tile_load16(bf16* tile, Src src) {
-  constexpr int NCH = NR * CPR;
-  constexpr int PERW = NCH / 64 / NW16;
-  static_assert(NCH % (64 * NW16) == 0, "tile must split evenly over the waves");
-  const int w = wave_id(), lane = lane_id();
-  const uint32_t base = lds_addr(tile);
+// B operand (32 x 16) from a row-major query tile: two transposing reads, rows +0 and +4
+template <int CPR>
+__device__ __forceinline__ bf16x8 lds_b16(const bf16* tile, uint32_t off) {
+  const char* base = reinterpret_cast<const char*>(tile);
+  const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(base + off));
+  const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(base + off + 4 * CPR * 16));
+  u32x4 r;
+  r[0] = __builtin_bit_cast(u32x2, lo)[0];
+  r[1] = __builtin_bit_cast(u32x2, lo)[1];
+  r[2] = __builtin_bit_cast(u32x2, hi)[0];
+  r[3] = __builtin_bit_cast(u32x2, hi)[1];
+  return __builtin_bit_cast(bf16x8, r);
+}
+// 16-byte row read
+__device__ __forceinline__ bf16x8 lds_16(const bf16* tile, uint32_t off) {
+  return *reinterpret_cast<const bf16x8*>(reinterpret_cast<const char*>(tile) + off);
+}
+// per-lane byte offset of the transposed B read of column block 0, rows +0 (XOR 32 b for
+// column block b)
+template <int CPR>
+__device__ __forceinline__ uint32_t tr16_base(int lane) {
+  const int row = 8 * (lane >> 4) + ((lane >> 2) & 3), col = 4 * (lane & 3);
+  return 2u * (uint32_t)(row * CPR * 8 + (((col >> 3) ^ swz16<CPR>(row)) << 3) + (col & 7));
+}
+
+template <int D>
+struct DynStage {
+  bf16 qs[BMQ * D];           // Q rows of the step, swizzled (swz16)
+  bf16 gs[BMQ * D];           // dO rows of the step
+  float tab[NWK][2 * BMQ];    // per wave: lse * log2(e) (+inf past T), then delta
+};
+template <int D>
+struct DynSmem {
+  DynStage<D> st[NSK];
+  bf16 vs[BNK * D];           // V rows of the key tile, swizzled (swzv)
+};
+struct FrzStage {
+  bf16 gs[BMQ * FCOLS];       // folded dO [q][column], swizzled (swz16); read transposed
+  float tab[NWK][128];        // per wave: log Z (+inf past T), then rho over the wave's
+                              // 63-distance window (-inf for negative distances)
+};
+
+template <int D>
+constexpr int dkdv_smem_bytes() {
+  return sizeof(DynSmem<D>) > NSK * sizeof(FrzStage) ? (int)sizeof(DynSmem<D>) : (int)(NSK * sizeof(FrzStage));
+}
+
+// Runs the item's steps 0 .. n_steps - 1 with stage st % NSK, the loads of step st + NSK - 1
+// issued at step st (L loads per wave and step, in issue order) and waited for NSK - 2 steps
+// later. Steps past n_steps are loaded too (their rows clamped, their tables sentinels) so
+// that every step issues the same L loads. The first DIAG_STEPS steps run with on_diag set.
+// Leaves no load outstanding.
+template <int L, class Load, class Compute>
+__device__ __forceinline__ void run_steps(int n_steps, Load load, Compute compute) {
 #pragma unroll
-  for (int x = 0; x < PERW; ++x) {
-    const int blk = w * PERW + x;
-    const int pch = blk * 64 + lane;
-    const int row = pch / CPR;
-    const int c = (pch % CPR) ^ swz16<CPR>(row);
-    g2lds16(src(row, c), base + blk * 1024);
+  for (int s = 0; s < NSK - 1; ++s) load(s, s);
+  wait_vm<L * (NSK - 2)>();
+  __syncthreads();
+  auto step = [&](int st, int u, bool on_diag) {
+    load(st + NSK - 1, (u + NSK - 1) % NSK);
+    compute(st, u, on_diag);
+    wait_vm<L * (NSK - 2)>();
+    __syncthreads();
+  };
+  bool more = true;
+  for (int st = 0; more && st < DIAG_STEPS; st += NSK) {
+#pragma unroll
+    for (int u = 0; u < NSK; ++u) {
+      if (st + u >= n_steps) {
+        more = false;
+        break;
+      }
+      step(st + u, u, true);
+    }
   }
+  for (int st = DIAG_STEPS; st < n_steps; st += NSK) {
+#pragma unroll
+    for (int u = 0; u < NSK; ++u)
+      if (st + u < n_steps) step(st + u, u, false);
+  }
+  wait_vm0();
 }
 
-template <int D>
-struct Dkdv16Stage {
-  bf16 qs[BMQ * D];   // Q rows of the step, swizzled (swz16)
-  bf16 gs[BMQ * D];   // dO rows of the step
-  float ls[BMQ];      // lse * log2(e) (+inf past T)
-  float dl[BMQ];      // delta
-};
-
-struct Frz16Stage {
-  bf16 gs[BMQ * FCOLS];   // folded dO [q][column], swizzled (swz16); read transposed
-  float lz[BMQ];          // log Z * log2(e) (+inf past T)
-  float rw[BMQ + BNK];    // rho * log2(e) over the step's distance window
-};
-
-template <int D>
-constexpr int dkdv16_smem_bytes() {
-  return 2 * (sizeof(Dkdv16Stage<D>) > sizeof(Frz16Stage) ? (int)sizeof(Dkdv16Stage<D>) : (int)sizeof(Frz16Stage));
-}
-
-// Frozen item (h, 128-key tile, column chunk): dV_b[j] = sum_{i>=j} P(i,j) dO_b[i] for the
-// batch folded into up to 256 columns. Each wave keeps 16 keys x 256 columns of fp32 dV;
+// Frozen item (h, 256-key tile, column chunk): dV_b[j] = sum_{i>=j} P(i,j) dO_b[i] for the
+// batch folded into up to 256 columns. Each wave keeps its 32 keys x 256 columns of fp32 dV;
 // P^T is regenerated per lane from alpha, rho and log Z (entries for j > i come out as 0 from
 // the -inf distances of the window) and split into bf16 high and low parts.
 template <int D>
-__device__ void dv_frz16(const BwdParams& p, int h, int chunk, int kt, unsigned char* smem_raw) {
+__device__ void dv_frz(const BwdParams& p, int h, int chunk, int kt, unsigned char* smem_raw) {
   constexpr int CPR = FCOLS / 8;
   constexpr int NCB = FCOLS / 16;
-  Frz16Stage* stg = reinterpret_cast<Frz16Stage*>(smem_raw);
-  const int t = threadIdx.x, lane = lane_id(), w = wave_id();
+  constexpr int PERW = BMQ * CPR / NTK;   // 16-byte chunks per lane per step
+  FrzStage* stg = reinterpret_cast<FrzStage*>(smem_raw);
+  const int lane = lane_id(), w = wave_id();
   const int n = lane & 15, g = lane >> 4;
   const int T = p.T, H = p.H, B = p.B;
   const int col0 = chunk * FCOLS;
   const int ncols = min(FCOLS, B * D - col0);
-  const int kbase = kt * BNK, k0w = kbase + 16 * w, j = k0w + n;
-  const float a2 = (j < T) ? p.alpha[(size_t)h * p.tab_stride + j] * kLog2e : kNegInf;
+  const int kbase = kt * BNK, k0w = kbase + KPW * w;
   const float* rho = p.rho + (size_t)h * p.tab_stride;
+  float a2[NKG];
+#pragma unroll
+  for (int kg = 0; kg < NKG; ++kg) {
+    const int j = k0w + 16 * kg + n;
+    a2[kg] = (j < T) ? p.alpha[(size_t)h * p.tab_stride + j] * kLog2e : kNegInf;
+  }
 
-  f32x4 dv[NCB];
+  f32x4 dv[NKG][NCB];
 #pragma unroll
-  for (int cb = 0; cb < NCB; ++cb) dv[cb] = f32x4{0.f, 0.f, 0.f, 0.f};
-  uint32_t goff[NCB][2];
+  for (int kg = 0; kg < NKG; ++kg)
 #pragma unroll
-  for (int cb = 0; cb < NCB; ++cb)
-#pragma unroll
-    for (int hf = 0; hf < 2; ++hf) {
-      const int row = 8 * g + ((lane >> 2) & 3) + 4 * hf, col = 16 * cb + 4 * (lane & 3);
-      goff[cb][hf] = 2u * (uint32_t)(row * FCOLS + (((col >> 3) ^ swz16<CPR>(row)) << 3) + (col & 7));
-    }
+    for (int cb = 0; cb < NCB; ++cb) dv[kg][cb] = f32x4{0.f, 0.f, 0.f, 0.f};
+  const uint32_t goff = tr16_base<CPR>(lane);
 
-  const int n_steps = (T - kbase + BMQ - 1) / BMQ;
-  constexpr int NTAB = BMQ + BMQ + BNK - 1;   // lz for the step's queries, then the rho window
-  static_assert(NTAB <= NTH16, "one table entry per thread");
-  float treg = 0.f;
-  auto load = [&](int st, Frz16Stage& sm) {
+  // this lane's chunks of each step's tile: folded column col0 + 8 chunk is column d of batch
+  // element bb (columns past B * D, in a partial last chunk, read element B - 1 and are not
+  // stored); 1 KiB block (w PERW + x) of the tile
+  const bf16* src[PERW];
+  int srow[PERW];
+#pragma unroll
+  for (int x = 0; x < PERW; ++x) {
+    const int pch = (w * PERW + x) * 64 + lane, row = pch / CPR;
+    const int col = col0 + ((pch % CPR) ^ swz16<CPR>(row)) * 8;
+    const int bb = min(col / D, B - 1), d = col % D;
+    src[x] = p.dO + (((size_t)bb * H + h) * T) * D + d;
+    srow[x] = row;
+  }
+  auto load = [&](int st, int u) {
+    FrzStage& sm = stg[u];
     const int i0 = kbase + st * BMQ;
-    tile_load16<CPR, BMQ>(sm.gs, [&](int row, int c) {
-      const int col = col0 + c * 8;
-      const int bb = min(col / D, B - 1), d = col % D;
-      return p.dO + (((size_t)bb * H + h) * T + min(i0 + row, T - 1)) * D + d;
-    });
-    if (t < BMQ) {
-      const int i = i0 + t;
-      treg = (i < T) ? p.lse[(size_t)h * T + i] * kLog2e : __builtin_huge_valf();
-    } else if (t < NTAB) {
-      const int dd = i0 - kbase - (BNK - 1) + (t - BMQ);
-      treg = (dd >= 0 && dd < T) ? rho[dd] * kLog2e : kNegInf;
+#pragma unroll
+    for (int x = 0; x < PERW; ++x)
+      g2lds16(src[x] + (size_t)min(i0 + srow[x], T - 1) * D, lds_addr(sm.gs) + (uint32_t)(w * PERW + x) * 1024u);
+    // table entry e = 64 y + lane: log Z of query i0 + e (e < 32), then rho at distance
+    // i0 - (k0w + 31) + e - 32 (32 <= e < 95)
+#pragma unroll
+    for (int y = 0; y < 2; ++y) {
+      const int e = 64 * y + lane;
+      const float* a;
+      if (e < BMQ) {
+        const int i = i0 + e;
+        a = (i < T) ? p.lse + (size_t)h * T + i : &kSentinel[0];
+      } else {
+        const int dd = i0 - (k0w + KPW - 1) + (e - BMQ);
+        a = (dd >= 0 && e < BMQ + BMQ + KPW - 1) ? rho + min(dd, T - 1) : &kSentinel[1];
+      }
+      g2lds4(a, lds_addr(&sm.tab[w][64 * y]));
     }
   };
-  auto store_tables = [&](Frz16Stage& sm) {
-    if (t < BMQ) sm.lz[t] = treg;
-    else if (t < NTAB) sm.rw[t - BMQ] = treg;
-  };
 
-  auto step = [&](int st, const Frz16Stage& sm, Frz16Stage& nxt) {
-    if (st + 1 < n_steps) load(st + 1, nxt);
+  auto compute = [&](int st, int u, bool on_diag) {
+    const FrzStage& sm = stg[u];
+    if (on_diag && st < w) return;   // the block ends before this wave's keys
+    const float* tb = sm.tab[w];
+    // queries i0 + 8 g + e; window index of distance i - j is (8 g + e) - (16 kg + n) + 31
+    const int qofs = 8 * g;
+    bf16x8 ahi[NKG], alo[NKG];
 #pragma unroll
-    for (int qb = 0; qb < BMQ / 32; ++qb) {
-      if (st * (BMQ / 32) + qb < (w >> 1)) continue;   // every query before this wave's keys
-      // queries i0 + qb*32 + 8 g + e; window index of distance i - j is
-      // (qb*32 + 8 g + e) - (16 w + n) + BNK - 1
-      const int qofs = qb * 32 + 8 * g;
-      const int rbase = qofs - (16 * w + n) + BNK - 1;
+    for (int kg = 0; kg < NKG; ++kg) {
+      const int rbase = BMQ + qofs - (16 * kg + n) + KPW - 1;
       float ph[8], pl[8];
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
-        const float pv = __builtin_amdgcn_exp2f(a2 + sm.rw[rbase + e] - sm.lz[qofs + e]);
+        const float pv = __builtin_amdgcn_exp2f(__builtin_fmaf(tb[rbase + e] - tb[qofs + e], kLog2e, a2[kg]));
         const bf16 hi = (bf16)pv;
         ph[e] = (float)hi;
         pl[e] = pv - ph[e];
       }
-      const bf16x8 ahi = pack8(ph), alo = pack8(pl);
-      pipelined<NCB>(
-          [&](int cb) {
-            const char* base = reinterpret_cast<const char*>(sm.gs) + qb * 32 * (CPR * 16);
-            const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(base + goff[cb][0]));
-            const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(base + goff[cb][1]));
-            u32x4 r;
-            r[0] = __builtin_bit_cast(u32x2, lo)[0];
-            r[1] = __builtin_bit_cast(u32x2, lo)[1];
-            r[2] = __builtin_bit_cast(u32x2, hi)[0];
-            r[3] = __builtin_bit_cast(u32x2, hi)[1];
-            return __builtin_bit_cast(bf16x8, r);
-          },
-          [&](int cb, const bf16x8& bg) {
-            dv[cb] = mfma16(ahi, bg, dv[cb]);
-            dv[cb] = mfma16(alo, bg, dv[cb]);
-          });
+      ahi[kg] = pack8(ph);
+      alo[kg] = pack8(pl);
     }
-    if (st + 1 < n_steps) store_tables(nxt);
-    wait_vm0();
-    __syncthreads();
+    pipelined<NCB>([&](int cb) { return lds_b16<CPR>(sm.gs, goff ^ (32u * cb)); },
+                   [&](int cb, const bf16x8& bg) {
+#pragma unroll
+                     for (int kg = 0; kg < NKG; ++kg) dv[kg][cb] = mfma16(ahi[kg], bg, dv[kg][cb]);
+#pragma unroll
+                     for (int kg = 0; kg < NKG; ++kg) dv[kg][cb] = mfma16(alo[kg], bg, dv[kg][cb]);
+                   });
   };
 
-  load(0, stg[0]);
-  store_tables(stg[0]);
-  wait_vm0();
-  __syncthreads();
-  for (int st = 0; st < n_steps; st += 2) {  // unrolled by two: the LDS stage is a constant
-    step(st, stg[0], stg[1]);
-    if (st + 1 < n_steps) step(st + 1, stg[1], stg[0]);
-  }
+  const int n_steps = (T - kbase + BMQ - 1) / BMQ;
+  run_steps<PERW + 2>(n_steps, load, compute);
 
 #pragma unroll
-  for (int cb = 0; cb < NCB; ++cb) {
-    const int col = col0 + 16 * cb + n;
-    if (16 * cb >= ncols) continue;
-    const int bb = col / D, d = col % D;
+  for (int kg = 0; kg < NKG; ++kg)
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int key = k0w + 4 * g + r;
-      if (key < T) p.dv[(((size_t)bb * H + h) * T + key) * D + d] = dv[cb][r];
+    for (int cb = 0; cb < NCB; ++cb) {
+      const int col = col0 + 16 * cb + n;
+      if (16 * cb >= ncols) continue;
+      const int bb = col / D, d = col % D;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int key = k0w + 16 * kg + 4 * g + r;
+        if (key < T) p.dv[(((size_t)bb * H + h) * T + key) * D + d] = dv[kg][cb][r];
+      }
     }
-  }
 }
 
+// Ordinary item (b, h, 256-key tile): dV and dK for the wave's 32 keys over all queries
+// from the tile's first one to T, one 32-query block per step.
 template <int D>
-__device__ void dkdv_dyn16(const BwdParams& p, int b, int h, int kt, unsigned char* smem_raw) {
+__device__ void dkdv_dyn(const BwdParams& p, int b, int h, int kt, unsigned char* smem_raw) {
   constexpr int CPR = D / 8;
   constexpr int NKS = D / 32;   // 32-wide k-steps over d
   constexpr int NDB = D / 16;   // 16-wide d blocks of dK, dV
-  Dkdv16Stage<D>* stg = reinterpret_cast<Dkdv16Stage<D>*>(smem_raw);
-  const int t = threadIdx.x, lane = lane_id(), w = wave_id();
+  // waves 0..3 load the step's Q rows, waves 4..7 its dO rows
+  constexpr int PERW = BMQ * CPR / (NTK / 2);
+  constexpr int PERV = BNK * CPR / NTK;   // V tile chunks per lane
+  static_assert(PERW >= 1 && PERV >= 1, "tile split");
+  DynSmem<D>* smem = reinterpret_cast<DynSmem<D>*>(smem_raw);
+  const int lane = lane_id(), w = wave_id();
   const int n = lane & 15, g = lane >> 4;
   const int T = p.T;
   const size_t head = ((size_t)b * p.H + h) * (size_t)T;
   const bf16* Q = p.q + head * D;
   const bf16* G = p.dO + head * D;
-  const int k0w = kt * BNK + 16 * w;
-  const int j = k0w + n;
+  const int kbase = kt * BNK, k0w = kbase + KPW * w;
 
-  bf16x8 kf[NKS], vf[NKS];   // B operands: K[j][32 ks + 8 g + e], V likewise
+  bf16x8 kf[NKG][NKS];   // B operands of S: K[j][32 ks + 8 g + e]
 #pragma unroll
-  for (int ks = 0; ks < NKS; ++ks) {
-    const size_t off = (head + min(j, T - 1)) * D + 32 * ks + 8 * g;
-    kf[ks] = *reinterpret_cast<const bf16x8*>(p.k + off);
-    vf[ks] = *reinterpret_cast<const bf16x8*>(p.v + off);
+  for (int kg = 0; kg < NKG; ++kg)
+#pragma unroll
+    for (int ks = 0; ks < NKS; ++ks)
+      kf[kg][ks] = *reinterpret_cast<const bf16x8*>(p.k + (head + min(k0w + 16 * kg + n, T - 1)) * D + 32 * ks + 8 * g);
+  // V rows of the key tile into LDS (rows past T re-read row T - 1; their keys are not stored)
+#pragma unroll
+  for (int x = 0; x < PERV; ++x) {
+    const int pch = (w * PERV + x) * 64 + lane, row = pch / CPR;
+    const int c = (pch % CPR) ^ swzv<CPR>(row);
+    g2lds16(p.v + (head + min(kbase + row, T - 1)) * D + c * 8, lds_addr(smem->vs) + (uint32_t)(w * PERV + x) * 1024u);
   }
-  f32x4 dv[NDB], dk[NDB];
+  f32x4 dv[NKG][NDB], dk[NKG][NDB];
 #pragma unroll
-  for (int db = 0; db < NDB; ++db) {
-    dv[db] = f32x4{0.f, 0.f, 0.f, 0.f};
-    dk[db] = f32x4{0.f, 0.f, 0.f, 0.f};
-  }
-  // per-lane byte offsets within a 32-row block of a tile (constant multiples of 32 rows
-  // keep the swizzle): A-row reads per (half, k-step), transposed B reads per (d-block, half)
-  uint32_t roff[2][NKS], toff[NDB][2];
+  for (int kg = 0; kg < NKG; ++kg)
 #pragma unroll
-  for (int hf = 0; hf < 2; ++hf)
-#pragma unroll
-    for (int ks = 0; ks < NKS; ++ks) {
-      const int row = 8 * (n >> 2) + 4 * hf + (n & 3), chunk = 4 * ks + g;
-      roff[hf][ks] = 16u * (uint32_t)(row * CPR + (chunk ^ swz16<CPR>(row)));
+    for (int db = 0; db < NDB; ++db) {
+      dv[kg][db] = f32x4{0.f, 0.f, 0.f, 0.f};
+      dk[kg][db] = f32x4{0.f, 0.f, 0.f, 0.f};
     }
-#pragma unroll
-  for (int db = 0; db < NDB; ++db)
-#pragma unroll
-    for (int hf = 0; hf < 2; ++hf) {
-      const int row = 8 * g + ((lane >> 2) & 3) + 4 * hf, col = 16 * db + 4 * (lane & 3);
-      toff[db][hf] = 2u * (uint32_t)(row * D + (((col >> 3) ^ swz16<CPR>(row)) << 3) + (col & 7));
-    }
+  // per-lane byte offsets: A rows of half 0, k-step 0 (half h adds 4 rows, k-step k XORs
+  // 64 k); the transposed B read of d-block 0 (d-block b XORs 32 b); the V read of key group
+  // 0, k-step 0 (key group m adds 16 rows, k-step k XORs 64 k)
+  const int arow = 8 * (n >> 2) + (n & 3);
+  const uint32_t aoff = 16u * (uint32_t)(arow * CPR + (g ^ swz16<CPR>(arow)));
+  const uint32_t boff = tr16_base<CPR>(lane);
+  const int vrow = KPW * w + n;
+  const uint32_t voff = 16u * (uint32_t)(vrow * CPR + (g ^ swzv<CPR>(vrow)));
 
-  const int i_start = kt * BNK;
-  const int n_steps = (T - i_start + BMQ - 1) / BMQ;
-  float lreg = 0.f, dreg = 0.f;
-  auto load = [&](int st, Dkdv16Stage<D>& sm) {
-    const int i0 = i_start + st * BMQ;
-    tile_load16<CPR, BMQ>(sm.qs, [&](int row, int c) { return Q + (size_t)min(i0 + row, T - 1) * D + c * 8; });
-    tile_load16<CPR, BMQ>(sm.gs, [&](int row, int c) { return G + (size_t)min(i0 + row, T - 1) * D + c * 8; });
-    if (t < BMQ) {
-      const int i = i0 + t;
-      lreg = (i < T) ? p.lse[head + i] * kLog2e : __builtin_huge_valf();
-      dreg = (i < T) ? p.delta[head + i] : 0.f;
+  const bf16* tsrc = (w < NWK / 2) ? Q : G;
+  const int wl = w & (NWK / 2 - 1);
+  auto load = [&](int st, int u) {
+    DynStage<D>& sm = smem->st[u];
+    const int i0 = kbase + st * BMQ;
+    bf16* tile = (w < NWK / 2) ? sm.qs : sm.gs;
+    // rows past T (the last step, and the steps past the end) re-read row T - 1; the base row
+    // ib <= every row read keeps the unsigned per-lane offsets non-negative
+    const int ib = min(i0, T - 1);
+#pragma unroll
+    for (int x = 0; x < PERW; ++x) {
+      const int pch = (wl * PERW + x) * 64 + lane, row = pch / CPR;
+      const int c = (pch % CPR) ^ swz16<CPR>(row);
+      const uint32_t o = 2u * (uint32_t)((min(i0 + row, T - 1) - ib) * D + c * 8);
+      g2lds16_s(tsrc + (size_t)ib * D, o, lds_addr(tile) + (uint32_t)(wl * PERW + x) * 1024u);
     }
-  };
-  auto store_rows = [&](Dkdv16Stage<D>& sm) {
-    if (t < BMQ) {
-      sm.ls[t] = lreg;
-      sm.dl[t] = dreg;
-    }
-  };
-  auto lds_a = [](const bf16* tile, int qb, uint32_t off) {
-    return *reinterpret_cast<const bf16x8*>(reinterpret_cast<const char*>(tile) + qb * 32 * (CPR * 16) + off);
-  };
-  auto lds_b = [](const bf16* tile, int qb, uint32_t off_lo, uint32_t off_hi) {
-    const char* base = reinterpret_cast<const char*>(tile) + qb * 32 * (CPR * 16);
-    const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(base + off_lo));
-    const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(base + off_hi));
-    u32x4 r;
-    r[0] = __builtin_bit_cast(u32x2, lo)[0];
-    r[1] = __builtin_bit_cast(u32x2, lo)[1];
-    r[2] = __builtin_bit_cast(u32x2, hi)[0];
-    r[3] = __builtin_bit_cast(u32x2, hi)[1];
-    return __builtin_bit_cast(bf16x8, r);
+    // table: lanes 0..31 lse * log2(e) of query i0 + lane, lanes 32..63 delta
+    const int i = i0 + (lane & 31);
+    const float* a = (lane < 32) ? ((i < T) ? p.ls2 + head + i : &kSentinel[0]) : p.delta + head + min(i, T - 1);
+    g2lds4(a, lds_addr(sm.tab[w]));
   };
 
   // one 32-query block: S, dP (two halves each), P and dS in registers, dV and dK.
-  // `diag` marks the block on the diagonal: a query before this lane's key (query offset
-  // 8 g + 4 h + r in the block, key offset 16 (w & 1) + n) gets zero weight.
-  const int kdiag = 16 * (w & 1) + n;
-  auto block = [&](const Dkdv16Stage<D>& sm, int qb, bool diag) {
-    f32x4 sc[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
-    f32x4 dp[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
-    pipelined<4 * NKS>(
-        [&](int x) { return lds_a((x & 1) ? sm.gs : sm.qs, qb, roff[(x >> 1) & 1][x >> 2]); },
-        [&](int x, const bf16x8& a) {
-          const int hf = (x >> 1) & 1, ks = x >> 2;
-          if (x & 1) dp[hf] = mfma16(a, vf[ks], dp[hf]);
-          else sc[hf] = mfma16(a, kf[ks], sc[hf]);
-        });
-    float pr[8], dsr[8];
+  // On the block that holds the wave's first key (`diag`), a query before a lane's key (query
+  // offset 8 g + 4 h + r, key offset 16 kg + n from the block start) gets zero weight.
+  auto compute = [&](int st, int u, bool on_diag) {
+    const DynStage<D>& sm = smem->st[u];
+    if (on_diag && st < w) return;   // the block ends before this wave's keys
+    const bool diag = on_diag && st == w;
+    const float* tb = sm.tab[w];
+    f32x4 sc[NKG][2], dp[NKG][2];
 #pragma unroll
-    for (int hf = 0; hf < 2; ++hf)
+    for (int kg = 0; kg < NKG; ++kg)
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int qi = qb * 32 + 8 * g + 4 * hf + r;
-        float pv = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[hf][r], p.c, -sm.ls[qi]));
-        if (diag && 8 * g + 4 * hf + r < kdiag) pv = 0.f;
-        pr[4 * hf + r] = pv;
-        dsr[4 * hf + r] = pv * (dp[hf][r] - sm.dl[qi]);
+      for (int hf = 0; hf < 2; ++hf) {
+        sc[kg][hf] = f32x4{0.f, 0.f, 0.f, 0.f};
+        dp[kg][hf] = f32x4{0.f, 0.f, 0.f, 0.f};
       }
-    const bf16x8 pa = pack8(pr), da = pack8(dsr);
-    // dV += P^T dO, dK += dS^T Q over the block's 32 queries (one 16x16x32 product each)
-    pipelined<2 * NDB>([&](int x) { return lds_b((x & 1) ? sm.qs : sm.gs, qb, toff[x >> 1][0], toff[x >> 1][1]); },
+    // per k-step: NKG V reads (B of dP), then Q rows of halves 0, 1 and dO rows of halves 0, 1
+    constexpr int PER = NKG + 4;
+    bf16x8 vb[NKG];
+    pipelined<PER * NKS>(
+        [&](int x) {
+          const int ks = x / PER, y = x % PER;
+          if (y < NKG) return lds_16(smem->vs, (voff ^ (64u * ks)) + y * (16 * CPR * 16));
+          const int hf = (y - NKG) & 1;
+          return lds_16((y - NKG) >= 2 ? sm.gs : sm.qs, (aoff ^ (64u * ks)) + hf * (4 * CPR * 16));
+        },
+        [&](int x, const bf16x8& a) {
+          const int ks = x / PER, y = x % PER;
+          if (y < NKG) {
+            vb[y] = a;
+            return;
+          }
+          const int hf = (y - NKG) & 1;
+#pragma unroll
+          for (int kg = 0; kg < NKG; ++kg) {
+            if ((y - NKG) >= 2) dp[kg][hf] = mfma16(a, vb[kg], dp[kg][hf]);
+            else sc[kg][hf] = mfma16(a, kf[kg][ks], sc[kg][hf]);
+          }
+        });
+    bf16x8 pa[NKG], da[NKG];
+#pragma unroll
+    for (int kg = 0; kg < NKG; ++kg) {
+      float pr[8], dsr[8];
+#pragma unroll
+      for (int hf = 0; hf < 2; ++hf)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int qi = 8 * g + 4 * hf + r;
+          float pv = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[kg][hf][r], p.c, -tb[qi]));
+          if (diag && qi < 16 * kg + n) pv = 0.f;
+          pr[4 * hf + r] = pv;
+          dsr[4 * hf + r] = pv * (dp[kg][hf][r] - tb[BMQ + qi]);
+        }
+      pa[kg] = pack8(pr);
+      da[kg] = pack8(dsr);
+    }
+    // dV += P^T dO, dK += dS^T Q over the block's 32 queries
+    pipelined<2 * NDB>([&](int x) { return lds_b16<CPR>((x & 1) ? sm.qs : sm.gs, boff ^ (32u * (x >> 1))); },
                        [&](int x, const bf16x8& bop) {
-                         if (x & 1) dk[x >> 1] = mfma16(da, bop, dk[x >> 1]);
-                         else dv[x >> 1] = mfma16(pa, bop, dv[x >> 1]);
+#pragma unroll
+                         for (int kg = 0; kg < NKG; ++kg) {
+                           if (x & 1) dk[kg][x >> 1] = mfma16(da[kg], bop, dk[kg][x >> 1]);
+                           else dv[kg][x >> 1] = mfma16(pa[kg], bop, dv[kg][x >> 1]);
+                         }
                        });
   };
 
-  auto step = [&](int st, const Dkdv16Stage<D>& sm, Dkdv16Stage<D>& nxt) {
-    if (st + 1 < n_steps) load(st + 1, nxt);
-    if (st * BMQ < BNK) {
-      // steps on the diagonal: 32-query block gq of the key tile meets this wave's keys
-      // (16 w .. 16 w + 15 within the tile) for gq >= w / 2, and gq == w / 2 needs the mask
-#pragma unroll
-      for (int qb = 0; qb < BMQ / 32; ++qb) {
-        const int gq = st * (BMQ / 32) + qb;
-        if (gq < (w >> 1)) continue;
-        block(sm, qb, gq == (w >> 1));
-      }
-    } else {
-#pragma unroll
-      for (int qb = 0; qb < BMQ / 32; ++qb) block(sm, qb, false);
-    }
-    if (st + 1 < n_steps) store_rows(nxt);
-    wait_vm0();
-    __syncthreads();
-  };
-
-  load(0, stg[0]);
-  store_rows(stg[0]);
-  wait_vm0();
-  __syncthreads();
-  for (int st = 0; st < n_steps; st += 2) {  // unrolled by two: the LDS stage is a constant
-    step(st, stg[0], stg[1]);
-    if (st + 1 < n_steps) step(st + 1, stg[1], stg[0]);
-  }
+  const int n_steps = (T - kbase + BMQ - 1) / BMQ;
+  run_steps<PERW + 1>(n_steps, load, compute);
 
 #pragma unroll
-  for (int db = 0; db < NDB; ++db)
+  for (int kg = 0; kg < NKG; ++kg)
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int key = k0w + 4 * g + r;
-      if (key < T) {
-        const size_t off = (head + key) * D + 16 * db + n;
-        p.dv[off] = dv[db][r];
-        p.dk[off] = dk[db][r] * p.scale;
+    for (int db = 0; db < NDB; ++db)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int key = k0w + 16 * kg + 4 * g + r;
+        if (key < T) {
+          const size_t off = (head + key) * D + 16 * db + n;
+          p.dv[off] = dv[kg][db][r];
+          p.dk[off] = dk[kg][db][r] * p.scale;
+        }
       }
-    }
 }
 
 // Both item kinds in one launch, heaviest key tile first: per key tile, the ordinary
 // (b, h) items, then the frozen (h, column chunk) items.
 template <int D>
-__global__ __launch_bounds__(NTH16, 2) void dkdv_kernel(const BwdParams p) {
-  __shared__ __attribute__((aligned(16))) unsigned char smem[dkdv16_smem_bytes<D>()];
+__global__ __launch_bounds__(NTK, 2) void dkdv_kernel(const BwdParams p) {
+  __shared__ __attribute__((aligned(16))) unsigned char smem[dkdv_smem_bytes<D>()];
   const int kt = blockIdx.x / p.per_tile;
   int rem = blockIdx.x % p.per_tile;
   const int nd = p.B * p.n_dyn;
   if (rem < nd) {
-    dkdv_dyn16<D>(p, rem / p.n_dyn, p.dyn[rem % p.n_dyn], kt, smem);
+    dkdv_dyn<D>(p, rem / p.n_dyn, p.dyn[rem % p.n_dyn], kt, smem);
   } else {
     rem -= nd;
-    dv_frz16<D>(p, p.frz[rem / p.n_chunks], rem % p.n_chunks, kt, smem);
+    dv_frz<D>(p, p.frz[rem / p.n_chunks], rem % p.n_chunks, kt, smem);
   }
 }
 
@@ -608,12 +689,14 @@ BwdParams make_params(const AttnArgs& a, const void* q, const void* k, const voi
 }  // namespace
 
 hipError_t launch_delta(const AttnArgs& a, const void* o, const void* dO, float* delta,
-                        hipStream_t s) {
+                        const float* lse, float* ls2, hipStream_t s) {
   if (a.heads.n_dyn == 0) return hipSuccess;
   DeltaParams p;
   p.o = o;
   p.dO = dO;
   p.delta = delta;
+  p.lse = lse;
+  p.ls2 = ls2;
   p.H = a.H;
   p.T = a.T;
   p.D = a.D;
@@ -631,9 +714,11 @@ hipError_t launch_bwd_bf16(const AttnArgs& a, const void* q, const void* k, cons
                            const void* o, const void* dO, const float* lse,
                            const float* alpha, const float* rho, float* dq, float* dk,
                            float* dv, float* delta, hipStream_t s) {
-  hipError_t e = launch_delta(a, o, dO, delta, s);
+  float* ls2 = delta + attn_ws_floats(a);
+  hipError_t e = launch_delta(a, o, dO, delta, lse, ls2, s);
   if (e != hipSuccess) return e;
   BwdParams p = make_params(a, q, k, v, dO, lse, delta, alpha, rho, dq, dk, dv);
+  p.ls2 = ls2;
   p.n_tiles = (a.T + BNK - 1) / BNK;
   p.n_chunks = (a.B * a.D + FCOLS - 1) / FCOLS;
   p.per_tile = a.B * p.n_dyn + p.n_frz * p.n_chunks;
@@ -641,9 +726,9 @@ hipError_t launch_bwd_bf16(const AttnArgs& a, const void* q, const void* k, cons
   if (n_items > 0) {
     prof_begin("dkdv", s);
     if (a.D == 64)
-      hipLaunchKernelGGL(dkdv_kernel<64>, dim3(n_items), dim3(NTH16), 0, s, p);
+      hipLaunchKernelGGL(dkdv_kernel<64>, dim3(n_items), dim3(NTK), 0, s, p);
     else
-      hipLaunchKernelGGL(dkdv_kernel<128>, dim3(n_items), dim3(NTH16), 0, s, p);
+      hipLaunchKernelGGL(dkdv_kernel<128>, dim3(n_items), dim3(NTK), 0, s, p);
     prof_end(s);
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }

@@ -164,7 +164,7 @@ saf_status saf_attn_fwd(const saf_attn_desc* desc, const void* q, const void* k,
 size_t saf_attn_workspace_size(const saf_attn_desc* desc) {
   saf::AttnArgs a;
   if (validate_attn(desc, &a) != SAF_OK) return 0;
-  return align256((size_t)a.B * a.H * a.T * sizeof(float));
+  return 2 * saf::attn_ws_floats(a) * sizeof(float);
 }
 
 saf_status saf_attn_bwd(const saf_attn_desc* desc, const void* q, const void* k, const void* v,

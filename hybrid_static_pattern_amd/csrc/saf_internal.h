@@ -35,11 +35,16 @@ hipError_t launch_fwd_fp32(const AttnArgs& a, const void* q, const void* k, cons
                            const float* alpha, const float* rho, void* o, float* lse,
                            hipStream_t s);
 
-// delta_i = sum_c dO_ic O_ic for ordinary heads, into `delta` [B, H, T] float32.
+// delta_i = sum_c dO_ic O_ic for ordinary heads, into `delta` [B, H, T] float32, and (if
+// ls2 is not null) ls2 = lse * log2(e) for the same rows.
 hipError_t launch_delta(const AttnArgs& a, const void* o, const void* dO, float* delta,
-                        hipStream_t s);
+                        const float* lse, float* ls2, hipStream_t s);
 
-// Backward. `delta` is workspace [B, H, T] float32.
+// Backward workspace: two [B, H, T] float32 arrays (delta, then lse * log2(e)), each padded
+// to a multiple of 64 floats; attn_ws_floats is one array's length.
+inline size_t attn_ws_floats(const AttnArgs& a) { return ((size_t)a.B * a.H * a.T + 63) / 64 * 64; }
+
+// Backward. `delta` is the workspace.
 hipError_t launch_bwd_bf16(const AttnArgs& a, const void* q, const void* k, const void* v,
                            const void* o, const void* dO, const float* lse,
                            const float* alpha, const float* rho, float* dq, float* dk,

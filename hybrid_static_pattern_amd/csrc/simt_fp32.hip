@@ -235,7 +235,7 @@ hipError_t launch_bwd_fp32(const AttnArgs& a, const void* q, const void* k, cons
                            const void* o, const void* dO, const float* lse,
                            const float* alpha, const float* rho, float* dq, float* dk,
                            float* dv, float* delta, hipStream_t s) {
-  hipError_t e = launch_delta(a, o, dO, delta, s);
+  hipError_t e = launch_delta(a, o, dO, delta, lse, nullptr, s);
   if (e != hipSuccess) return e;
   F32Params p = base_params(a);
   p.q = static_cast<const float*>(q);
