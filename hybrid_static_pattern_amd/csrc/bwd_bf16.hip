@@ -31,11 +31,12 @@ namespace saf {
 
 namespace {
 
-constexpr int NTH = 256;
 constexpr int BNK = 256;   // keys per dK/dV workgroup
 constexpr int BMQ = 32;    // queries per dK/dV step
-constexpr int BMD = 128;   // queries per dQ workgroup
+constexpr int NWD = 4;     // waves per dQ workgroup (two workgroups per CU)
+constexpr int BMD = 32 * NWD;   // queries per dQ workgroup
 constexpr int BND = 64;    // keys per dQ step
+constexpr int NSD = 2;     // dQ LDS stages
 constexpr int FCOLS = 256;
 
 struct BwdParams {
@@ -219,42 +220,6 @@ constexpr int dkdv_smem_bytes() {
   return sizeof(DynSmem<D>) > NSK * sizeof(FrzStage) ? (int)sizeof(DynSmem<D>) : (int)(NSK * sizeof(FrzStage));
 }
 
-// Runs the item's steps 0 .. n_steps - 1 with stage st % NSK, the loads of step st + NSK - 1
-// issued at step st (L loads per wave and step, in issue order) and waited for NSK - 2 steps
-// later. Steps past n_steps are loaded too (their rows clamped, their tables sentinels) so
-// that every step issues the same L loads. The first DIAG_STEPS steps run with on_diag set.
-// Leaves no load outstanding.
-template <int L, class Load, class Compute>
-__device__ __forceinline__ void run_steps(int n_steps, Load load, Compute compute) {
-#pragma unroll
-  for (int s = 0; s < NSK - 1; ++s) load(s, s);
-  wait_vm<L * (NSK - 2)>();
-  __syncthreads();
-  auto step = [&](int st, int u, bool on_diag) {
-    load(st + NSK - 1, (u + NSK - 1) % NSK);
-    compute(st, u, on_diag);
-    wait_vm<L * (NSK - 2)>();
-    __syncthreads();
-  };
-  bool more = true;
-  for (int st = 0; more && st < DIAG_STEPS; st += NSK) {
-#pragma unroll
-    for (int u = 0; u < NSK; ++u) {
-      if (st + u >= n_steps) {
-        more = false;
-        break;
-      }
-      step(st + u, u, true);
-    }
-  }
-  for (int st = DIAG_STEPS; st < n_steps; st += NSK) {
-#pragma unroll
-    for (int u = 0; u < NSK; ++u)
-      if (st + u < n_steps) step(st + u, u, false);
-  }
-  wait_vm0();
-}
-
 // Frozen item (h, 256-key tile, column chunk): dV_b[j] = sum_{i>=j} P(i,j) dO_b[i] for the
 // batch folded into up to 256 columns. Each wave keeps its 32 keys x 256 columns of fp32 dV;
 // P^T is regenerated per lane from alpha, rho and log Z (entries for j > i come out as 0 from
@@ -353,7 +318,7 @@ __device__ void dv_frz(const BwdParams& p, int h, int chunk, int kt, unsigned ch
   };
 
   const int n_steps = (T - kbase + BMQ - 1) / BMQ;
-  run_steps<PERW + 2>(n_steps, load, compute);
+  run_pipeline<NSK, NSK - 1, PERW + 2, DIAG_STEPS>(n_steps, load, compute);
 
 #pragma unroll
   for (int kg = 0; kg < NKG; ++kg)
@@ -442,15 +407,12 @@ __device__ void dkdv_dyn(const BwdParams& p, int b, int h, int kt, unsigned char
     g2lds4(a, lds_addr(sm.tab[w]));
   };
 
-  // one 32-query block: S, dP (two halves each), P and dS in registers, dV and dK.
-  // On the block that holds the wave's first key (`diag`), a query before a lane's key (query
-  // offset 8 g + 4 h + r, key offset 16 kg + n from the block start) gets zero weight.
-  auto compute = [&](int st, int u, bool on_diag) {
-    const DynStage<D>& sm = smem->st[u];
-    if (on_diag && st < w) return;   // the block ends before this wave's keys
-    const bool diag = on_diag && st == w;
-    const float* tb = sm.tab[w];
-    f32x4 sc[NKG][2], dp[NKG][2];
+  // One 32-query block: products() computes S and dP (two 16-query halves each) into sc, dp;
+  // finish() turns them into P and dS in registers and accumulates dV and dK. On the block
+  // that holds the wave's first key, a query before a lane's key (query offset 8 g + 4 h + r,
+  // key offset 16 kg + n from the block start) gets S = -inf, so P = 0.
+  f32x4 sc[NKG][2], dp[NKG][2];
+  auto products = [&](const DynStage<D>& sm, bool diag) {
 #pragma unroll
     for (int kg = 0; kg < NKG; ++kg)
 #pragma unroll
@@ -481,6 +443,18 @@ __device__ void dkdv_dyn(const BwdParams& p, int b, int h, int kt, unsigned char
             else sc[kg][hf] = mfma16(a, kf[kg][ks], sc[kg][hf]);
           }
         });
+    if (diag) {
+#pragma unroll
+      for (int kg = 0; kg < NKG; ++kg)
+#pragma unroll
+        for (int hf = 0; hf < 2; ++hf)
+#pragma unroll
+          for (int r = 0; r < 4; ++r)
+            if (8 * g + 4 * hf + r < 16 * kg + n) sc[kg][hf][r] = kNegInf;
+    }
+  };
+  auto finish = [&](const DynStage<D>& sm) {
+    const float* tb = sm.tab[w];
     bf16x8 pa[NKG], da[NKG];
 #pragma unroll
     for (int kg = 0; kg < NKG; ++kg) {
@@ -490,8 +464,7 @@ __device__ void dkdv_dyn(const BwdParams& p, int b, int h, int kt, unsigned char
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
           const int qi = 8 * g + 4 * hf + r;
-          float pv = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[kg][hf][r], p.c, -tb[qi]));
-          if (diag && qi < 16 * kg + n) pv = 0.f;
+          const float pv = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[kg][hf][r], p.c, -tb[qi]));
           pr[4 * hf + r] = pv;
           dsr[4 * hf + r] = pv * (dp[kg][hf][r] - tb[BMQ + qi]);
         }
@@ -508,9 +481,15 @@ __device__ void dkdv_dyn(const BwdParams& p, int b, int h, int kt, unsigned char
                          }
                        });
   };
+  // block st meets this wave's keys iff 32 st + 31 >= 32 w; the block holding key 32 w is st = w
+  auto compute = [&](int st, int u, bool on_diag) {
+    if (on_diag && st < w) return;
+    products(smem->st[u], on_diag && st == w);
+    finish(smem->st[u]);
+  };
 
   const int n_steps = (T - kbase + BMQ - 1) / BMQ;
-  run_steps<PERW + 1>(n_steps, load, compute);
+  run_pipeline<NSK, NSK - 1, PERW + 1, DIAG_STEPS>(n_steps, load, compute);
 
 #pragma unroll
   for (int kg = 0; kg < NKG; ++kg)
@@ -552,10 +531,10 @@ struct DqSmem {
 };
 
 template <int D>
-__global__ __launch_bounds__(NTH, 2) void dq_kernel(const BwdParams p) {
+__global__ __launch_bounds__(64 * NWD, 2) void dq_kernel(const BwdParams p) {
   constexpr int CPR = D / 8;
   constexpr int NDB = D / 32;
-  __shared__ __attribute__((aligned(16))) unsigned char smem_raw[2 * sizeof(DqSmem<D>)];
+  __shared__ __attribute__((aligned(16))) unsigned char smem_raw[NSD * sizeof(DqSmem<D>)];
   DqSmem<D>* stg = reinterpret_cast<DqSmem<D>*>(smem_raw);
   const int item = blockIdx.x;
   const int n_qt = p.n_tiles;
@@ -583,11 +562,10 @@ __global__ __launch_bounds__(NTH, 2) void dq_kernel(const BwdParams p) {
 #pragma unroll
   for (int db = 0; db < NDB; ++db) acc[db] = f32x16{};
 
-  const int n_kt = min(2 * qt + 2, (T + BND - 1) / BND);
-  auto load = [&](int J, DqSmem<D>& sm) {
-    const int j0 = J * BND;
-    tile_load<CPR, BND>(sm.k, [&](int row, int c) { return K + (size_t)min(j0 + row, T - 1) * D + c * 8; });
-    tile_load<CPR, BND>(sm.v, [&](int row, int c) { return V + (size_t)min(j0 + row, T - 1) * D + c * 8; });
+  const int n_kt = min((qt + 1) * (BMD / BND), (T + BND - 1) / BND);
+  auto load = [&](int J, int u) {
+    tile_load_rows<CPR, BND, NWD>(stg[u].k, K, J * BND, T);
+    tile_load_rows<CPR, BND, NWD>(stg[u].v, V, J * BND, T);
   };
 
   uint32_t koff[D / 16], toff[NDB][2];
@@ -599,8 +577,8 @@ __global__ __launch_bounds__(NTH, 2) void dq_kernel(const BwdParams p) {
     toff[db][1] = tr_off<CPR>(db * 32, 1, lane);
   }
 
-  auto tile = [&](int J, const DqSmem<D>& sm, DqSmem<D>& nxt) {
-    if (J + 1 < n_kt) load(J + 1, nxt);
+  auto tile = [&](int J, int u, bool) {
+    const DqSmem<D>& sm = stg[u];
     const int j0 = J * BND;
     if (j0 <= i0w) {
       // per 32-key block: S^T = K Q^T and dP^T = V dO^T (two independent chains), then dS^T
@@ -627,17 +605,9 @@ __global__ __launch_bounds__(NTH, 2) void dq_kernel(const BwdParams p) {
       pipelined<4 * NDB>([&](int x) { return lds_tr<CPR>(sm.k, (x / NDB) * 16, toff[x % NDB][0], toff[x % NDB][1]); },
                          [&](int x, const bf16x8& a) { acc[x % NDB] = mfma32(a, dsb[x / NDB], acc[x % NDB]); });
     }
-    wait_vm0();
-    __syncthreads();
   };
-
-  load(0, stg[0]);
-  wait_vm0();
-  __syncthreads();
-  for (int J = 0; J < n_kt; J += 2) {  // unrolled by two: the LDS stage is a constant
-    tile(J, stg[0], stg[1]);
-    if (J + 1 < n_kt) tile(J + 1, stg[1], stg[0]);
-  }
+  constexpr int PERW = BND * CPR / (64 * NWD);   // loads per wave and tile, for each of K, V
+  run_pipeline<NSD, NSD - 1, 2 * PERW, 0>(n_kt, load, tile);
 
   if (i < T) {
     float* out = p.dq + (head + i) * D;
@@ -737,9 +707,9 @@ hipError_t launch_bwd_bf16(const AttnArgs& a, const void* q, const void* k, cons
   const int n_dq = p.n_tiles * a.B * p.n_dyn;
   prof_begin("dq", s);
   if (a.D == 64)
-    hipLaunchKernelGGL(dq_kernel<64>, dim3(n_dq), dim3(NTH), 0, s, p);
+    hipLaunchKernelGGL(dq_kernel<64>, dim3(n_dq), dim3(64 * NWD), 0, s, p);
   else
-    hipLaunchKernelGGL(dq_kernel<128>, dim3(n_dq), dim3(NTH), 0, s, p);
+    hipLaunchKernelGGL(dq_kernel<128>, dim3(n_dq), dim3(64 * NWD), 0, s, p);
   prof_end(s);
   return hipGetLastError();
 }

@@ -22,9 +22,12 @@
 //   frozen (h, q-tile, column chunk): the batch is folded into the columns, so one
 //       item multiplies the regenerated pattern tile by up to 256 columns of
 //       [V_0 | V_1 | ...] and the exp work is shared by every batch entry.
-// Key tiles go from HBM straight into double-buffered LDS (no staging registers), one
-// barrier per tile; V is stored row-major and read transposed (ds_read_b64_tr_b16). Items are issued heaviest
-// q-tile first; key tiles above the causal diagonal are skipped.
+// Key tiles (and a frozen item's per-wave alpha / rho tables) go from HBM straight into one of
+// NS LDS stages, NS - 1 tiles ahead of their use (no staging registers), one barrier per
+// tile; V is stored row-major and read transposed (ds_read_b64_tr_b16). Two workgroups share
+// a CU: their waves are not tied by a common barrier, so one runs its softmax arithmetic
+// while the other keeps the matrix cores busy. Items are issued heaviest q-tile first; key
+// tiles above a wave's causal diagonal are skipped by that wave.
 #include "saf_device.h"
 #include "saf_internal.h"
 
@@ -32,10 +35,16 @@ namespace saf {
 
 namespace {
 
-constexpr int BM = 128;        // queries per workgroup
+constexpr int NW = 4;          // waves per workgroup
+constexpr int BM = 32 * NW;    // queries per workgroup
 constexpr int BN = 64;         // keys per tile
-constexpr int NTH = 256;
+constexpr int NTH = 64 * NW;
+constexpr int NS = 2;          // LDS stages
 constexpr int FCOLS = 256;     // batch-folded columns per frozen item
+constexpr int FTAB = 192;      // per-wave frozen table: alpha of the tile's keys, then rho
+
+// -inf, read in place of table entries past the data (keys past T, negative distances)
+__device__ float kNegSentinel[1] = {-__builtin_huge_valf()};
 constexpr float kRescaleSlack = 8.0f;  // log2 units
 
 struct FwdParams {
@@ -61,14 +70,14 @@ struct DynStage {
 };
 
 struct FrzStage {
-  bf16 v[BN * FCOLS];    // folded value tile [key][column], swizzled; read transposed
-  float a2[BN];          // alpha * log2(e) of the tile's keys
-  float rw[BM + BN];     // rho * log2(e) over the tile's distance window
+  bf16 v[BN * FCOLS];     // folded value tile [key][column], swizzled; read transposed
+  float tab[NW][FTAB];    // per wave: alpha of the tile's 64 keys, then rho over the wave's
+                          // 95-distance window (-inf past the data)
 };
 
 template <int D>
-constexpr int stage_bytes() {
-  return sizeof(DynStage<D>) > sizeof(FrzStage) ? (int)sizeof(DynStage<D>) : (int)sizeof(FrzStage);
+constexpr int smem_bytes() {
+  return NS * (sizeof(DynStage<D>) > sizeof(FrzStage) ? (int)sizeof(DynStage<D>) : (int)sizeof(FrzStage));
 }
 
 // Online-softmax bookkeeping of one lane (one query row). `mx` is this lane's max over its
@@ -119,11 +128,10 @@ __device__ void dyn_item(const FwdParams& p, int b, int h, int qt, unsigned char
   for (int db = 0; db < D / 32; ++db) o[db] = f32x16{};
   float m_used = kNegInf, l = 0.f;
 
-  const int n_kt = min(2 * qt + 2, (T + BN - 1) / BN);
-  auto load = [&](int J, DynStage<D>& sm) {
-    const int j0 = J * BN;
-    tile_load<CPR, BN>(sm.k, [&](int row, int c) { return K + (size_t)min(j0 + row, T - 1) * D + c * 8; });
-    tile_load<CPR, BN>(sm.v, [&](int row, int c) { return V + (size_t)min(j0 + row, T - 1) * D + c * 8; });
+  const int n_kt = min((qt + 1) * (BM / BN), (T + BN - 1) / BN);
+  auto load = [&](int J, int u) {
+    tile_load_rows<CPR, BN, NW>(st[u].k, K, J * BN, T);
+    tile_load_rows<CPR, BN, NW>(st[u].v, V, J * BN, T);
   };
 
   // per-lane LDS offsets: K rows in pi order (one per k-step), V^T reads (per d-block)
@@ -137,8 +145,8 @@ __device__ void dyn_item(const FwdParams& p, int b, int h, int qt, unsigned char
     voff[db][1] = tr_off<CPR>(db * 32, 1, lane);
   }
 
-  auto tile = [&](int J, const DynStage<D>& sm, DynStage<D>& nxt) {
-    if (J + 1 < n_kt) load(J + 1, nxt);
+  auto tile = [&](int J, int u, bool) {
+    const DynStage<D>& sm = st[u];
     const int j0 = J * BN;
     if (j0 <= i0w) {  // tile meets this wave's causal region
       // S^T for keys j0 .. j0+63: two independent 32-key chains, interleaved
@@ -175,17 +183,9 @@ __device__ void dyn_item(const FwdParams& p, int b, int h, int qt, unsigned char
           [&](int x) { return lds_tr<CPR>(sm.v, (x / NDB) * 16, voff[x % NDB][0], voff[x % NDB][1]); },
           [&](int x, const bf16x8& a) { o[x % NDB] = mfma32(a, pb[x / NDB], o[x % NDB]); });
     }
-    wait_vm0();
-    __syncthreads();
   };
-
-  load(0, st[0]);
-  wait_vm0();
-  __syncthreads();
-  for (int J = 0; J < n_kt; J += 2) {  // unrolled by two: the LDS stage is a constant
-    tile(J, st[0], st[1]);
-    if (J + 1 < n_kt) tile(J + 1, st[1], st[0]);
-  }
+  constexpr int PERW = BN * CPR / (64 * NW);   // loads per wave and tile, for each of K, V
+  run_pipeline<NS, NS - 1, 2 * PERW, 0>(n_kt, load, tile);
 
   const float lt = l + wave_shfl_xor32(l);
   if (i < T) {
@@ -211,12 +211,12 @@ template <int D>
 __device__ void frz_item(const FwdParams& p, int h, int chunk, int qt, unsigned char* smem_raw) {
   constexpr int CPR = FCOLS / 8;
   FrzStage* st = reinterpret_cast<FrzStage*>(smem_raw);
-  const int t = threadIdx.x, lane = lane_id(), w = wave_id();
+  const int lane = lane_id(), w = wave_id();
   const int m = lane & 31, hh = lane >> 5;
   const int T = p.T, H = p.H, B = p.B;
   const int col0 = chunk * FCOLS;
   const int ncols = min(FCOLS, B * D - col0);
-  const int i0 = qt * BM, i0w = i0 + w * 32, i = i0w + m;
+  const int i0w = qt * BM + w * 32, i = i0w + m;
   const float* alpha = p.alpha + (size_t)h * p.tab_stride;
   const float* rho = p.rho + (size_t)h * p.tab_stride;
 
@@ -226,25 +226,41 @@ __device__ void frz_item(const FwdParams& p, int h, int chunk, int qt, unsigned 
   for (int cb = 0; cb < FCOLS / 32; ++cb) o[cb] = f32x16{};
   float m_used = kNegInf, l = 0.f;
 
-  const int n_kt = min(2 * qt + 2, (T + BN - 1) / BN);
-  float treg = 0.f;
-  auto load = [&](int J, FrzStage& sm) {
+  const int n_kt = min((qt + 1) * (BM / BN), (T + BN - 1) / BN);
+  // this lane's chunks of each tile: folded column col0 + 8 chunk is column d of batch
+  // element bb (columns past B * D, in a partial last chunk, read element B - 1 and are not
+  // stored); 1 KiB block (w PERW + x) of the tile
+  constexpr int PERW = BN * CPR / (64 * NW);
+  const bf16* src[PERW];
+  int srow[PERW];
+#pragma unroll
+  for (int x = 0; x < PERW; ++x) {
+    const int pch = (w * PERW + x) * 64 + lane, row = pch / CPR;
+    const int col = col0 + ((pch % CPR) ^ swz<CPR>(row)) * 8;
+    const int bb = min(col / D, B - 1), d = col % D;
+    src[x] = p.v + (((size_t)bb * H + h) * T) * D + d;
+    srow[x] = row;
+  }
+  auto load = [&](int J, int u) {
+    FrzStage& sm = st[u];
     const int j0 = J * BN;
-    tile_load<CPR, BN>(sm.v, [&](int row, int c) {
-      const int col = col0 + c * 8;
-      const int bb = min(col / D, B - 1), d = col % D;
-      return p.v + (((size_t)bb * H + h) * T + min(j0 + row, T - 1)) * D + d;
-    });
-    if (t < BN) {
-      treg = (j0 + t < T) ? alpha[j0 + t] * kLog2e : kNegInf;
-    } else if (t < BN + BM + BN - 1) {
-      const int dd = i0 - j0 - (BN - 1) + (t - BN);
-      treg = (dd >= 0 && dd < T) ? rho[dd] * kLog2e : kNegInf;
+#pragma unroll
+    for (int x = 0; x < PERW; ++x)
+      g2lds16(src[x] + (size_t)min(j0 + srow[x], T - 1) * D, lds_addr(sm.v) + (uint32_t)(w * PERW + x) * 1024u);
+    // table entry e = 64 y + lane: alpha of key j0 + e (e < 64), then rho at distance
+    // i0w - (j0 + 63) + (e - 64) (64 <= e < 159); -inf past the data
+#pragma unroll
+    for (int y = 0; y < FTAB / 64; ++y) {
+      const int e = 64 * y + lane;
+      const float* a = &kNegSentinel[0];
+      if (e < BN) {
+        if (j0 + e < T) a = alpha + j0 + e;
+      } else if (e < 2 * BN + 31) {
+        const int dd = i0w - (j0 + BN - 1) + (e - BN);
+        if (dd >= 0) a = rho + min(dd, T - 1);
+      }
+      g2lds4(a, lds_addr(&sm.tab[w][64 * y]));
     }
-  };
-  auto store_tables = [&](FrzStage& sm) {
-    if (t < BN) sm.a2[t] = treg;
-    else if (t < BN + BM + BN - 1) sm.rw[t - BN] = treg;
   };
 
   uint32_t voff[FCOLS / 32][2];
@@ -254,28 +270,29 @@ __device__ void frz_item(const FwdParams& p, int h, int chunk, int qt, unsigned 
     voff[cb][1] = tr_off<CPR>(cb * 32, 1, lane);
   }
 
-  auto tile = [&](int J, const FrzStage& sm, FrzStage& nxt) {
-    if (J + 1 < n_kt) load(J + 1, nxt);
+  auto tile = [&](int J, int u, bool) {
+    const FrzStage& sm = st[u];
     const int j0 = J * BN;
     if (j0 <= i0w) {
-      // logits alpha(j) + rho(i - j) in log2 units; the distance window index of
-      // (i, j0 + kofs + e) is (i - i0) - (kofs + e) + BN - 1, and entries for j > i hold
-      // -inf, so the causal mask comes for free. They are read twice from LDS (for the
-      // max, then for the exps) rather than held in registers next to 128 accumulators.
-      const int rb0 = (i - i0) + BN - 1 - hh * 8;
+      // logits alpha(j) + rho(i - j); the window index of (i, j0 + kofs + e) is
+      // m - (kofs + e) + 63, and entries for j > i hold -inf, so the causal mask comes for
+      // free. They are read twice from LDS (for the max, then for the exps) rather than held
+      // in registers next to 128 accumulators.
+      const float* tb = sm.tab[w];
+      const int rb0 = BN + m + BN - 1 - hh * 8;
       float mx = kNegInf;
 #pragma unroll
       for (int ks = 0; ks < 4; ++ks)
 #pragma unroll
-        for (int e = 0; e < 8; ++e) mx = fmaxf(mx, sm.a2[ks * 16 + hh * 8 + e] + sm.rw[rb0 - ks * 16 - e]);
-      const float msub = online_rescale<FCOLS / 32>(mx, 1.f, m_used, l, o);
+        for (int e = 0; e < 8; ++e) mx = fmaxf(mx, tb[ks * 16 + hh * 8 + e] + tb[rb0 - ks * 16 - e]);
+      const float msub = online_rescale<FCOLS / 32>(mx, kLog2e, m_used, l, o);
 #pragma unroll
       for (int ks = 0; ks < 4; ++ks) {
         const int kofs = ks * 16 + hh * 8;
         float pv[8];
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
-          pv[e] = __builtin_amdgcn_exp2f(sm.a2[kofs + e] + sm.rw[rb0 - ks * 16 - e] - msub);
+          pv[e] = __builtin_amdgcn_exp2f(__builtin_fmaf(tb[kofs + e] + tb[rb0 - ks * 16 - e], kLog2e, -msub));
           l += pv[e];
         }
         const bf16x8 pb = pack8(pv);
@@ -283,19 +300,8 @@ __device__ void frz_item(const FwdParams& p, int h, int chunk, int qt, unsigned 
                               [&](int cb, const bf16x8& a) { o[cb] = mfma32(a, pb, o[cb]); });
       }
     }
-    if (J + 1 < n_kt) store_tables(nxt);
-    wait_vm0();
-    __syncthreads();
   };
-
-  load(0, st[0]);
-  store_tables(st[0]);
-  wait_vm0();
-  __syncthreads();
-  for (int J = 0; J < n_kt; J += 2) {  // unrolled by two: the LDS stage is a constant
-    tile(J, st[0], st[1]);
-    if (J + 1 < n_kt) tile(J + 1, st[1], st[0]);
-  }
+  run_pipeline<NS, NS - 1, PERW + FTAB / 64, 0>(n_kt, load, tile);
 
   const float lt = l + wave_shfl_xor32(l);
   if (i < T) {
@@ -323,7 +329,7 @@ __device__ void frz_item(const FwdParams& p, int h, int chunk, int qt, unsigned 
 
 template <int D>
 __global__ __launch_bounds__(NTH, 2) void hybrid_fwd_kernel(const FwdParams p) {
-  __shared__ __attribute__((aligned(16))) unsigned char smem[2 * stage_bytes<D>()];
+  __shared__ __attribute__((aligned(16))) unsigned char smem[smem_bytes<D>()];
   const int item = blockIdx.x;
   const int qt = p.n_qt - 1 - item / p.per_qt;
   int rem = item % p.per_qt;

@@ -199,6 +199,69 @@ __device__ __forceinline__ void pipelined(Read read, Mma mma) {
   }
 }
 
+// Multi-stage LDS pipeline over the steps 0 .. n_steps - 1 of a work item. Step st
+// computes on stage st % NS; the loads of step st + PD (L vector-memory loads per wave and
+// step, direct to LDS) are issued at step st and waited for PD - 1 steps later, one barrier
+// per step. PD <= NS - 1; with PD < NS - 1 the stages of steps st - 1 .. st + PD - NS stay
+// intact during step st (for consumers that lag behind). Steps past n_steps are loaded too
+// (callers clamp their rows or read sentinels), so every step issues the same L loads. The
+// first NPEEL steps (a multiple of NS) run with `peeled` set, in a loop of their own.
+// load(step, stage) and compute(step, stage, peeled) are called with compile-time stage
+// indices. Leaves no load outstanding.
+template <int NS, int PD, int L, int NPEEL, class Load, class Compute>
+__device__ __forceinline__ void run_pipeline(int n_steps, Load load, Compute compute) {
+  static_assert(NS >= 2 && PD >= 1 && PD <= NS - 1 && NPEEL % NS == 0, "pipeline shape");
+#pragma unroll
+  for (int s = 0; s < PD; ++s) load(s, s);
+  wait_vm<L * (PD - 1)>();
+  __syncthreads();
+  auto step = [&](int st, int u, bool peeled) {
+    load(st + PD, (u + PD) % NS);
+    compute(st, u, peeled);
+    wait_vm<L * (PD - 1)>();
+    __syncthreads();
+  };
+  if constexpr (NPEEL > 0) {
+    bool more = true;
+    for (int st = 0; more && st < NPEEL; st += NS) {
+#pragma unroll
+      for (int u = 0; u < NS; ++u) {
+        if (st + u >= n_steps) {
+          more = false;
+          break;
+        }
+        step(st + u, u, true);
+      }
+    }
+  }
+  for (int st = NPEEL; st < n_steps; st += NS) {
+#pragma unroll
+    for (int u = 0; u < NS; ++u)
+      if (st + u < n_steps) step(st + u, u, false);
+  }
+  wait_vm0();
+}
+
+// Loads rows j0 .. j0 + NR - 1 (rows past T - 1 re-read row T - 1) of a row-major
+// [T, 8 CPR] bf16 matrix into a tile swizzled with swz<CPR>, using all NW waves: wave w
+// fills 1 KiB blocks w PERW .. w PERW + PERW - 1. One load per block and lane; the base row
+// jb <= every row read keeps the unsigned per-lane offsets non-negative.
+template <int CPR, int NR, int NW>
+__device__ __forceinline__ void tile_load_rows(bf16* tile, const bf16* src, int j0, int T) {
+  constexpr int PERW = NR * CPR / (64 * NW);
+  static_assert(PERW >= 1 && NR * CPR == PERW * 64 * NW, "tile must split evenly over the waves");
+  const int w = wave_id(), lane = lane_id();
+  const int jb = min(j0, T - 1);
+  const bf16* base = src + (size_t)jb * (CPR * 8);
+#pragma unroll
+  for (int x = 0; x < PERW; ++x) {
+    const int pch = (w * PERW + x) * 64 + lane, row = pch / CPR;
+    const int c = (pch % CPR) ^ swz<CPR>(row);
+    const uint32_t o = 2u * (uint32_t)((min(j0 + row, T - 1) - jb) * (CPR * 8) + c * 8);
+    g2lds16_s(base, o, lds_addr(tile) + (uint32_t)(w * PERW + x) * 1024u);
+  }
+}
+
 __device__ __forceinline__ float wave_shfl_xor32(float x) {
   return __shfl_xor(x, 32, 64);
 }
