@@ -562,8 +562,12 @@ __global__ __launch_bounds__(64 * NWD, 2) void dq_kernel(const BwdParams p) {
 #pragma unroll
   for (int db = 0; db < NDB; ++db) acc[db] = f32x16{};
 
+  // Key tiles are visited from the last one down, so that the two tiles that can hold a wave's
+  // diagonal (BMD = 2 BND) come first: they run in a peeled region with the causal mask, and
+  // every later tile is a full one with no mask arithmetic.
   const int n_kt = min((qt + 1) * (BMD / BND), (T + BND - 1) / BND);
-  auto load = [&](int J, int u) {
+  auto load = [&](int s, int u) {
+    const int J = max(n_kt - 1 - s, 0);   // steps past the end reload tile 0
     tile_load_rows<CPR, BND, NWD>(stg[u].k, K, J * BND, T);
     tile_load_rows<CPR, BND, NWD>(stg[u].v, V, J * BND, T);
   };
@@ -577,37 +581,43 @@ __global__ __launch_bounds__(64 * NWD, 2) void dq_kernel(const BwdParams p) {
     toff[db][1] = tr_off<CPR>(db * 32, 1, lane);
   }
 
-  auto tile = [&](int J, int u, bool) {
-    const DqSmem<D>& sm = stg[u];
-    const int j0 = J * BND;
-    if (j0 <= i0w) {
-      // per 32-key block: S^T = K Q^T and dP^T = V dO^T (two independent chains), then dS^T
-      const bool diag = (j0 + BND - 1 > i0w);
-      const int lim = i - j0 - 8 * hh;
-      bf16x8 dsb[4];
+  // one key tile; `diag` (the tile holding this wave's diagonal) zeroes keys after the query
+  auto body = [&](const DqSmem<D>& sm, int j0, bool diag) {
+    // per 32-key block: S^T = K Q^T and dP^T = V dO^T (two independent chains), then dS^T
+    const int lim = i - j0 - 8 * hh;
+    bf16x8 dsb[4];
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-        f32x16 sd[2] = {f32x16{}, f32x16{}};   // 0: S^T, 1: dP^T
-        pipelined<D / 8>(
-            [&](int x) { return lds_row<CPR>((x & 1) ? sm.v : sm.k, kb * 32, koff[x >> 1]); },
-            [&](int x, const bf16x8& a) { sd[x & 1] = mfma32(a, (x & 1) ? gf[x >> 1] : qf[x >> 1], sd[x & 1]); });
-        float dsr[16];
+    for (int kb = 0; kb < 2; ++kb) {
+      f32x16 sd[2] = {f32x16{}, f32x16{}};   // 0: S^T, 1: dP^T
+      pipelined<D / 8>(
+          [&](int x) { return lds_row<CPR>((x & 1) ? sm.v : sm.k, kb * 32, koff[x >> 1]); },
+          [&](int x, const bf16x8& a) { sd[x & 1] = mfma32(a, (x & 1) ? gf[x >> 1] : qf[x >> 1], sd[x & 1]); });
+      float dsr[16];
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          float pv = __builtin_amdgcn_exp2f(__builtin_fmaf(sd[0][r], p.c, -lse2));
-          if (diag && kb * 32 + ((r >> 3) << 4) + (r & 7) > lim) pv = 0.f;
-          dsr[r] = pv * (sd[1][r] - dlt);
-        }
-        dsb[2 * kb] = pack8(dsr);
-        dsb[2 * kb + 1] = pack8(dsr + 8);
+      for (int r = 0; r < 16; ++r) {
+        float pv = __builtin_amdgcn_exp2f(__builtin_fmaf(sd[0][r], p.c, -lse2));
+        if (diag && kb * 32 + ((r >> 3) << 4) + (r & 7) > lim) pv = 0.f;
+        dsr[r] = pv * (sd[1][r] - dlt);
       }
-      // dQ^T += K^T dS^T, K^T read transposed from the key tile
-      pipelined<4 * NDB>([&](int x) { return lds_tr<CPR>(sm.k, (x / NDB) * 16, toff[x % NDB][0], toff[x % NDB][1]); },
-                         [&](int x, const bf16x8& a) { acc[x % NDB] = mfma32(a, dsb[x / NDB], acc[x % NDB]); });
+      dsb[2 * kb] = pack8(dsr);
+      dsb[2 * kb + 1] = pack8(dsr + 8);
+    }
+    // dQ^T += K^T dS^T, K^T read transposed from the key tile
+    pipelined<4 * NDB>([&](int x) { return lds_tr<CPR>(sm.k, (x / NDB) * 16, toff[x % NDB][0], toff[x % NDB][1]); },
+                       [&](int x, const bf16x8& a) { acc[x % NDB] = mfma32(a, dsb[x / NDB], acc[x % NDB]); });
+  };
+  auto tile = [&](int s, int u, bool peeled) {
+    const int j0 = (n_kt - 1 - s) * BND;
+    if (peeled) {
+      if (j0 > i0w) return;  // the tile lies after this wave's queries
+      body(stg[u], j0, j0 + BND - 1 > i0w);
+    } else {
+      body(stg[u], j0, false);
     }
   };
   constexpr int PERW = BND * CPR / (64 * NWD);   // loads per wave and tile, for each of K, V
-  run_pipeline<NSD, NSD - 1, 2 * PERW, 0>(n_kt, load, tile);
+  static_assert(BMD == 2 * BND && NSD == 2, "the diagonal lies in the first two tiles visited");
+  run_pipeline<NSD, NSD - 1, 2 * PERW, 2>(n_kt, load, tile);
 
   if (i < T) {
     float* out = p.dq + (head + i) * D;

@@ -128,12 +128,15 @@ __device__ void dyn_item(const FwdParams& p, int b, int h, int qt, unsigned char
   for (int db = 0; db < D / 32; ++db) o[db] = f32x16{};
   float m_used = kNegInf, l = 0.f;
 
+  // Key tiles are visited from the last one down, so that the two tiles that can hold a wave's
+  // diagonal (BM = 2 BN) come first: they run in a peeled region with the causal mask, and
+  // every later tile is a full one with no mask arithmetic.
   const int n_kt = min((qt + 1) * (BM / BN), (T + BN - 1) / BN);
-  auto load = [&](int J, int u) {
+  auto load = [&](int s, int u) {
+    const int J = max(n_kt - 1 - s, 0);   // steps past the end reload tile 0
     tile_load_rows<CPR, BN, NW>(st[u].k, K, J * BN, T);
     tile_load_rows<CPR, BN, NW>(st[u].v, V, J * BN, T);
   };
-
   // per-lane LDS offsets: K rows in pi order (one per k-step), V^T reads (per d-block)
   constexpr int NDB = D / 32;
   uint32_t koff[D / 16], voff[NDB][2];
@@ -145,15 +148,14 @@ __device__ void dyn_item(const FwdParams& p, int b, int h, int qt, unsigned char
     voff[db][1] = tr_off<CPR>(db * 32, 1, lane);
   }
 
-  auto tile = [&](int J, int u, bool) {
-    const DynStage<D>& sm = st[u];
-    const int j0 = J * BN;
-    if (j0 <= i0w) {  // tile meets this wave's causal region
+  // one key tile; `diag` (the tile holding this wave's diagonal) masks keys after the query
+  auto body = [&](const DynStage<D>& sm, int j0, bool diag) {
+    {
       // S^T for keys j0 .. j0+63: two independent 32-key chains, interleaved
       f32x16 s[2] = {f32x16{}, f32x16{}};
       pipelined<D / 8>([&](int x) { return lds_row<CPR>(sm.k, (x & 1) * 32, koff[x >> 1]); },
                        [&](int x, const bf16x8& a) { s[x & 1] = mfma32(a, qf[x >> 1], s[x & 1]); });
-      if (j0 + BN - 1 > i0w) {  // diagonal tile: keys after the query get -inf
+      if (diag) {  // keys after the query get -inf
         const int lim = i - j0 - 8 * hh;  // key offset kb*32 + acc_pos(r, hh) > i - j0
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb)
@@ -184,8 +186,18 @@ __device__ void dyn_item(const FwdParams& p, int b, int h, int qt, unsigned char
           [&](int x, const bf16x8& a) { o[x % NDB] = mfma32(a, pb[x / NDB], o[x % NDB]); });
     }
   };
+  auto tile = [&](int s, int u, bool peeled) {
+    const int j0 = (n_kt - 1 - s) * BN;
+    if (peeled) {
+      if (j0 > i0w) return;  // the tile lies after this wave's queries
+      body(st[u], j0, j0 + BN - 1 > i0w);
+    } else {
+      body(st[u], j0, false);
+    }
+  };
   constexpr int PERW = BN * CPR / (64 * NW);   // loads per wave and tile, for each of K, V
-  run_pipeline<NS, NS - 1, 2 * PERW, 0>(n_kt, load, tile);
+  static_assert(BM == 2 * BN && NS == 2, "the diagonal lies in the first two tiles visited");
+  run_pipeline<NS, NS - 1, 2 * PERW, 2>(n_kt, load, tile);
 
   const float lt = l + wave_shfl_xor32(l);
   if (i < T) {
