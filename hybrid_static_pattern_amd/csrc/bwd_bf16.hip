@@ -511,9 +511,9 @@ __device__ void dkdv_dyn(const BwdParams& p, int b, int h, int kt, unsigned char
 template <int D>
 __global__ __launch_bounds__(NTK, 2) void dkdv_kernel(const BwdParams p) {
   __shared__ __attribute__((aligned(16))) unsigned char smem[dkdv_smem_bytes<D>()];
-  const int kt = blockIdx.x / p.per_tile;
-  int rem = blockIdx.x % p.per_tile;
   const int nd = p.B * p.n_dyn;
+  int kt, rem;   // heaviest key tile (kt = 0) first
+  if (!xcd_item(blockIdx.x, nd, p.n_frz * p.n_chunks, kt, rem)) return;
   if (rem < nd) {
     dkdv_dyn<D>(p, rem / p.n_dyn, p.dyn[rem % p.n_dyn], kt, smem);
   } else {
@@ -536,10 +536,9 @@ __global__ __launch_bounds__(64 * NWD, 2) void dq_kernel(const BwdParams p) {
   constexpr int NDB = D / 32;
   __shared__ __attribute__((aligned(16))) unsigned char smem_raw[NSD * sizeof(DqSmem<D>)];
   DqSmem<D>* stg = reinterpret_cast<DqSmem<D>*>(smem_raw);
-  const int item = blockIdx.x;
-  const int n_qt = p.n_tiles;
-  const int qt = n_qt - 1 - item / (p.B * p.n_dyn);
-  const int bh = item % (p.B * p.n_dyn);
+  int row, bh;
+  if (!xcd_item(blockIdx.x, p.B * p.n_dyn, 0, row, bh)) return;
+  const int qt = p.n_tiles - 1 - row;   // heaviest q-tile first
   const int b = bh / p.n_dyn, h = p.dyn[bh % p.n_dyn];
   const int lane = lane_id(), w = wave_id();
   const int m = lane & 31, hh = lane >> 5;
@@ -702,8 +701,8 @@ hipError_t launch_bwd_bf16(const AttnArgs& a, const void* q, const void* k, cons
   p.n_tiles = (a.T + BNK - 1) / BNK;
   p.n_chunks = (a.B * a.D + FCOLS - 1) / FCOLS;
   p.per_tile = a.B * p.n_dyn + p.n_frz * p.n_chunks;
-  const int n_items = p.n_tiles * p.per_tile;
-  if (n_items > 0) {
+  const int n_items = p.n_tiles * xcd_row_slots(a.B * p.n_dyn, p.n_frz * p.n_chunks);
+  if (p.per_tile > 0) {
     prof_begin("dkdv", s);
     if (a.D == 64)
       hipLaunchKernelGGL(dkdv_kernel<64>, dim3(n_items), dim3(NTK), 0, s, p);
@@ -714,7 +713,7 @@ hipError_t launch_bwd_bf16(const AttnArgs& a, const void* q, const void* k, cons
   }
   if (p.n_dyn == 0) return hipSuccess;
   p.n_tiles = (a.T + BMD - 1) / BMD;
-  const int n_dq = p.n_tiles * a.B * p.n_dyn;
+  const int n_dq = p.n_tiles * xcd_row_slots(a.B * p.n_dyn, 0);
   prof_begin("dq", s);
   if (a.D == 64)
     hipLaunchKernelGGL(dq_kernel<64>, dim3(n_dq), dim3(64 * NWD), 0, s, p);

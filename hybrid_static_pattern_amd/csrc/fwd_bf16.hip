@@ -342,10 +342,10 @@ __device__ void frz_item(const FwdParams& p, int h, int chunk, int qt, unsigned 
 template <int D>
 __global__ __launch_bounds__(NTH, 2) void hybrid_fwd_kernel(const FwdParams p) {
   __shared__ __attribute__((aligned(16))) unsigned char smem[smem_bytes<D>()];
-  const int item = blockIdx.x;
-  const int qt = p.n_qt - 1 - item / p.per_qt;
-  int rem = item % p.per_qt;
   const int nd = p.B * p.n_dyn;
+  int row, rem;
+  if (!xcd_item(blockIdx.x, nd, p.n_frz * p.n_chunks, row, rem)) return;
+  const int qt = p.n_qt - 1 - row;   // heaviest q-tile first
   if (rem < nd) {
     dyn_item<D>(p, rem / p.n_dyn, p.dyn[rem % p.n_dyn], qt, smem);
   } else {
@@ -381,8 +381,8 @@ hipError_t launch_fwd_bf16(const AttnArgs& a, const void* q, const void* k, cons
     p.dyn[x] = a.heads.dyn[x];
     p.frz[x] = a.heads.frz[x];
   }
-  const int n_items = p.n_qt * p.per_qt;
-  if (n_items == 0) return hipSuccess;
+  const int n_items = p.n_qt * xcd_row_slots(a.B * p.n_dyn, p.n_frz * p.n_chunks);
+  if (p.per_qt == 0) return hipSuccess;
   prof_begin("hybrid_fwd", s);
   if (a.D == 64)
     hipLaunchKernelGGL(hybrid_fwd_kernel<64>, dim3(n_items), dim3(NTH), 0, s, p);

@@ -262,6 +262,31 @@ __device__ __forceinline__ void tile_load_rows(bf16* tile, const bf16* src, int 
   }
 }
 
+// XCD-aware work-item map. MI355X has 8 XCDs, each with its own L2, and workgroup b runs on
+// XCD b % 8. Items come in rows (one row per tile position, heaviest row first) of nd
+// "stream" items (one per ordinary (b, h): the items of one stream read the same K/V or Q/dO
+// rows) followed by nf other items. A row is padded to a multiple of 8 slots, so stream item
+// x of every row lands on XCD x % 8 and its reads are shared through one L2; the nf items and
+// the empty slots of the padding rotate by row so that every XCD gets the same share of them.
+// Returns false for an empty slot; else the row and the item index in the row (0 .. nd + nf).
+constexpr int kNumXcd = 8;
+__host__ __device__ __forceinline__ int xcd_row_slots(int nd, int nf) {
+  return (nd + nf + kNumXcd - 1) / kNumXcd * kNumXcd;
+}
+__device__ __forceinline__ bool xcd_item(int b, int nd, int nf, int& row, int& item) {
+  const int slots = xcd_row_slots(nd, nf);
+  row = b / slots;
+  const int slot = b % slots;
+  if (slot < nd) {
+    item = slot;
+    return true;
+  }
+  const int tail = slots - nd;   // nf items and slots - nd - nf empty slots, rotated by row
+  const int t = (slot - nd + row * (tail - nf)) % tail;
+  item = nd + t;
+  return t < nf;
+}
+
 __device__ __forceinline__ float wave_shfl_xor32(float x) {
   return __shfl_xor(x, 32, 64);
 }
