@@ -89,7 +89,7 @@ constexpr int smem_bytes() {
 template <int NACC>
 __device__ __forceinline__ float online_rescale(float mx, float c, float& m_used, float& l,
                                                 f32x16 (&acc)[NACC]) {
-  mx = fmaxf(mx, wave_shfl_xor32(mx)) * c;
+  mx = xhalf_max(mx) * c;
   const bool up = mx > m_used + kRescaleSlack;
   if (__any(up)) {
     const float m_new = up ? mx : m_used;
@@ -199,7 +199,7 @@ __device__ void dyn_item(const FwdParams& p, int b, int h, int qt, unsigned char
   static_assert(BM == 2 * BN && NS == 2, "the diagonal lies in the first two tiles visited");
   run_pipeline<NS, NS - 1, 2 * PERW, 2>(n_kt, load, tile);
 
-  const float lt = l + wave_shfl_xor32(l);
+  const float lt = xhalf_sum(l);
   if (i < T) {
     const float inv = 1.f / lt;
     bf16* O = p.o + head * D + (size_t)i * D;
@@ -315,7 +315,7 @@ __device__ void frz_item(const FwdParams& p, int h, int chunk, int qt, unsigned 
   };
   run_pipeline<NS, NS - 1, PERW + FTAB / 64, 0>(n_kt, load, tile);
 
-  const float lt = l + wave_shfl_xor32(l);
+  const float lt = xhalf_sum(l);
   if (i < T) {
     const float inv = 1.f / lt;
 #pragma unroll

@@ -287,8 +287,24 @@ __device__ __forceinline__ bool xcd_item(int b, int nd, int nf, int& row, int& i
   return t < nf;
 }
 
-__device__ __forceinline__ float wave_shfl_xor32(float x) {
-  return __shfl_xor(x, 32, 64);
+// Combine a value across the two half-waves (lanes l and l ^ 32) with v_permlane32_swap (no
+// LDS round trip). Swapping two copies of x leaves the lower half's values in the first and
+// the upper half's in the second, on every lane. Inline assembly keeps the two copies in
+// separate registers (the compiler folds the builtin's results when both inputs are equal).
+__device__ __forceinline__ void xhalf_swap(float x, float& lo, float& hi) {
+  lo = x;
+  hi = x;
+  asm volatile("s_nop 1\n\tv_permlane32_swap_b32 %0, %1" : "+v"(lo), "+v"(hi));
+}
+__device__ __forceinline__ float xhalf_max(float x) {
+  float lo, hi;
+  xhalf_swap(x, lo, hi);
+  return fmaxf(lo, hi);
+}
+__device__ __forceinline__ float xhalf_sum(float x) {
+  float lo, hi;
+  xhalf_swap(x, lo, hi);
+  return lo + hi;
 }
 
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {

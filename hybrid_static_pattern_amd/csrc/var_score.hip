@@ -107,7 +107,7 @@ __global__ __launch_bounds__(NTH, 2) void var_lse_kernel(const VarParams p) {
           s[kb][r] = x;
           mx = fmaxf(mx, x);
         }
-      mx = fmaxf(mx, wave_shfl_xor32(mx));
+      mx = xhalf_max(mx);
       const float m_new = fmaxf(mx_run, mx);
       l *= (mx_run == kNegInf) ? 0.f : __builtin_amdgcn_exp2f(mx_run - m_new);
       mx_run = m_new;
@@ -119,7 +119,7 @@ __global__ __launch_bounds__(NTH, 2) void var_lse_kernel(const VarParams p) {
     wait_vm0();
     __syncthreads();
   }
-  const float lt = l + wave_shfl_xor32(l);
+  const float lt = xhalf_sum(l);
   if (i < T && hh == 0) p.lse2[head + i] = mx_run + __log2f(lt);
 }
 
