@@ -98,6 +98,7 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-sweep", action="store_true", help="skip the r=0 / r=50%% timings")
     ap.add_argument("--no-calibration", action="store_true", help="skip the calibration-score timing")
+    ap.add_argument("--no-prefill", action="store_true", help="skip the causal-prefill timings")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="first run one plain elementwise copy (torch.neg) of this many MiB, a "
                          "known-size reference for the FETCH_SIZE / WRITE_SIZE counters")
@@ -209,6 +210,9 @@ def main():
     if not args.no_calibration:
         log("timing the calibration score")
         out["calibration"] = calibration(torch, inputs, profiling, saf, args.steps, args.warmup)
+    if not args.no_prefill:
+        log("timing the causal prefill workload")
+        out["prefill"] = prefill(torch, inputs, saf, args.steps, args.warmup)
     if not args.no_cpu_baseline:
         log("timing the CPU oracle on a sample of the layer")
     out["cpu_baseline"] = None if args.no_cpu_baseline else cpu_baseline(L, n_dyn, n_frz)
@@ -221,6 +225,60 @@ def traffic_bytes(profiling, prof_name):
     k = profiling.PROF_TO_KERNEL.get(prof_name)
     d = profiling.read_summary(k, os.path.join(ROOT, "profiles")) if k else None
     return None if d is None else d["fetch_bytes"] + d["write_bytes"]
+
+
+def prefill(torch, inputs, saf, steps, warmup):
+    """Causal prefill (forward only) on the 124M shape, H = 12, d_h = 64: batch 64 for each
+    length in inputs.PREFILL at r = 0, 25% and 50%, and B = 1, T = 4096. Q, K, V are drawn on
+    the device (seeded N(0, 1) in bf16), alpha / rho from inputs.make_tables; the frozen heads
+    are a seeded sample. Reports ms per forward, tokens/s and the speed-up over r = 0."""
+    P = inputs.PREFILL
+    H, D = P["H"], P["D"]
+    dev = torch.device("cuda:0")
+    gen = torch.Generator(device=dev)
+
+    def masks(seed):
+        out = []
+        for nf in P["n_frozen"]:
+            m = np.zeros(H, np.uint8)
+            if nf:
+                m[np.sort(np.random.default_rng(seed).choice(H, nf, replace=False))] = 1
+            out.append(m)
+        return out
+
+    def run(B, T, seed):
+        gen.manual_seed(seed)
+        q, k, v = (torch.randn((B, H, T, D), generator=gen, device=dev).to(torch.bfloat16) for _ in range(3))
+        alpha, rho = (torch.from_numpy(x).to(dev) for x in inputs.make_tables(np.random.default_rng(seed), H, T))
+        o = torch.empty_like(v)
+        lse = torch.empty((B, H, T), dtype=torch.float32, device=dev)
+        res = {}
+        for m in masks(seed):
+            for _ in range(warmup):
+                saf.attn_fwd(q, k, v, m, alpha, rho, o=o, lse=lse)
+            torch.cuda.synchronize()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            for _ in range(steps):
+                saf.attn_fwd(q, k, v, m, alpha, rho, o=o, lse=lse)
+            e1.record()
+            torch.cuda.synchronize()
+            ms = e0.elapsed_time(e1) / steps
+            nf = int(m.sum())
+            res[f"r{round(100 * nf / H)}"] = {"ms": ms, "tokens_per_s": B * T / (ms * 1e-3),
+                                               "tflops": (4 * (H - nf) + 2 * nf) * B * D * causal_pairs(T) / (ms * 1e-3) / 1e12}
+        for key in list(res):
+            if key != "r0":
+                res[key]["speedup_vs_r0"] = res["r0"]["ms"] / res[key]["ms"]
+        del q, k, v, o, lse
+        return res
+
+    out = {"workload": f"causal prefill, forward only, H={H}, d_h={D}, bf16", "B": P["B"], "by_T": {}}
+    for T in P["T"]:
+        out["by_T"][str(T)] = run(P["B"], T, P["seed"] + T)
+    s = P["single"]
+    out["single"] = {"B": s["B"], "T": s["T"], **run(s["B"], s["T"], P["seed"])}
+    return out
 
 
 def calibration(torch, inputs, profiling, saf, steps, warmup):

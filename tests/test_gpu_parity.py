@@ -290,6 +290,14 @@ def test_full_1b_half_frozen(S):
     _full(S, "l1b_fwdbwd", [(0, first_frozen)], n_frozen=8)
 
 
+def test_full_prefill_t512(S):
+    _full(S, "prefill_t512", [(63, first_frozen), (0, last_dynamic)], bwd=False)
+
+
+def test_full_prefill_t2048_half_frozen(S):
+    _full(S, "prefill_t2048", [(31, first_frozen), (5, last_dynamic)], bwd=False)
+
+
 def test_full_calibration_sampled(S):
     C = inputs.make_calibration(**inputs.CALIBRATION)
     tau = C["tau"]
