@@ -37,7 +37,7 @@ constexpr int NWD = 4;     // waves per dQ workgroup (two workgroups per CU)
 constexpr int BMD = 32 * NWD;   // queries per dQ workgroup
 constexpr int BND = 64;    // keys per dQ step
 constexpr int NSD = 2;     // dQ LDS stages
-constexpr int FCOLS = 256;
+constexpr int FCOLS = 256;   // batch-folded columns per frozen item (at most)
 
 struct BwdParams {
   const bf16* q;
@@ -221,20 +221,24 @@ constexpr int dkdv_smem_bytes() {
 }
 
 // Frozen item (h, 256-key tile, column chunk): dV_b[j] = sum_{i>=j} P(i,j) dO_b[i] for the
-// batch folded into up to 256 columns. Each wave keeps its 32 keys x 256 columns of fp32 dV;
-// P^T is regenerated per lane from alpha, rho and log Z (entries for j > i come out as 0 from
-// the -inf distances of the window) and split into bf16 high and low parts.
-template <int D>
+// batch folded into FC (64, 128 or 256) columns. Each wave keeps its 32 keys x FC columns of
+// fp32 dV; P^T is regenerated per lane from alpha, rho and log Z (entries for j > i come out
+// as 0 from the -inf distances of the window) and split into bf16 high and low parts.
+template <int D, int FC>
 __device__ void dv_frz(const BwdParams& p, int h, int chunk, int kt, unsigned char* smem_raw) {
-  constexpr int CPR = FCOLS / 8;
-  constexpr int NCB = FCOLS / 16;
-  constexpr int PERW = BMQ * CPR / NTK;   // 16-byte chunks per lane per step
+  constexpr int CPR = FC / 8;
+  constexpr int NCB = FC / 16;
+  // 16-byte chunks per lane per step. At FC = 64 the 32 x 64 tile is 4 KiB, half a chunk per
+  // lane: every wave still loads one (the same number of loads on every wave keeps the
+  // pipeline's counter waits uniform), and waves 4-7 fill blocks 4-7 of the stage, past the
+  // tile, with the next 32 rows, which no one reads.
+  constexpr int PERW = BMQ * CPR >= NTK ? BMQ * CPR / NTK : 1;
   FrzStage* stg = reinterpret_cast<FrzStage*>(smem_raw);
   const int lane = lane_id(), w = wave_id();
   const int n = lane & 15, g = lane >> 4;
   const int T = p.T, H = p.H, B = p.B;
-  const int col0 = chunk * FCOLS;
-  const int ncols = min(FCOLS, B * D - col0);
+  const int col0 = chunk * FC;
+  const int ncols = min(FC, B * D - col0);
   const int kbase = kt * BNK, k0w = kbase + KPW * w;
   const float* rho = p.rho + (size_t)h * p.tab_stride;
   float a2[NKG];
@@ -508,7 +512,7 @@ __device__ void dkdv_dyn(const BwdParams& p, int b, int h, int kt, unsigned char
 
 // Both item kinds in one launch, heaviest key tile first: per key tile, the ordinary
 // (b, h) items, then the frozen (h, column chunk) items.
-template <int D>
+template <int D, int FC>
 __global__ __launch_bounds__(NTK, 2) void dkdv_kernel(const BwdParams p) {
   __shared__ __attribute__((aligned(16))) unsigned char smem[dkdv_smem_bytes<D>()];
   const int nd = p.B * p.n_dyn;
@@ -518,7 +522,7 @@ __global__ __launch_bounds__(NTK, 2) void dkdv_kernel(const BwdParams p) {
     dkdv_dyn<D>(p, rem / p.n_dyn, p.dyn[rem % p.n_dyn], kt, smem);
   } else {
     rem -= nd;
-    dv_frz<D>(p, p.frz[rem / p.n_chunks], rem % p.n_chunks, kt, smem);
+    dv_frz<D, FC>(p, p.frz[rem / p.n_chunks], rem % p.n_chunks, kt, smem);
   }
 }
 
@@ -699,15 +703,22 @@ hipError_t launch_bwd_bf16(const AttnArgs& a, const void* q, const void* k, cons
   BwdParams p = make_params(a, q, k, v, dO, lse, delta, alpha, rho, dq, dk, dv);
   p.ls2 = ls2;
   p.n_tiles = (a.T + BNK - 1) / BNK;
-  p.n_chunks = (a.B * a.D + FCOLS - 1) / FCOLS;
+  // folded columns per frozen item: B * D rounded up to 64, 128 or 256
+  const int fc = a.B * a.D <= 64 ? 64 : (a.B * a.D <= 128 ? 128 : FCOLS);
+  p.n_chunks = (a.B * a.D + fc - 1) / fc;
   p.per_tile = a.B * p.n_dyn + p.n_frz * p.n_chunks;
   const int n_items = p.n_tiles * xcd_row_slots(a.B * p.n_dyn, p.n_frz * p.n_chunks);
   if (p.per_tile > 0) {
     prof_begin("dkdv", s);
-    if (a.D == 64)
-      hipLaunchKernelGGL(dkdv_kernel<64>, dim3(n_items), dim3(NTK), 0, s, p);
-    else
-      hipLaunchKernelGGL(dkdv_kernel<128>, dim3(n_items), dim3(NTK), 0, s, p);
+    const dim3 grid(n_items), block(NTK);
+    if (a.D == 64) {
+      if (fc == 64) hipLaunchKernelGGL((dkdv_kernel<64, 64>), grid, block, 0, s, p);
+      else if (fc == 128) hipLaunchKernelGGL((dkdv_kernel<64, 128>), grid, block, 0, s, p);
+      else hipLaunchKernelGGL((dkdv_kernel<64, FCOLS>), grid, block, 0, s, p);
+    } else {
+      if (fc == 128) hipLaunchKernelGGL((dkdv_kernel<128, 128>), grid, block, 0, s, p);
+      else hipLaunchKernelGGL((dkdv_kernel<128, FCOLS>), grid, block, 0, s, p);
+    }
     prof_end(s);
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }

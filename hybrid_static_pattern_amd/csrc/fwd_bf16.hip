@@ -40,7 +40,7 @@ constexpr int BM = 32 * NW;    // queries per workgroup
 constexpr int BN = 64;         // keys per tile
 constexpr int NTH = 64 * NW;
 constexpr int NS = 2;          // LDS stages
-constexpr int FCOLS = 256;     // batch-folded columns per frozen item
+constexpr int FCOLS = 256;     // batch-folded columns per frozen item (at most)
 constexpr int FTAB = 192;      // per-wave frozen table: alpha of the tile's keys, then rho
 
 // -inf, read in place of table entries past the data (keys past T, negative distances)
@@ -219,23 +219,24 @@ __device__ void dyn_item(const FwdParams& p, int b, int h, int qt, unsigned char
 
 // ---------------------------------------------------------------- frozen item
 
-template <int D>
+// FC: folded columns per item (64, 128 or 256: B * D rounded up, at most 256)
+template <int D, int FC>
 __device__ void frz_item(const FwdParams& p, int h, int chunk, int qt, unsigned char* smem_raw) {
-  constexpr int CPR = FCOLS / 8;
+  constexpr int CPR = FC / 8;
   FrzStage* st = reinterpret_cast<FrzStage*>(smem_raw);
   const int lane = lane_id(), w = wave_id();
   const int m = lane & 31, hh = lane >> 5;
   const int T = p.T, H = p.H, B = p.B;
-  const int col0 = chunk * FCOLS;
-  const int ncols = min(FCOLS, B * D - col0);
+  const int col0 = chunk * FC;
+  const int ncols = min(FC, B * D - col0);
   const int i0w = qt * BM + w * 32, i = i0w + m;
   const float* alpha = p.alpha + (size_t)h * p.tab_stride;
   const float* rho = p.rho + (size_t)h * p.tab_stride;
 
   // Columns past B*D (a partial last chunk) read clamped, valid data and are not stored.
-  f32x16 o[FCOLS / 32];
+  f32x16 o[FC / 32];
 #pragma unroll
-  for (int cb = 0; cb < FCOLS / 32; ++cb) o[cb] = f32x16{};
+  for (int cb = 0; cb < FC / 32; ++cb) o[cb] = f32x16{};
   float m_used = kNegInf, l = 0.f;
 
   const int n_kt = min((qt + 1) * (BM / BN), (T + BN - 1) / BN);
@@ -275,9 +276,9 @@ __device__ void frz_item(const FwdParams& p, int h, int chunk, int qt, unsigned 
     }
   };
 
-  uint32_t voff[FCOLS / 32][2];
+  uint32_t voff[FC / 32][2];
 #pragma unroll
-  for (int cb = 0; cb < FCOLS / 32; ++cb) {
+  for (int cb = 0; cb < FC / 32; ++cb) {
     voff[cb][0] = tr_off<CPR>(cb * 32, 0, lane);
     voff[cb][1] = tr_off<CPR>(cb * 32, 1, lane);
   }
@@ -288,28 +289,36 @@ __device__ void frz_item(const FwdParams& p, int h, int chunk, int qt, unsigned 
     if (j0 <= i0w) {
       // logits alpha(j) + rho(i - j); the window index of (i, j0 + kofs + e) is
       // m - (kofs + e) + 63, and entries for j > i hold -inf, so the causal mask comes for
-      // free. They are read twice from LDS (for the max, then for the exps) rather than held
-      // in registers next to 128 accumulators.
+      // free. Up to 128 columns the 32 logits stay in registers between the max and the
+      // exps; next to the 128 accumulators of 256 columns they are read twice from LDS.
       const float* tb = sm.tab[w];
       const int rb0 = BN + m + BN - 1 - hh * 8;
+      auto logit = [&](int ks, int e) { return tb[ks * 16 + hh * 8 + e] + tb[rb0 - ks * 16 - e]; };
+      float lg[FC <= 128 ? 4 : 1][8];
       float mx = kNegInf;
 #pragma unroll
       for (int ks = 0; ks < 4; ++ks)
 #pragma unroll
-        for (int e = 0; e < 8; ++e) mx = fmaxf(mx, tb[ks * 16 + hh * 8 + e] + tb[rb0 - ks * 16 - e]);
-      const float msub = online_rescale<FCOLS / 32>(mx, kLog2e, m_used, l, o);
+        for (int e = 0; e < 8; ++e) {
+          const float x = logit(ks, e);
+          if constexpr (FC <= 128) lg[ks][e] = x;
+          mx = fmaxf(mx, x);
+        }
+      const float msub = online_rescale<FC / 32>(mx, kLog2e, m_used, l, o);
 #pragma unroll
       for (int ks = 0; ks < 4; ++ks) {
-        const int kofs = ks * 16 + hh * 8;
         float pv[8];
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
-          pv[e] = __builtin_amdgcn_exp2f(__builtin_fmaf(tb[kofs + e] + tb[rb0 - ks * 16 - e], kLog2e, -msub));
+          float x;
+          if constexpr (FC <= 128) x = lg[ks][e];
+          else x = logit(ks, e);
+          pv[e] = __builtin_amdgcn_exp2f(__builtin_fmaf(x, kLog2e, -msub));
           l += pv[e];
         }
         const bf16x8 pb = pack8(pv);
-        pipelined<FCOLS / 32>([&](int cb) { return lds_tr<CPR>(sm.v, ks * 16, voff[cb][0], voff[cb][1]); },
-                              [&](int cb, const bf16x8& a) { o[cb] = mfma32(a, pb, o[cb]); });
+        pipelined<FC / 32>([&](int cb) { return lds_tr<CPR>(sm.v, ks * 16, voff[cb][0], voff[cb][1]); },
+                           [&](int cb, const bf16x8& a) { o[cb] = mfma32(a, pb, o[cb]); });
       }
     }
   };
@@ -319,7 +328,7 @@ __device__ void frz_item(const FwdParams& p, int h, int chunk, int qt, unsigned 
   if (i < T) {
     const float inv = 1.f / lt;
 #pragma unroll
-    for (int cb = 0; cb < FCOLS / 32; ++cb) {
+    for (int cb = 0; cb < FC / 32; ++cb) {
       if (cb * 32 >= ncols) continue;
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
@@ -339,7 +348,7 @@ __device__ void frz_item(const FwdParams& p, int h, int chunk, int qt, unsigned 
   }
 }
 
-template <int D>
+template <int D, int FC>
 __global__ __launch_bounds__(NTH, 2) void hybrid_fwd_kernel(const FwdParams p) {
   __shared__ __attribute__((aligned(16))) unsigned char smem[smem_bytes<D>()];
   const int nd = p.B * p.n_dyn;
@@ -350,7 +359,7 @@ __global__ __launch_bounds__(NTH, 2) void hybrid_fwd_kernel(const FwdParams p) {
     dyn_item<D>(p, rem / p.n_dyn, p.dyn[rem % p.n_dyn], qt, smem);
   } else {
     rem -= nd;
-    frz_item<D>(p, p.frz[rem / p.n_chunks], rem % p.n_chunks, qt, smem);
+    frz_item<D, FC>(p, p.frz[rem / p.n_chunks], rem % p.n_chunks, qt, smem);
   }
 }
 
@@ -375,7 +384,9 @@ hipError_t launch_fwd_bf16(const AttnArgs& a, const void* q, const void* k, cons
   p.n_dyn = a.heads.n_dyn;
   p.n_frz = a.heads.n_frz;
   p.n_qt = (a.T + BM - 1) / BM;
-  p.n_chunks = (a.B * a.D + FCOLS - 1) / FCOLS;
+  // folded columns per frozen item: B * D rounded up to 64, 128 or 256
+  const int fc = a.B * a.D <= 64 ? 64 : (a.B * a.D <= 128 ? 128 : FCOLS);
+  p.n_chunks = (a.B * a.D + fc - 1) / fc;
   p.per_qt = a.B * p.n_dyn + p.n_frz * p.n_chunks;
   for (int x = 0; x < kMaxHeads; ++x) {
     p.dyn[x] = a.heads.dyn[x];
@@ -384,10 +395,15 @@ hipError_t launch_fwd_bf16(const AttnArgs& a, const void* q, const void* k, cons
   const int n_items = p.n_qt * xcd_row_slots(a.B * p.n_dyn, p.n_frz * p.n_chunks);
   if (p.per_qt == 0) return hipSuccess;
   prof_begin("hybrid_fwd", s);
-  if (a.D == 64)
-    hipLaunchKernelGGL(hybrid_fwd_kernel<64>, dim3(n_items), dim3(NTH), 0, s, p);
-  else
-    hipLaunchKernelGGL(hybrid_fwd_kernel<128>, dim3(n_items), dim3(NTH), 0, s, p);
+  const dim3 grid(n_items), block(NTH);
+  if (a.D == 64) {
+    if (fc == 64) hipLaunchKernelGGL((hybrid_fwd_kernel<64, 64>), grid, block, 0, s, p);
+    else if (fc == 128) hipLaunchKernelGGL((hybrid_fwd_kernel<64, 128>), grid, block, 0, s, p);
+    else hipLaunchKernelGGL((hybrid_fwd_kernel<64, FCOLS>), grid, block, 0, s, p);
+  } else {
+    if (fc == 128) hipLaunchKernelGGL((hybrid_fwd_kernel<128, 128>), grid, block, 0, s, p);
+    else hipLaunchKernelGGL((hybrid_fwd_kernel<128, FCOLS>), grid, block, 0, s, p);
+  }
   prof_end(s);
   return hipGetLastError();
 }

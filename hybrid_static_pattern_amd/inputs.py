@@ -119,11 +119,12 @@ WORKLOADS = {
 }
 CALIBRATION = dict(N=64, H=12, T=1024, D=64, dtype=BF16, seed=4)
 # Causal prefill on the 124M shape (forward only): batch 64 over a range of lengths at
-# r = 0, 25% and 50%, and the single-sequence case B = 1, T = 4096. The two entries below are
-# the parity cases; bench.py times the whole range.
+# r = 0, 25% and 50%, and the single-sequence case B = 1, T = 4096. The entries below are the
+# parity cases; bench.py times the whole range.
 WORKLOADS.update({
     "prefill_t512": dict(B=64, H=12, T=512, D=64, dtype=BF16, seed=5, n_frozen=3),
     "prefill_t2048": dict(B=64, H=12, T=2048, D=64, dtype=BF16, seed=6, n_frozen=6),
+    "prefill_b1_t4096": dict(B=1, H=12, T=4096, D=64, dtype=BF16, seed=8, n_frozen=6),
 })
 PREFILL = dict(B=64, H=12, D=64, T=(512, 1024, 2048, 4096, 8192, 16384), n_frozen=(0, 3, 6),
                single=dict(B=1, T=4096), seed=7)

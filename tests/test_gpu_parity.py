@@ -83,6 +83,8 @@ BF16_CASES = [
     (2, 3, 64, 64, []),           # all ordinary (r = 0)
     (2, 2, 200, 128, [0, 1]),     # all frozen: q, k are NULL
     (1, 2, 513, 128, [1]),        # crosses the 512-key boundary of the dK/dV tiles
+    (1, 2, 700, 64, [0]),         # folded columns 64 (the narrowest frozen item), ragged
+    (3, 2, 150, 64, [1]),         # folded columns 192 in a 256-column item
 ]
 
 
@@ -292,6 +294,10 @@ def test_full_1b_half_frozen(S):
 
 def test_full_prefill_t512(S):
     _full(S, "prefill_t512", [(63, first_frozen), (0, last_dynamic)], bwd=False)
+
+
+def test_full_prefill_single_sequence(S):
+    _full(S, "prefill_b1_t4096", [(0, first_frozen), (0, last_dynamic)])
 
 
 def test_full_prefill_t2048_half_frozen(S):
