@@ -54,18 +54,19 @@ def _f64(x):
 def pattern_stats(A):
     """Eq. (4) statistics of a causal row-stochastic target A [T,T] (entries j > i unused).
 
-    col(j)  = sum_{i >= j} A(i, j)        absolute key-position marginal;
-    dist(d) = sum_{i >= d} A(i, i - d)    distance marginal;
-    ent     = -(1/T) sum_i sum_{j<=i} A(i,j) log A(i,j), with 0 log 0 = 0: the mean row
-              entropy, the constant that turns the cross-entropy into the KL.
+    col(j)  = sum_{i >= j} A(i, j)             absolute key-position marginal;
+    dist(d) = sum_{i >= d} A(i, i - d)         distance marginal;
+    ent(j)  = -sum_{i >= j} A(i, j) log A(i, j) with 0 log 0 = 0, the column's share of the
+              target's entropy: sum_j ent(j) / T is the mean row entropy, the constant that
+              turns the mean row cross-entropy into the mean row KL.
     """
     A = _f64(A)
     T = A.shape[0]
     L = np.tril(A)
     col = L.sum(axis=0)
     dist = np.array([np.trace(L, offset=-d) for d in range(T)])
-    pos = L > 0
-    ent = float(-(L[pos] * np.log(L[pos])).sum() / T)
+    logL = np.log(np.where(L > 0, L, 1.0))
+    ent = -(L * logL).sum(axis=0)
     return col, dist, ent
 
 

@@ -32,9 +32,10 @@ def _stats_entropy_sign(A):
     return col, dist, -ent
 
 
-def _stats_entropy_sum(A):
-    col, dist, ent = _orig("pattern_stats")(A)
-    return col, dist, ent * np.shape(A)[0]
+def _stats_entropy_by_rows(A):
+    col, dist, _ = _orig("pattern_stats")(A)
+    L = np.tril(np.asarray(A, float))
+    return col, dist, -(L * np.log(np.where(L > 0, L, 1.0))).sum(axis=1)
 
 
 def _grad_sign(alpha, rho, col, dist):
@@ -91,7 +92,7 @@ MUTANTS = {
     "stats: distance marginal from the upper diagonals": ("pattern_stats", _stats_dist_transposed),
     "stats: column marginal replaced by row sums": ("pattern_stats", _stats_row_sums),
     "stats: entropy sign": ("pattern_stats", _stats_entropy_sign),
-    "stats: entropy summed, not averaged, over rows": ("pattern_stats", _stats_entropy_sum),
+    "stats: entropy shares by rows, not columns": ("pattern_stats", _stats_entropy_by_rows),
     "gradient: sign flipped": ("objective_gradient", _grad_sign),
     "gradient: 1/T dropped": ("objective_gradient", _grad_no_T),
     "gradient: marginals swapped": ("objective_gradient", _grad_swapped),
