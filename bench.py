@@ -28,6 +28,9 @@ PEAK_FP32_VALU_TFLOPS = 256 * 4 * 16 * 2 * 2.4e9 / 1e12
 # fp32 operations per (causal pair, sequence) in the Welford pass of the calibration score:
 # logit-to-log2 FMA (2), exp2 (1), delta (1), mean FMA (2), M2 subtract + FMA (3)
 WELFORD_FLOP_PER_SAMPLE = 9
+# exp2 rate: transcendental VALU instructions issue at a quarter of the fp32 rate, so
+# 256 CUs x 4 SIMDs x 4 lanes per clock x 2.4 GHz
+PEAK_EXP_PER_S = 256 * 4 * 4 * 2.4e9
 
 
 def log(msg: str) -> None:
@@ -99,6 +102,7 @@ def main():
     ap.add_argument("--no-sweep", action="store_true", help="skip the r=0 / r=50%% timings")
     ap.add_argument("--no-calibration", action="store_true", help="skip the calibration-score timing")
     ap.add_argument("--no-prefill", action="store_true", help="skip the causal-prefill timings")
+    ap.add_argument("--no-fit", action="store_true", help="skip the compact-fit timing")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="first run one plain elementwise copy (torch.neg) of this many MiB, a "
                          "known-size reference for the FETCH_SIZE / WRITE_SIZE counters")
@@ -210,6 +214,9 @@ def main():
     if not args.no_calibration:
         log("timing the calibration score")
         out["calibration"] = calibration(torch, inputs, profiling, saf, args.steps, args.warmup)
+    if not args.no_fit:
+        log("timing the compact pattern fit")
+        out["fit"] = fit(torch, inputs, saf, args.no_cpu_baseline)
     if not args.no_prefill:
         log("timing the causal prefill workload")
         out["prefill"] = prefill(torch, inputs, saf, args.steps, args.warmup)
@@ -322,6 +329,75 @@ def calibration(torch, inputs, profiling, saf, steps, warmup):
                      "unit": "TFLOP/s", "frac": wf / PEAK_FP32_VALU_TFLOPS,
                      "traffic": traffic_bytes(profiling, "var_welford")},
     }
+
+
+def fit(torch, inputs, saf, no_cpu):
+    """The compact fit (saf_pattern_stats + saf_compact_fit, 400 Adam steps) of every head of
+    the calibration workload, on the mean attention its saf_var_score produces, and the
+    selection with the fit's acceptance test at r = 25%."""
+    C = inputs.make_calibration(**inputs.CALIBRATION)
+    N, H, T, D = C["N"], C["H"], C["T"], C["D"]
+    dev = torch.device("cuda:0")
+    q = torch.from_numpy(C["q"]).to(dev).to(torch.bfloat16)
+    k = torch.from_numpy(C["k"]).to(dev).to(torch.bfloat16)
+    a_hat, s_var, _ = saf.var_score(q, k)
+    del q, k
+    steps = saf.FIT_STEPS
+    ws = torch.empty(saf.fit_workspace_size(H, T, steps), dtype=torch.uint8, device=dev)
+    col, dist, ent = (torch.empty((H, T), dtype=torch.float32, device=dev) for _ in range(3))
+    alpha, rho = (torch.empty((H, T), dtype=torch.float32, device=dev) for _ in range(2))
+    kl = torch.empty((H,), dtype=torch.float32, device=dev)
+
+    def run():
+        saf.pattern_stats(a_hat, col, dist, ent)
+        alpha.zero_()
+        rho.zero_()
+        saf.compact_fit(col, dist, ent, alpha=alpha, rho=rho, kl=kl, steps=steps, workspace=ws)
+
+    run()
+    torch.cuda.synchronize()
+    st = torch.cuda.current_stream()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    reps = 5
+    e0.record(st)
+    for _ in range(reps):
+        run()
+    e1.record(st)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / reps
+    saf.prof_enable(True)
+    run()
+    recs = saf.prof_read()
+    saf.prof_enable(False)
+    per = {}
+    for name, t in recs:
+        per.setdefault(name, []).append(t)
+    kern = {n: {"launches": len(v), "avg_us": 1e3 * float(np.mean(v))} for n, v in per.items()}
+    exps = steps * 3 * causal_pairs(T) * H     # log Z pass + both marginals, every step
+    achieved = exps / (ms * 1e-3)
+    kl_h = kl.cpu().numpy()
+    out = {
+        "workload": f"compact fit of the calibration heads: H={H} T={T}, {steps} Adam steps, targets from "
+                    f"saf_var_score (N={N})",
+        "ms": ms, "ms_per_step": ms / steps, "kernels": kern,
+        "kl": [float(x) for x in kl_h],
+        "selected_r25": [int(x) for x in saf.select_fitted(s_var.cpu().numpy(), kl_h, 0.25)],
+        "roofline": {"kernel": "fit_logz + fit_adam", "bound": "alu", "achieved": achieved / 1e12,
+                     "peak": PEAK_EXP_PER_S / 1e12, "unit": "Texp/s", "frac": achieved / PEAK_EXP_PER_S,
+                     "traffic": None},
+    }
+    if not no_cpu:
+        from oracle import compact_fit as cf
+        A0 = a_hat[0].double().cpu().numpy()
+        c0, d0, _ = cf.pattern_stats(A0)
+        n_cpu = 3
+        t0 = time.perf_counter()
+        cf.adam_fit(c0, d0, np.zeros(T), np.zeros(T), steps=n_cpu)
+        per_head_step = (time.perf_counter() - t0) / n_cpu
+        out["cpu_baseline"] = {"value": 1e3 * per_head_step * steps * H, "unit": "ms per fit (projected)",
+                               "cores": 1, "kind": "oracle",
+                               "sample": f"{n_cpu} Adam steps of one head at T={T}, scaled to {H} heads x {steps} steps"}
+    return out
 
 
 if __name__ == "__main__":

@@ -1,0 +1,280 @@
+// Compact static pattern fit (web page "When Can Attention Heads Be Statically Defined?:
+// 中文精读笔记", part 二.3, Eq. (3), Eq. (4), Appendix A.2).
+//
+// A candidate head's target pattern A (its mean attention) is replaced by
+//   P(i,j) = exp(alpha(j) + rho(i-j)) / Z(i),  j <= i,
+// fitted by minimising the mean row cross-entropy of P relative to A. That objective
+// depends on A only through its key-position marginal col(j) = sum_i A(i,j) and its
+// distance marginal dist(d) = sum_i A(i,i-d) (Eq. (4)):
+//   CE = (1/T) [sum_i log Z(i) - sum_j alpha(j) col(j) - sum_d rho(d) dist(d)],
+// with gradient (colP(j) - col(j)) / T and (distP(d) - dist(d)) / T, where colP and distP
+// are the same marginals of P. Each Adam step therefore needs log Z(i) for every row, then
+// both marginals of P; the mean row KL reported at the end is CE minus the target's mean
+// row entropy, whose per-column shares the statistics pass also produces.
+//
+// Every kernel gives one wave to one output (a row, a column or a distance) and spreads
+// the sum over that output's line of the causal triangle across the 64 lanes: the reads of
+// alpha, rho and log Z along a line are consecutive, L2-resident floats, and the work per
+// step (1.5 T(T+1) exps per head) is spread over 3 T waves per head instead of T threads.
+// Exponents are shifted by the row's max (log Z) or are never positive (the marginals, since
+// log Z(i) bounds every logit of row i), so no exp overflows.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+
+#include "saf_internal.h"
+
+namespace saf {
+namespace {
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kNegInf = -INFINITY;
+constexpr int FW = 4;      // waves per workgroup in the per-line kernels
+constexpr int SW = 16;     // waves per workgroup in the statistics kernel
+constexpr int U = 16;      // keys (or terms) per lane loaded before use in the per-line kernels
+
+__device__ __forceinline__ float wave_max(float x) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) x = fmaxf(x, __shfl_xor(x, o, 64));
+  return x;
+}
+__device__ __forceinline__ float wave_sum(float x) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) x += __shfl_xor(x, o, 64);
+  return x;
+}
+__device__ __forceinline__ double wave_sum(double x) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) x += __shfl_xor(x, o, 64);
+  return x;
+}
+
+// Eq. (4) statistics of the target A [H, T, T] (entries above the diagonal are not read):
+// col(x), dist(x) and ent(x) = -sum_{i>=x} A(i,x) log A(i,x) for x = 64 blockIdx.x + lane.
+// Wave w sums rows i = x0 + w, x0 + w + SW, ...; row i reads A(i, x) and A(i, i - x), both
+// 64 consecutive floats. The SW partial sums are added in a fixed order.
+__global__ __launch_bounds__(64 * SW) void stats_kernel(int T, const float* __restrict__ a,
+                                                        float* __restrict__ col,
+                                                        float* __restrict__ dist,
+                                                        float* __restrict__ ent) {
+  __shared__ float part[3][SW][64];
+  const int h = blockIdx.y, lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int x0 = blockIdx.x * 64, x = x0 + lane;
+  const float* ah = a + (size_t)h * T * T;
+  float c = 0.f, g = 0.f, e = 0.f;
+  for (int i = x0 + w; i < T; i += SW) {
+    if (x <= i) {
+      const float* row = ah + (size_t)i * T;
+      const float v = row[x];
+      c += v;
+      if (v > 0.f) e -= v * logf(v);
+      g += row[i - x];
+    }
+  }
+  part[0][w][lane] = c;
+  part[1][w][lane] = g;
+  part[2][w][lane] = e;
+  __syncthreads();
+  if (w < 3 && x < T) {
+    float s = 0.f;
+    for (int u = 0; u < SW; ++u) s += part[w][u][lane];
+    float* out = w == 0 ? col : (w == 1 ? dist : ent);
+    out[(size_t)h * T + x] = s;
+  }
+}
+
+// log Z(i) = log sum_{j<=i} exp(alpha(j) + rho(i-j)) for row i = FW blockIdx.x + wave.
+// The row is taken in chunks of 64 U keys: each lane first loads its U logits of the chunk
+// (U independent loads in flight, instead of one round trip per key), then the chunk's max
+// over the wave raises the running shift and the lane's partial sum is rescaled once.
+__global__ __launch_bounds__(64 * FW) void logz_kernel(int T, const float* __restrict__ alpha,
+                                                       const float* __restrict__ rho,
+                                                       float* __restrict__ logz) {
+  const int h = blockIdx.y, lane = threadIdx.x & 63;
+  const int i = blockIdx.x * FW + (threadIdx.x >> 6);
+  if (i >= T) return;
+  const float* al = alpha + (size_t)h * T;
+  const float* rh = rho + (size_t)h * T;
+  float mx = kNegInf, s = 0.f;
+  for (int j0 = 0; j0 <= i; j0 += 64 * U) {
+    float x[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int j = j0 + 64 * u + lane;
+      x[u] = j <= i ? al[j] + rh[i - j] : kNegInf;
+    }
+    float cm = x[0];
+#pragma unroll
+    for (int u = 1; u < U; ++u) cm = fmaxf(cm, x[u]);
+    const float m_new = fmaxf(mx, wave_max(cm));   // finite: key j0 <= i is in the chunk
+    float cs = 0.f;
+#pragma unroll
+    for (int u = 0; u < U; ++u) cs += __builtin_amdgcn_exp2f((x[u] - m_new) * kLog2e);
+    s = s * __builtin_amdgcn_exp2f((mx - m_new) * kLog2e) + cs;
+    mx = m_new;
+  }
+  s = wave_sum(s);
+  if (lane == 0) logz[(size_t)h * T + i] = mx + logf(s);
+}
+
+struct AdamStep {
+  float lr, beta1, beta2, eps;
+  float bc1, bc2;      // 1 - beta1^t, 1 - beta2^t
+  float inv_t;         // 1 / T
+};
+
+// Marginals of P for outputs o = FW blockIdx.x + wave in [0, 2T): o < T is column x = o
+// (own = alpha(x), other = rho), o >= T is distance x = o - T (own = rho(x), other = alpha).
+// Both are S(x) = sum_{t=0}^{T-1-x} exp(other(t) + own(x) - log Z(x + t)).
+// ADAM = false writes S into colP / distP. ADAM = true takes one Adam step on own(x) with
+// gradient (S - target(x)) / T and writes the new value to the other parameter buffer (the
+// current values are still being read by other waves); m and v are [H, 2T].
+template <bool ADAM>
+__global__ __launch_bounds__(64 * FW) void marg_kernel(int T, const float* __restrict__ alpha,
+                                                       const float* __restrict__ rho,
+                                                       const float* __restrict__ logz,
+                                                       float* __restrict__ out_col,    // colP, or new alpha
+                                                       float* __restrict__ out_dist,   // distP, or new rho
+                                                       const float* __restrict__ col,
+                                                       const float* __restrict__ dist,
+                                                       float* __restrict__ m, float* __restrict__ v,
+                                                       AdamStep st) {
+  const int h = blockIdx.y, lane = threadIdx.x & 63;
+  const int o = blockIdx.x * FW + (threadIdx.x >> 6);
+  if (o >= 2 * T) return;
+  const bool is_col = o < T;
+  const int x = is_col ? o : o - T;
+  const size_t hb = (size_t)h * T;
+  const float* own = (is_col ? alpha : rho) + hb;
+  const float* oth = (is_col ? rho : alpha) + hb;
+  const float* lz = logz + hb + x;
+  const float ox = own[x];
+  float s = 0.f;
+  for (int t0 = 0; t0 < T - x; t0 += 64 * U) {   // U loads of each array in flight per lane
+    float e[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int t = t0 + 64 * u + lane;
+      e[u] = t < T - x ? oth[t] + ox - lz[t] : kNegInf;
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) s += __builtin_amdgcn_exp2f(e[u] * kLog2e);
+  }
+  s = wave_sum(s);
+  if (lane != 0) return;
+  float* out = (is_col ? out_col : out_dist) + hb;
+  if constexpr (!ADAM) {
+    out[x] = s;
+  } else {
+    const float g = (s - (is_col ? col : dist)[hb + x]) * st.inv_t;
+    const size_t k = (size_t)h * 2 * T + o;
+    const float mm = st.beta1 * m[k] + (1.f - st.beta1) * g;
+    const float vv = st.beta2 * v[k] + (1.f - st.beta2) * g * g;
+    m[k] = mm;
+    v[k] = vv;
+    out[x] = ox - st.lr * (mm / st.bc1) / (sqrtf(vv / st.bc2) + st.eps);
+  }
+}
+
+// Mean row KL of each head: (1/T) [sum_i log Z(i) - sum_j alpha(j) col(j)
+// - sum_d rho(d) dist(d) - sum_j ent(j)], summed in double (the terms are O(T) and cancel).
+__global__ __launch_bounds__(256) void kl_kernel(int T, const float* __restrict__ alpha,
+                                                 const float* __restrict__ rho,
+                                                 const float* __restrict__ logz,
+                                                 const float* __restrict__ col,
+                                                 const float* __restrict__ dist,
+                                                 const float* __restrict__ ent,
+                                                 float* __restrict__ kl) {
+  __shared__ double part[4];
+  const int h = blockIdx.x, lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const size_t hb = (size_t)h * T;
+  double acc = 0.0;
+  for (int x = threadIdx.x; x < T; x += 256)
+    acc += (double)logz[hb + x] - (double)alpha[hb + x] * col[hb + x] -
+           (double)rho[hb + x] * dist[hb + x] - (double)ent[hb + x];
+  acc = wave_sum(acc);
+  if (lane == 0) part[w] = acc;
+  __syncthreads();
+  if (threadIdx.x == 0) kl[h] = (float)((part[0] + part[1] + part[2] + part[3]) / T);
+}
+
+__global__ void fill_kernel(float* __restrict__ p, size_t n, float val) {
+  for (size_t x = (size_t)blockIdx.x * blockDim.x + threadIdx.x; x < n; x += (size_t)gridDim.x * blockDim.x)
+    p[x] = val;
+}
+
+__global__ void copy_kernel(float* __restrict__ dst, const float* __restrict__ src, size_t n) {
+  for (size_t x = (size_t)blockIdx.x * blockDim.x + threadIdx.x; x < n; x += (size_t)gridDim.x * blockDim.x)
+    dst[x] = src[x];
+}
+
+int elementwise_blocks(size_t n) { return (int)std::min<size_t>((n + 255) / 256, 4096); }
+
+size_t pad64(size_t n) { return (n + 63) / 64 * 64; }
+
+}  // namespace
+
+hipError_t launch_pattern_stats(int H, int T, const float* a, float* col, float* dist, float* ent,
+                                hipStream_t s) {
+  prof_begin("fit_stats", s);
+  hipLaunchKernelGGL(stats_kernel, dim3((T + 63) / 64, H), dim3(64 * SW), 0, s, T, a, col, dist, ent);
+  prof_end(s);
+  return hipGetLastError();
+}
+
+hipError_t launch_compact_marginals(int H, int T, const float* alpha, const float* rho, float* logz,
+                                    float* col_p, float* dist_p, hipStream_t s) {
+  prof_begin("fit_logz", s);
+  hipLaunchKernelGGL(logz_kernel, dim3((T + FW - 1) / FW, H), dim3(64 * FW), 0, s, T, alpha, rho, logz);
+  prof_end(s);
+  prof_begin("fit_marginals", s);
+  hipLaunchKernelGGL(marg_kernel<false>, dim3((2 * T + FW - 1) / FW, H), dim3(64 * FW), 0, s, T, alpha,
+                     rho, (const float*)logz, col_p, dist_p, (const float*)nullptr, (const float*)nullptr,
+                     (float*)nullptr, (float*)nullptr, AdamStep{});
+  prof_end(s);
+  return hipGetLastError();
+}
+
+size_t fit_workspace_floats(int H, int T) { return 7 * pad64((size_t)H * T); }
+
+hipError_t launch_compact_fit(const FitArgs& f, const float* col, const float* dist, const float* ent,
+                              float* alpha, float* rho, float* kl, float* ws, hipStream_t s) {
+  const int H = f.H, T = f.T;
+  const size_t n = pad64((size_t)H * T);
+  float* logz = ws;
+  float* alt_alpha = ws + n;
+  float* alt_rho = ws + 2 * n;
+  float* m = ws + 3 * n;       // [H, 2T]
+  float* v = ws + 5 * n;       // [H, 2T]
+  hipLaunchKernelGGL(fill_kernel, dim3(elementwise_blocks(4 * n)), dim3(256), 0, s, m, 4 * n, 0.f);
+  float* cur[2] = {alpha, rho};
+  float* nxt[2] = {alt_alpha, alt_rho};
+  const dim3 lz_grid((T + FW - 1) / FW, H), mg_grid((2 * T + FW - 1) / FW, H), blk(64 * FW);
+  double p1 = 1.0, p2 = 1.0;
+  for (int t = 1; t <= f.steps; ++t) {
+    p1 *= f.beta1;
+    p2 *= f.beta2;
+    const AdamStep st{f.lr, f.beta1, f.beta2, f.eps, (float)(1.0 - p1), (float)(1.0 - p2), 1.f / T};
+    prof_begin("fit_logz", s);
+    hipLaunchKernelGGL(logz_kernel, lz_grid, blk, 0, s, T, (const float*)cur[0], (const float*)cur[1], logz);
+    prof_end(s);
+    prof_begin("fit_adam", s);
+    hipLaunchKernelGGL(marg_kernel<true>, mg_grid, blk, 0, s, T, (const float*)cur[0], (const float*)cur[1],
+                       (const float*)logz, nxt[0], nxt[1], col, dist, m, v, st);
+    prof_end(s);
+    std::swap(cur[0], nxt[0]);
+    std::swap(cur[1], nxt[1]);
+  }
+  if (cur[0] != alpha) {
+    hipLaunchKernelGGL(copy_kernel, dim3(elementwise_blocks((size_t)H * T)), dim3(256), 0, s, alpha,
+                       (const float*)cur[0], (size_t)H * T);
+    hipLaunchKernelGGL(copy_kernel, dim3(elementwise_blocks((size_t)H * T)), dim3(256), 0, s, rho,
+                       (const float*)cur[1], (size_t)H * T);
+  }
+  hipLaunchKernelGGL(logz_kernel, lz_grid, blk, 0, s, T, (const float*)alpha, (const float*)rho, logz);
+  hipLaunchKernelGGL(kl_kernel, dim3(H), dim3(256), 0, s, T, (const float*)alpha, (const float*)rho,
+                     (const float*)logz, col, dist, ent, kl);
+  return hipGetLastError();
+}
+
+}  // namespace saf

@@ -255,6 +255,95 @@ int32_t saf_select_heads(const double* s_var_all, int32_t n_heads, double r, int
   return kk;
 }
 
+static saf_status validate_fit_shape(int32_t H, int32_t T) {
+  if (H < 1 || T < 1) return fail(SAF_EINVAL, "H and T must be >= 1 (got %d, %d)", H, T);
+  if (H > 65535) return fail(SAF_EUNSUPPORTED, "H must be <= 65535 (got %d)", H);
+  if ((int64_t)H * T > (int64_t)1 << 31) return fail(SAF_EUNSUPPORTED, "H*T must be <= 2^31");
+  return SAF_OK;
+}
+
+saf_status saf_pattern_stats(int32_t H, int32_t T, const float* a, float* col, float* dist, float* ent,
+                             void* stream) {
+  SAF_TRY(validate_fit_shape(H, T));
+  SAF_TRY(check_ptr(a, true, "a"));
+  SAF_TRY(check_ptr(col, true, "col"));
+  SAF_TRY(check_ptr(dist, true, "dist"));
+  SAF_TRY(check_ptr(ent, true, "ent"));
+  (void)hipGetLastError();
+  hipError_t e = saf::launch_pattern_stats(H, T, a, col, dist, ent, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "pattern statistics launch");
+  return SAF_OK;
+}
+
+saf_status saf_compact_marginals(int32_t H, int32_t T, const float* alpha, const float* rho, float* logz,
+                                 float* col, float* dist, void* stream) {
+  SAF_TRY(validate_fit_shape(H, T));
+  SAF_TRY(check_ptr(alpha, true, "alpha"));
+  SAF_TRY(check_ptr(rho, true, "rho"));
+  SAF_TRY(check_ptr(logz, true, "logz"));
+  SAF_TRY(check_ptr(col, true, "col"));
+  SAF_TRY(check_ptr(dist, true, "dist"));
+  (void)hipGetLastError();
+  hipError_t e = saf::launch_compact_marginals(H, T, alpha, rho, logz, col, dist, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "compact marginals launch");
+  return SAF_OK;
+}
+
+static saf_status validate_fit(const saf_fit_desc* d, saf::FitArgs* f) {
+  if (!d) return fail(SAF_EINVAL, "desc is NULL");
+  SAF_TRY(validate_fit_shape(d->H, d->T));
+  if (d->steps < 0) return fail(SAF_EINVAL, "steps must be >= 0 (got %d)", d->steps);
+  if (!(d->lr > 0.f) || !std::isfinite(d->lr)) return fail(SAF_EINVAL, "lr must be finite and > 0");
+  if (!(d->beta1 >= 0.f && d->beta1 < 1.f) || !(d->beta2 >= 0.f && d->beta2 < 1.f))
+    return fail(SAF_EINVAL, "beta1 and beta2 must lie in [0, 1)");
+  if (!(d->eps >= 0.f) || !std::isfinite(d->eps)) return fail(SAF_EINVAL, "eps must be finite and >= 0");
+  *f = saf::FitArgs{d->H, d->T, d->steps, d->lr, d->beta1, d->beta2, d->eps};
+  return SAF_OK;
+}
+
+size_t saf_fit_workspace_size(const saf_fit_desc* desc) {
+  saf::FitArgs f;
+  if (validate_fit(desc, &f) != SAF_OK) return 0;
+  return saf::fit_workspace_floats(f.H, f.T) * sizeof(float);
+}
+
+saf_status saf_compact_fit(const saf_fit_desc* desc, const float* col, const float* dist, const float* ent,
+                           float* alpha, float* rho, float* kl, void* workspace, size_t ws_bytes,
+                           void* stream) {
+  saf::FitArgs f;
+  SAF_TRY(validate_fit(desc, &f));
+  SAF_TRY(check_ptr(col, true, "col"));
+  SAF_TRY(check_ptr(dist, true, "dist"));
+  SAF_TRY(check_ptr(ent, true, "ent"));
+  SAF_TRY(check_ptr(alpha, true, "alpha"));
+  SAF_TRY(check_ptr(rho, true, "rho"));
+  SAF_TRY(check_ptr(kl, true, "kl"));
+  SAF_TRY(check_ptr(workspace, true, "workspace"));
+  const size_t need = saf::fit_workspace_floats(f.H, f.T) * sizeof(float);
+  if (ws_bytes < need) return fail(SAF_EWORKSPACE, "workspace has %zu bytes, needs %zu", ws_bytes, need);
+  (void)hipGetLastError();
+  hipError_t e = saf::launch_compact_fit(f, col, dist, ent, alpha, rho, kl, static_cast<float*>(workspace),
+                                         static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "compact fit launch");
+  return SAF_OK;
+}
+
+int32_t saf_select_fitted(const double* s_var_all, const float* kl_all, int32_t n_heads, double r,
+                          float max_kl, int32_t* out) {
+  if (!s_var_all || !kl_all || !out || n_heads < 1 || !(r >= 0.0 && r <= 1.0) || std::isnan(max_kl)) {
+    fail(SAF_EINVAL, "saf_select_fitted: bad arguments");
+    return -1;
+  }
+  std::vector<int32_t> idx(n_heads);
+  std::iota(idx.begin(), idx.end(), 0);
+  std::stable_sort(idx.begin(), idx.end(), [&](int32_t x, int32_t y) { return s_var_all[x] < s_var_all[y]; });
+  const int32_t kk = (int32_t)std::floor(r * n_heads + 0.5);
+  int32_t kept = 0;
+  for (int32_t x = 0; x < n_heads && kept < kk; ++x)
+    if (kl_all[idx[x]] <= max_kl) out[kept++] = idx[x];
+  return kept;
+}
+
 const char* saf_status_string(saf_status st) {
   switch (st) {
     case SAF_OK: return "SAF_OK";

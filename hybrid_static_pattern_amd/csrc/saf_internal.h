@@ -64,4 +64,19 @@ size_t var_workspace_bytes(const VarArgs& a);
 hipError_t launch_var_score(const VarArgs& a, const void* q, const void* k, float* a_hat,
                             double* s_var, int32_t* rank, void* ws, hipStream_t s);
 
+// Compact pattern fit.
+struct FitArgs {
+  int H, T, steps;
+  float lr, beta1, beta2, eps;
+};
+hipError_t launch_pattern_stats(int H, int T, const float* a, float* col, float* dist, float* ent,
+                                hipStream_t s);
+hipError_t launch_compact_marginals(int H, int T, const float* alpha, const float* rho, float* logz,
+                                    float* col_p, float* dist_p, hipStream_t s);
+// Workspace of the fit: log Z, the other alpha and rho buffers, and Adam's m and v for both
+// ([H, 2T] each), every array padded to a multiple of 64 floats.
+size_t fit_workspace_floats(int H, int T);
+hipError_t launch_compact_fit(const FitArgs& f, const float* col, const float* dist, const float* ent,
+                              float* alpha, float* rho, float* kl, float* ws, hipStream_t s);
+
 }  // namespace saf

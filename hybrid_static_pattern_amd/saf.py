@@ -23,7 +23,8 @@ SAF_FP32, SAF_BF16 = 0, 1
 EXPORTS = (
     "saf_attn_fwd", "saf_attn_workspace_size", "saf_attn_bwd", "saf_var_workspace_size",
     "saf_var_score", "saf_select_heads", "saf_status_string", "saf_last_error",
-    "saf_prof_enable", "saf_prof_read",
+    "saf_prof_enable", "saf_prof_read", "saf_pattern_stats", "saf_compact_marginals",
+    "saf_fit_workspace_size", "saf_compact_fit", "saf_select_fitted",
 )
 
 
@@ -47,6 +48,17 @@ class VarDesc(ctypes.Structure):
         ("io_dtype", ctypes.c_int), ("scale", ctypes.c_float),
     ]
 
+
+class FitDesc(ctypes.Structure):
+    _fields_ = [
+        ("H", ctypes.c_int32), ("T", ctypes.c_int32), ("steps", ctypes.c_int32),
+        ("lr", ctypes.c_float), ("beta1", ctypes.c_float), ("beta2", ctypes.c_float), ("eps", ctypes.c_float),
+    ]
+
+
+# Fit settings: 400 Adam steps (the page); lr, betas and eps are a reading (the page names
+# only the optimiser); acceptance at a mean row KL of 0.2 nat (the page).
+FIT_STEPS, FIT_LR, FIT_BETA1, FIT_BETA2, FIT_EPS, FIT_MAX_KL = 400, 0.1, 0.9, 0.999, 1e-8, 0.2
 
 _lib = None
 
@@ -76,7 +88,17 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.saf_prof_enable.argtypes = [ctypes.c_int]
     lib.saf_prof_read.argtypes = [ctypes.POINTER(ctypes.c_char_p), ctypes.POINTER(ctypes.c_float), i32]
     lib.saf_prof_read.restype = i32
-    for fn in ("saf_attn_fwd", "saf_attn_bwd", "saf_var_score", "saf_prof_enable"):
+    pf = ctypes.POINTER(FitDesc)
+    lib.saf_pattern_stats.argtypes = [i32, i32, vp, vp, vp, vp, vp]
+    lib.saf_compact_marginals.argtypes = [i32, i32, vp, vp, vp, vp, vp, vp]
+    lib.saf_fit_workspace_size.argtypes = [pf]
+    lib.saf_fit_workspace_size.restype = sz
+    lib.saf_compact_fit.argtypes = [pf, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+    lib.saf_select_fitted.argtypes = [ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_float), i32,
+                                      ctypes.c_double, ctypes.c_float, ctypes.POINTER(i32)]
+    lib.saf_select_fitted.restype = i32
+    for fn in ("saf_attn_fwd", "saf_attn_bwd", "saf_var_score", "saf_prof_enable", "saf_pattern_stats",
+               "saf_compact_marginals", "saf_compact_fit"):
         getattr(lib, fn).restype = ctypes.c_int
     _lib = lib
     return lib
@@ -239,6 +261,97 @@ def select_heads(s_var_all, r: float) -> np.ndarray:
     out = np.zeros(s.size, dtype=np.int32)
     kk = load().saf_select_heads(s.ctypes.data_as(ctypes.POINTER(ctypes.c_double)), s.size, float(r),
                                  out.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)))
+    if kk < 0:
+        _check(SAF_EINVAL)
+    return out[:kk].copy()
+
+
+def pattern_stats(a, col=None, dist=None, ent=None):
+    """Eq. (4) statistics of targets a [H,T,T] float32 (saf_pattern_stats). Returns
+    (col, dist, ent), each [H,T] float32 on a's device."""
+    lib = load()
+    _need(a, "a", dtype=torch.float32)
+    if a.dim() != 3 or a.shape[1] != a.shape[2]:
+        raise ValueError(f"a must be [H, T, T], got {tuple(a.shape)}")
+    H, T = a.shape[0], a.shape[1]
+    outs = []
+    for name, t in (("col", col), ("dist", dist), ("ent", ent)):
+        _need(t, name, shape=(H, T), dtype=torch.float32, device=a.device)
+        outs.append(t if t is not None else torch.empty((H, T), dtype=torch.float32, device=a.device))
+    _check(lib.saf_pattern_stats(H, T, _ptr(a), *(_ptr(t) for t in outs), _stream(a)))
+    return tuple(outs)
+
+
+def compact_marginals(alpha, rho, logz=None, col=None, dist=None):
+    """log Z and the two marginals of the compact pattern (saf_compact_marginals). alpha, rho:
+    [H,T] float32. Returns (logz, col, dist), each [H,T] float32."""
+    lib = load()
+    _need(alpha, "alpha", dtype=torch.float32)
+    if alpha.dim() != 2:
+        raise ValueError(f"alpha must be [H, T], got {tuple(alpha.shape)}")
+    H, T = alpha.shape
+    _need(rho, "rho", shape=(H, T), dtype=torch.float32, device=alpha.device)
+    outs = []
+    for name, t in (("logz", logz), ("col", col), ("dist", dist)):
+        _need(t, name, shape=(H, T), dtype=torch.float32, device=alpha.device)
+        outs.append(t if t is not None else torch.empty((H, T), dtype=torch.float32, device=alpha.device))
+    _check(lib.saf_compact_marginals(H, T, _ptr(alpha), _ptr(rho), *(_ptr(t) for t in outs), _stream(alpha)))
+    return tuple(outs)
+
+
+def _fit_desc(H, T, steps, lr, beta1, beta2, eps):
+    return FitDesc(H, T, int(steps), float(lr), float(beta1), float(beta2), float(eps))
+
+
+def fit_workspace_size(H, T, steps=FIT_STEPS, lr=FIT_LR, beta1=FIT_BETA1, beta2=FIT_BETA2, eps=FIT_EPS) -> int:
+    d = _fit_desc(H, T, steps, lr, beta1, beta2, eps)
+    return int(load().saf_fit_workspace_size(ctypes.byref(d)))
+
+
+def compact_fit(col, dist, ent, alpha=None, rho=None, kl=None, steps=FIT_STEPS, lr=FIT_LR,
+                beta1=FIT_BETA1, beta2=FIT_BETA2, eps=FIT_EPS, workspace=None):
+    """Fits alpha, rho [H,T] to targets with statistics (col, dist, ent) (saf_compact_fit).
+    alpha, rho: the starting point, updated in place (zeros, the uniform pattern, when None).
+    Returns (alpha, rho, kl [H] float32: mean row KL of each fitted pattern)."""
+    lib = load()
+    _need(col, "col", dtype=torch.float32)
+    if col.dim() != 2:
+        raise ValueError(f"col must be [H, T], got {tuple(col.shape)}")
+    H, T = col.shape
+    dev = col.device
+    for name, t in (("dist", dist), ("ent", ent), ("alpha", alpha), ("rho", rho)):
+        _need(t, name, shape=(H, T), dtype=torch.float32, device=dev)
+    _need(kl, "kl", shape=(H,), dtype=torch.float32, device=dev)
+    if dist is None or ent is None:
+        raise ValueError("dist and ent are required")
+    d = _fit_desc(H, T, steps, lr, beta1, beta2, eps)
+    need = int(lib.saf_fit_workspace_size(ctypes.byref(d)))
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+    _need(workspace, "workspace", device=dev)
+    if alpha is None:
+        alpha = torch.zeros((H, T), dtype=torch.float32, device=dev)
+    if rho is None:
+        rho = torch.zeros((H, T), dtype=torch.float32, device=dev)
+    if kl is None:
+        kl = torch.empty((H,), dtype=torch.float32, device=dev)
+    _check(lib.saf_compact_fit(ctypes.byref(d), _ptr(col), _ptr(dist), _ptr(ent), _ptr(alpha), _ptr(rho),
+                               _ptr(kl), _ptr(workspace), workspace.numel() * workspace.element_size(),
+                               _stream(col)))
+    return alpha, rho, kl
+
+
+def select_fitted(s_var_all, kl_all, r: float, max_kl: float = FIT_MAX_KL) -> np.ndarray:
+    """Walks all heads by ascending s_var and keeps those whose fit passes (mean row KL <=
+    max_kl) until round(r * n) are kept (host only). Returns the kept indices in walk order."""
+    s = np.ascontiguousarray(np.asarray(s_var_all, dtype=np.float64).reshape(-1))
+    kl = np.ascontiguousarray(np.asarray(kl_all, dtype=np.float32).reshape(-1))
+    if kl.size != s.size:
+        raise ValueError("s_var_all and kl_all differ in length")
+    out = np.zeros(s.size, dtype=np.int32)
+    kk = load().saf_select_fitted(s.ctypes.data_as(ctypes.POINTER(ctypes.c_double)),
+                                  kl.ctypes.data_as(ctypes.POINTER(ctypes.c_float)), s.size, float(r),
+                                  float(max_kl), out.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)))
     if kk < 0:
         _check(SAF_EINVAL)
     return out[:kk].copy()

@@ -123,6 +123,61 @@ saf_status saf_var_score(const saf_var_desc* desc, const void* q, const void* k,
  * indices to out[0..k-1] (out holds n_heads entries). Returns k, or -1 on bad arguments. */
 int32_t saf_select_heads(const double* s_var_all, int32_t n_heads, double r, int32_t* out);
 
+/* ---- Compact static pattern fit (part 二.3, Eq. (3), Eq. (4), Appendix A.2) ----
+ * A candidate head's target pattern A [T, T] (its mean attention, e.g. a_hat of
+ * saf_var_score: causal, rows summing to 1) is replaced by
+ *   P(i,j) = exp(alpha(j) + rho(i-j)) / Z(i) for j <= i,
+ * with alpha, rho fitted by minimising the mean over rows of the cross-entropy
+ * -sum_j A(i,j) log P(i,j). That objective depends on A only through two marginals
+ * (Eq. (4)); the fit runs Adam on them and reports the mean row KL(A_i || P_i), which the
+ * page accepts at <= 0.2 nat. alpha, rho, the marginals and log Z are [H, T] float32,
+ * contiguous, one row per fitted pattern. */
+
+/* Eq. (4) statistics of H targets a [H, T, T] float32 (entries above the diagonal are not
+ * read): col[h, j] = sum_{i>=j} a(i, j), dist[h, d] = sum_{i>=d} a(i, i-d), and
+ * ent[h, j] = -sum_{i>=j} a(i,j) log a(i,j) (0 log 0 = 0), whose sum over j divided by T is
+ * the mean row entropy. H, T >= 1. No workspace. */
+saf_status saf_pattern_stats(int32_t H, int32_t T, const float* a, float* col, float* dist,
+                             float* ent, void* stream);
+
+/* The same marginals of the compact pattern itself, and its normaliser:
+ * logz[h, i] = log Z(i); col[h, j] = sum_{i>=j} P(i, j); dist[h, d] = sum_{i>=d} P(i, i-d).
+ * alpha, rho follow the value rules of saf_attn_fwd (finite, or -inf with a finite logit
+ * left in every row). No workspace. */
+saf_status saf_compact_marginals(int32_t H, int32_t T, const float* alpha, const float* rho,
+                                 float* logz, float* col, float* dist, void* stream);
+
+/* One fit of H patterns of length T: `steps` Adam steps (the page uses 400) with learning
+ * rate lr, moment decays beta1 and beta2 and denominator offset eps (a reading, since the
+ * page names only the optimiser: 0.1, 0.9, 0.999, 1e-8). lr > 0, 0 <= beta < 1, eps >= 0,
+ * steps >= 0, H in [1, 65535], T >= 1, H * T <= 2^31. */
+typedef struct {
+  int32_t H, T;
+  int32_t steps;
+  float lr, beta1, beta2, eps;
+} saf_fit_desc;
+
+/* Workspace bytes saf_compact_fit needs (0 on a NULL or invalid descriptor). */
+size_t saf_fit_workspace_size(const saf_fit_desc* desc);
+
+/* Fits alpha, rho [H, T] (in: the starting point, e.g. zeros, the uniform causal pattern;
+ * out: the fitted tables) to the targets whose saf_pattern_stats are col, dist, ent, by
+ * bias-corrected Adam on the mean row cross-entropy, whose gradient is
+ * (colP - col) / T for alpha and (distP - dist) / T for rho. Writes kl[h], the mean row
+ * KL of the fitted pattern (float32, [H]). workspace as for saf_attn_bwd. */
+saf_status saf_compact_fit(const saf_fit_desc* desc, const float* col, const float* dist,
+                           const float* ent, float* alpha, float* rho, float* kl,
+                           void* workspace, size_t ws_bytes, void* stream);
+
+/* Host-only selection with the fit's acceptance test (part 二.1 and Appendix A.2): walks the
+ * n_heads heads (all L*H of a model) by ascending s_var, ties to the lower index, keeps a
+ * head when kl_all[head] <= max_kl and skips it otherwise, and stops once
+ * k = floor(r*n + 1/2) heads are kept. Writes the kept indices, in walk order, to out
+ * (n_heads entries) and returns their number (less than k when too few fits pass), or -1 on
+ * bad arguments. */
+int32_t saf_select_fitted(const double* s_var_all, const float* kl_all, int32_t n_heads,
+                          double r, float max_kl, int32_t* out);
+
 const char* saf_status_string(saf_status status);
 const char* saf_last_error(void);
 

@@ -102,3 +102,35 @@ def test_select_heads_matches_oracle(lib):
     for frac in (0.0, 0.1, 0.25, 0.5, 1.0):
         assert list(saf.select_heads(s, frac)) == list(saf_oracle.select_heads(s, frac))
     assert len(saf.select_heads(s, 0.25)) == 36
+
+
+def test_fit_contract(lib):
+    assert lib.saf_pattern_stats(0, 16, FAKE, FAKE, FAKE, FAKE, None) == saf.SAF_EINVAL
+    assert lib.saf_pattern_stats(2, 16, None, FAKE, FAKE, FAKE, None) == saf.SAF_EINVAL
+    assert lib.saf_compact_marginals(70000, 16, FAKE, FAKE, FAKE, FAKE, FAKE, None) == saf.SAF_EUNSUPPORTED
+    assert lib.saf_compact_marginals(2, 16, FAKE, ctypes.c_void_p(0x10008), FAKE, FAKE, FAKE, None) == saf.SAF_EINVAL
+    good = saf.FitDesc(3, 100, 400, 0.1, 0.9, 0.999, 1e-8)
+    need = lib.saf_fit_workspace_size(ctypes.byref(good))
+    assert need >= 7 * 3 * 100 * 4 and need % 256 == 0
+    assert lib.saf_compact_fit(ctypes.byref(good), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, need - 1,
+                               None) == saf.SAF_EWORKSPACE
+    for bad in (saf.FitDesc(3, 100, -1, 0.1, 0.9, 0.999, 1e-8), saf.FitDesc(3, 100, 400, 0.0, 0.9, 0.999, 1e-8),
+                saf.FitDesc(3, 100, 400, 0.1, 1.0, 0.999, 1e-8), saf.FitDesc(3, 100, 400, 0.1, 0.9, 0.999, -1.0),
+                saf.FitDesc(3, 0, 400, 0.1, 0.9, 0.999, 1e-8)):
+        assert lib.saf_fit_workspace_size(ctypes.byref(bad)) == 0
+        assert lib.saf_compact_fit(ctypes.byref(bad), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 1 << 30,
+                                   None) == saf.SAF_EINVAL
+    assert lib.saf_compact_fit(ctypes.byref(good), FAKE, FAKE, None, FAKE, FAKE, FAKE, FAKE, need,
+                               None) == saf.SAF_EINVAL
+
+
+def test_select_fitted_matches_oracle(lib):
+    from oracle import compact_fit
+    r = np.random.default_rng(1)
+    s = r.random(144)
+    s[3] = s[77]  # a tie: lower index first
+    kl = r.random(144).astype(np.float32) * 0.4
+    for frac in (0.0, 0.1, 0.25, 0.5, 1.0):
+        for thr in (0.2, 0.05, 1.0):
+            assert list(saf.select_fitted(s, kl, frac, thr)) == list(compact_fit.select_fitted(s, kl, frac, thr))
+    assert lib.saf_select_fitted(None, None, 4, 0.5, 0.2, None) == -1
