@@ -85,27 +85,42 @@ def frozen_probs(alpha, rho):
     return P, np.log(Z)
 
 
+def _kv_group(frozen, v):
+    """Head counts of a layer: H query heads (len(frozen)), H_kv key/value heads (v.shape[1]),
+    and the group size G = H / H_kv. H_kv = H is ordinary multi-head attention; H_kv < H is
+    grouped-query attention (part 二.4, the GQA path of section 3.3 / Appendix D.2): query head
+    h reads the keys and values of head h // G, so a frozen head still mixes the current V of
+    its group and drops only its query."""
+    H, H_kv = len(frozen), np.shape(v)[1]
+    if H_kv < 1 or H % H_kv:
+        raise ValueError(f"{H} query heads cannot share {H_kv} key/value heads evenly")
+    return H, H_kv, H // H_kv
+
+
 def attn_fwd(q, k, v, frozen, alpha, rho, scale: float):
-    """Hybrid causal attention forward over [B,H,T,D].
+    """Hybrid causal attention forward. q: [B,H,T,D]; k, v: [B,H_kv,T,D] (H_kv = H, or a
+    divisor of H for grouped-query attention, see _kv_group).
 
     Ordinary heads: O = A V (part 一). Frozen heads (frozen[h] != 0): O = P-hat V with the
-    current V (part 二.4, Fig. 2); their q, k are never used.
+    current V (part 二.4, Fig. 2); their q (and, in MHA, k) are never used.
     Returns O [B,H,T,D] and lse [B,H,T] (log-normaliser of each row, see module notes).
     """
     v = _f64(v)
-    B, H, T, D = v.shape
+    B, _, T, D = v.shape
+    H, _, G = _kv_group(frozen, v)
     O = np.empty((B, H, T, D))
     lse = np.empty((B, H, T))
     for h in range(H):
+        g = h // G
         if frozen[h]:
             P, logZ = frozen_probs(alpha[h, :T], rho[h, :T])
             for b in range(B):
-                O[b, h] = P @ v[b, h]
+                O[b, h] = P @ v[b, g]
                 lse[b, h] = logZ
         else:
             for b in range(B):
-                A, l = dynamic_probs(q[b, h], k[b, h], scale)
-                O[b, h] = A @ v[b, h]
+                A, l = dynamic_probs(q[b, h], k[b, g], scale)
+                O[b, h] = A @ v[b, g]
                 lse[b, h] = l
     return O, lse
 
@@ -117,28 +132,36 @@ def attn_bwd(q, k, v, do, frozen, alpha, rho, scale: float):
         dV = A^T dO;  dA = dO V^T;  dS_ij = A_ij (dA_ij - sum_k A_ik dA_ik);
         dQ = scale * dS K;  dK = scale * dS^T Q.
     Frozen heads (part 二.4): dV = P-hat^T dO only; alpha and rho are fixed buffers, and
-    no query or key exists, so dQ and dK of a frozen head are NaN here (never produced).
-    Returns dQ, dK, dV [B,H,T,D].
+    no query or key exists, so dQ of a frozen head is NaN here (never produced).
+    With shared key/value heads (grouped-query attention) the gradient of a shared K or V is
+    the sum over the query heads that read it: dK of head g sums the ordinary heads of its
+    group (NaN, never produced, when the group has none) and dV of head g sums all of them.
+    Returns dQ [B,H,T,D], dK, dV [B,H_kv,T,D].
     """
     v, do = _f64(v), _f64(do)
-    B, H, T, D = v.shape
+    B, H_kv, T, D = v.shape
+    H, _, G = _kv_group(frozen, v)
     dq = np.full((B, H, T, D), np.nan)
-    dk = np.full((B, H, T, D), np.nan)
-    dv = np.empty((B, H, T, D))
+    dk = np.zeros((B, H_kv, T, D))
+    dv = np.zeros((B, H_kv, T, D))
     for h in range(H):
+        g = h // G
         if frozen[h]:
             P, _ = frozen_probs(alpha[h, :T], rho[h, :T])
             for b in range(B):
-                dv[b, h] = P.T @ do[b, h]
+                dv[b, g] += P.T @ do[b, h]
             continue
         for b in range(B):
-            qb, kb = _f64(q[b, h]), _f64(k[b, h])
+            qb, kb = _f64(q[b, h]), _f64(k[b, g])
             A, _ = dynamic_probs(qb, kb, scale)
-            dv[b, h] = A.T @ do[b, h]
-            dA = do[b, h] @ v[b, h].T
+            dv[b, g] += A.T @ do[b, h]
+            dA = do[b, h] @ v[b, g].T
             dS = A * (dA - (A * dA).sum(axis=1, keepdims=True))
             dq[b, h] = scale * (dS @ kb)
-            dk[b, h] = scale * (dS.T @ qb)
+            dk[b, g] += scale * (dS.T @ qb)
+    for g in range(H_kv):
+        if all(frozen[h] for h in range(g * G, (g + 1) * G)):
+            dk[:, g] = np.nan   # no query head reads this K: no gradient is produced
     return dq, dk, dv
 
 

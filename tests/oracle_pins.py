@@ -215,6 +215,62 @@ def pin_gradients_finite_difference(orc):
     assert np.max(np.abs(num_q[:, 1])) == 0.0
 
 
+def pin_gqa_equals_repeated_heads(orc):
+    """Grouped-query attention (shared K/V, part 二.4) is ordinary attention on K and V
+    repeated for each query head of a group; the shared K and V receive the sum of the
+    repeated copies' gradients (dK only from ordinary heads, NaN for a group of frozen heads
+    only)."""
+    B, T, D = 2, 9, 4
+    scale = 0.5
+    r = _rng(21)
+    for H, H_kv, frozen in ((4, 2, [0, 1, 1, 1]), (6, 2, [1, 0, 0, 1, 0, 1]), (3, 1, [0, 1, 0])):
+        G = H // H_kv
+        frozen = np.array(frozen, np.uint8)
+        q, do = r.standard_normal((B, H, T, D)), r.standard_normal((B, H, T, D))
+        k, v = r.standard_normal((B, H_kv, T, D)), r.standard_normal((B, H_kv, T, D))
+        alpha, rho = r.standard_normal((H, T)), r.standard_normal((H, T))
+        kr, vr = np.repeat(k, G, axis=1), np.repeat(v, G, axis=1)
+        O, lse = orc.attn_fwd(q, k, v, frozen, alpha, rho, scale)
+        O_r, lse_r = orc.attn_fwd(q, kr, vr, frozen, alpha, rho, scale)
+        assert np.max(np.abs(O - O_r)) < 1e-13 and np.max(np.abs(lse - lse_r)) < 1e-13
+        dq, dk, dv = orc.attn_bwd(q, k, v, do, frozen, alpha, rho, scale)
+        dq_r, dk_r, dv_r = orc.attn_bwd(q, kr, vr, do, frozen, alpha, rho, scale)
+        assert np.array_equal(np.isnan(dq), np.isnan(dq_r))
+        assert np.nanmax(np.abs(dq - dq_r)) < 1e-13
+        for g in range(H_kv):
+            heads = range(g * G, (g + 1) * G)
+            want_v = sum(dv_r[:, h] for h in heads)
+            assert np.max(np.abs(dv[:, g] - want_v)) < 1e-12
+            ordinary = [h for h in heads if not frozen[h]]
+            if ordinary:
+                want_k = sum(dk_r[:, h] for h in ordinary)
+                assert np.max(np.abs(dk[:, g] - want_k)) < 1e-12
+            else:
+                assert np.all(np.isnan(dk[:, g]))
+
+
+def pin_gqa_gradients_finite_difference(orc):
+    """dK and dV of shared key/value heads against central differences of <dO, O>
+    (H = 4 query heads over 2 shared heads, one frozen head in each group)."""
+    B, H, H_kv, T, D = 1, 4, 2, 6, 3
+    scale = 0.7
+    r = _rng(22)
+    q, do = r.standard_normal((B, H, T, D)), r.standard_normal((B, H, T, D))
+    k, v = r.standard_normal((B, H_kv, T, D)), r.standard_normal((B, H_kv, T, D))
+    alpha, rho = r.standard_normal((H, T)), r.standard_normal((H, T))
+    frozen = np.array([0, 1, 1, 0], np.uint8)
+
+    def loss():
+        return float((orc.attn_fwd(q, k, v, frozen, alpha, rho, scale)[0] * do).sum())
+
+    dq, dk, dv = orc.attn_bwd(q, k, v, do, frozen, alpha, rho, scale)
+    for name, x, g in (("dk", k, dk), ("dv", v, dv), ("dq", q, dq)):
+        num = _fd_grad(loss, x)
+        sel = (slice(None), [0, 3]) if name == "dq" else (slice(None),)
+        err = np.max(np.abs(g[sel] - num[sel])) / np.max(np.abs(num[sel]))
+        assert err < 1e-7, (name, err)
+
+
 # ---------------------------------------------------------------- calibration, Eq. (1)
 
 def pin_var_identical_inputs(orc):

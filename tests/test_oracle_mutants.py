@@ -87,6 +87,53 @@ def _bwd_factory(kind):
     return attn_bwd
 
 
+def _gqa_factory(kind):
+    def attn_bwd(q, k, v, do, frozen, alpha, rho, scale):
+        v, do = np.asarray(v, float), np.asarray(do, float)
+        B, H_kv, T, D = v.shape
+        H = len(frozen)
+        G = H // H_kv
+        dq = np.full((B, H, T, D), np.nan); dk = np.zeros(v.shape); dv = np.zeros(v.shape)
+        for h in range(H):
+            g = h % H_kv if kind == "interleaved" else h // G
+            for b in range(B):
+                if frozen[h]:
+                    if kind != "frozen_dv_dropped":
+                        P, _ = so.frozen_probs(alpha[h, :T], rho[h, :T])
+                        dv[b, g] += P.T @ do[b, h]
+                    continue
+                qb, kb = np.asarray(q[b, h], float), np.asarray(k[b, g], float)
+                A, _ = so.dynamic_probs(qb, kb, scale)
+                dv[b, g] += A.T @ do[b, h]
+                dA = do[b, h] @ v[b, g].T
+                dS = A * (dA - (A * dA).sum(1, keepdims=True))
+                dq[b, h] = scale * (dS @ kb)
+                contrib = scale * (dS.T @ qb)
+                dk[b, g] = contrib if kind == "dk_overwritten" else dk[b, g] + contrib
+        for g in range(H_kv):
+            if all(frozen[h] for h in range(g * G, (g + 1) * G)):
+                dk[:, g] = np.nan
+        return dq, dk, dv
+    return attn_bwd
+
+
+def _gqa_fwd_interleaved(q, k, v, frozen, alpha, rho, scale):
+    v = np.asarray(v, float)
+    B, H_kv, T, D = v.shape
+    H = len(frozen)
+    O = np.empty((B, H, T, D)); lse = np.empty((B, H, T))
+    for h in range(H):
+        g = h % H_kv
+        for b in range(B):
+            if frozen[h]:
+                P, lz = so.frozen_probs(alpha[h, :T], rho[h, :T])
+            else:
+                P, lz = so.dynamic_probs(q[b, h], k[b, g], scale)
+            O[b, h] = P @ v[b, g]
+            lse[b, h] = lz
+    return O, lse
+
+
 def _var_div_n(A_stack):
     A_stack = np.asarray(A_stack, float)
     N, T, _ = A_stack.shape
@@ -117,6 +164,10 @@ MUTANTS = {
     "bwd: dK operand not transposed": ("attn_bwd", _bwd_factory("dk_untransposed")),
     "bwd: dQ scale dropped": ("attn_bwd", _bwd_factory("dq_no_scale")),
     "bwd: frozen dV with P instead of P^T": ("attn_bwd", _bwd_factory("frozen_no_T")),
+    "gqa fwd: query head h reads shared head h mod H_kv": ("attn_fwd", _gqa_fwd_interleaved),
+    "gqa bwd: query head h reads shared head h mod H_kv": ("attn_bwd", _gqa_factory("interleaved")),
+    "gqa bwd: frozen heads left out of the shared dV": ("attn_bwd", _gqa_factory("frozen_dv_dropped")),
+    "gqa bwd: shared dK overwritten, not summed": ("attn_bwd", _gqa_factory("dk_overwritten")),
     "var: divides by N": ("variance_score", _var_div_n),
     "var: divides by causal pairs": ("variance_score", _var_div_pairs),
     "rank: descending": ("rank_heads", _rank_desc),
