@@ -53,6 +53,7 @@ struct BwdParams {
   float* dk;
   float* dv;
   int tab_stride, B, H, T;
+  int Hkv, G;   // key/value heads; query heads per key/value head
   float c;      // scale * log2(e)
   float scale;
   int n_dyn, n_frz, n_chunks, per_tile, n_tiles;
@@ -355,6 +356,7 @@ __device__ void dkdv_dyn(const BwdParams& p, int b, int h, int kt, unsigned char
   const int n = lane & 15, g = lane >> 4;
   const int T = p.T;
   const size_t head = ((size_t)b * p.H + h) * (size_t)T;
+  const size_t kv_head = ((size_t)b * p.Hkv + h / p.G) * (size_t)T;   // shared K/V of h's group
   const bf16* Q = p.q + head * D;
   const bf16* G = p.dO + head * D;
   const int kbase = kt * BNK, k0w = kbase + KPW * w;
@@ -364,13 +366,13 @@ __device__ void dkdv_dyn(const BwdParams& p, int b, int h, int kt, unsigned char
   for (int kg = 0; kg < NKG; ++kg)
 #pragma unroll
     for (int ks = 0; ks < NKS; ++ks)
-      kf[kg][ks] = *reinterpret_cast<const bf16x8*>(p.k + (head + min(k0w + 16 * kg + n, T - 1)) * D + 32 * ks + 8 * g);
+      kf[kg][ks] = *reinterpret_cast<const bf16x8*>(p.k + (kv_head + min(k0w + 16 * kg + n, T - 1)) * D + 32 * ks + 8 * g);
   // V rows of the key tile into LDS (rows past T re-read row T - 1; their keys are not stored)
 #pragma unroll
   for (int x = 0; x < PERV; ++x) {
     const int pch = (w * PERV + x) * 64 + lane, row = pch / CPR;
     const int c = (pch % CPR) ^ swzv<CPR>(row);
-    g2lds16(p.v + (head + min(kbase + row, T - 1)) * D + c * 8, lds_addr(smem->vs) + (uint32_t)(w * PERV + x) * 1024u);
+    g2lds16(p.v + (kv_head + min(kbase + row, T - 1)) * D + c * 8, lds_addr(smem->vs) + (uint32_t)(w * PERV + x) * 1024u);
   }
   f32x4 dv[NKG][NDB], dk[NKG][NDB];
 #pragma unroll
@@ -548,8 +550,9 @@ __global__ __launch_bounds__(64 * NWD, 2) void dq_kernel(const BwdParams p) {
   const int m = lane & 31, hh = lane >> 5;
   const int T = p.T;
   const size_t head = ((size_t)b * p.H + h) * (size_t)T;
-  const bf16* K = p.k + head * D;
-  const bf16* V = p.v + head * D;
+  const size_t kv_head = ((size_t)b * p.Hkv + h / p.G) * (size_t)T;   // shared K/V of h's group
+  const bf16* K = p.k + kv_head * D;
+  const bf16* V = p.v + kv_head * D;
   const int i0w = qt * BMD + 32 * w, i = i0w + m;
 
   bf16x8 qf[D / 16], gf[D / 16];
@@ -658,6 +661,8 @@ BwdParams make_params(const AttnArgs& a, const void* q, const void* k, const voi
   p.B = a.B;
   p.H = a.H;
   p.T = a.T;
+  p.Hkv = a.Hkv;
+  p.G = a.G;
   p.c = a.scale * kLog2e;
   p.scale = a.scale;
   p.n_dyn = a.heads.n_dyn;

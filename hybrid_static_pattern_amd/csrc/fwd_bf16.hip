@@ -57,6 +57,7 @@ struct FwdParams {
   float* lse;
   int tab_stride;
   int B, H, T;
+  int Hkv, G;  // key/value heads; query heads per key/value head
   float c;  // scale * log2(e)
   int n_dyn, n_frz, n_qt, n_chunks, per_qt;
   uint8_t dyn[kMaxHeads];
@@ -112,9 +113,10 @@ __device__ void dyn_item(const FwdParams& p, int b, int h, int qt, unsigned char
   const int m = lane & 31, hh = lane >> 5;
   const int T = p.T;
   const size_t head = ((size_t)b * p.H + h) * (size_t)T;
+  const size_t kv_head = ((size_t)b * p.Hkv + h / p.G) * (size_t)T;   // shared K/V of h's group
   const bf16* Q = p.q + head * D;
-  const bf16* K = p.k + head * D;
-  const bf16* V = p.v + head * D;
+  const bf16* K = p.k + kv_head * D;
+  const bf16* V = p.v + kv_head * D;
   const int i0w = qt * BM + w * 32;
   const int i = i0w + m;
 
@@ -251,7 +253,7 @@ __device__ void frz_item(const FwdParams& p, int h, int chunk, int qt, unsigned 
     const int pch = (w * PERW + x) * 64 + lane, row = pch / CPR;
     const int col = col0 + ((pch % CPR) ^ swz<CPR>(row)) * 8;
     const int bb = min(col / D, B - 1), d = col % D;
-    src[x] = p.v + (((size_t)bb * H + h) * T) * D + d;
+    src[x] = p.v + (((size_t)bb * p.Hkv + h / p.G) * T) * D + d;   // V of h's key/value head
     srow[x] = row;
   }
   auto load = [&](int J, int u) {
@@ -380,6 +382,8 @@ hipError_t launch_fwd_bf16(const AttnArgs& a, const void* q, const void* k, cons
   p.B = a.B;
   p.H = a.H;
   p.T = a.T;
+  p.Hkv = a.Hkv;
+  p.G = a.G;
   p.c = a.scale * kLog2e;
   p.n_dyn = a.heads.n_dyn;
   p.n_frz = a.heads.n_frz;

@@ -89,8 +89,13 @@ saf_status validate_attn(const saf_attn_desc* d, saf::AttnArgs* a) {
   if (!d->frozen_mask) return fail(SAF_EINVAL, "frozen_mask is NULL");
   if ((int64_t)d->B * d->H * d->T > (int64_t)1 << 31)
     return fail(SAF_EUNSUPPORTED, "B*H*T must be <= 2^31");
+  const int32_t hkv = d->kv_heads == 0 ? d->H : d->kv_heads;
+  if (hkv < 1 || hkv > d->H || d->H % hkv != 0)
+    return fail(SAF_EINVAL, "kv_heads (%d) must be 0 or a divisor of H (%d)", d->kv_heads, d->H);
   a->B = d->B;
   a->H = d->H;
+  a->Hkv = hkv;
+  a->G = d->H / hkv;
   a->T = d->T;
   a->D = d->D;
   a->bf16 = d->io_dtype == SAF_BF16;
@@ -164,7 +169,7 @@ saf_status saf_attn_fwd(const saf_attn_desc* desc, const void* q, const void* k,
 size_t saf_attn_workspace_size(const saf_attn_desc* desc) {
   saf::AttnArgs a;
   if (validate_attn(desc, &a) != SAF_OK) return 0;
-  return 2 * saf::attn_ws_floats(a) * sizeof(float);
+  return (2 * saf::attn_ws_floats(a) + 2 * saf::gqa_ws_floats(a)) * sizeof(float);
 }
 
 saf_status saf_attn_bwd(const saf_attn_desc* desc, const void* q, const void* k, const void* v,
@@ -191,10 +196,19 @@ saf_status saf_attn_bwd(const saf_attn_desc* desc, const void* q, const void* k,
   hipStream_t s = static_cast<hipStream_t>(stream);
   (void)hipGetLastError();
   float* delta = static_cast<float*>(workspace);
+  // shared key/value heads: per-query-head dK, dV into the workspace, then summed per group
+  float* dk_out = static_cast<float*>(dk);
+  float* dv_out = static_cast<float*>(dv);
+  if (a.G > 1) {
+    dk_out = delta + 2 * saf::attn_ws_floats(a);
+    dv_out = dk_out + saf::gqa_ws_floats(a);
+  }
   hipError_t e = a.bf16 ? saf::launch_bwd_bf16(a, q, k, v, o, dO, lse, alpha, rho, static_cast<float*>(dq),
-                                               static_cast<float*>(dk), static_cast<float*>(dv), delta, s)
+                                               dk_out, dv_out, delta, s)
                         : saf::launch_bwd_fp32(a, q, k, v, o, dO, lse, alpha, rho, static_cast<float*>(dq),
-                                               static_cast<float*>(dk), static_cast<float*>(dv), delta, s);
+                                               dk_out, dv_out, delta, s);
+  if (e == hipSuccess && a.G > 1)
+    e = saf::launch_gqa_reduce(a, dk_out, dv_out, static_cast<float*>(dk), static_cast<float*>(dv), s);
   if (e != hipSuccess) return hip_fail(e, "hybrid backward launch");
   return SAF_OK;
 }

@@ -17,6 +17,7 @@ struct HeadLists {
 
 struct AttnArgs {
   int B, H, T, D;
+  int Hkv, G;           // key/value heads and query heads per key/value head (H = G * Hkv)
   bool bf16;            // io dtype
   float scale;
   int tab_stride;
@@ -43,6 +44,14 @@ hipError_t launch_delta(const AttnArgs& a, const void* o, const void* dO, float*
 // Backward workspace: two [B, H, T] float32 arrays (delta, then lse * log2(e)), each padded
 // to a multiple of 64 floats; attn_ws_floats is one array's length.
 inline size_t attn_ws_floats(const AttnArgs& a) { return ((size_t)a.B * a.H * a.T + 63) / 64 * 64; }
+// With shared key/value heads (G > 1) the backward kernels write per-query-head dK and dV
+// into two more [B, H, T, D] float32 arrays of the workspace, which launch_gqa_reduce sums
+// over each group.
+inline size_t gqa_ws_floats(const AttnArgs& a) {
+  return a.G > 1 ? ((size_t)a.B * a.H * a.T * a.D + 63) / 64 * 64 : 0;
+}
+hipError_t launch_gqa_reduce(const AttnArgs& a, const float* dk_heads, const float* dv_heads, float* dk,
+                             float* dv, hipStream_t s);
 
 // Backward. `delta` is the workspace.
 hipError_t launch_bwd_bf16(const AttnArgs& a, const void* q, const void* k, const void* v,

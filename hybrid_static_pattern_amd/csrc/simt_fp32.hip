@@ -30,9 +30,15 @@ struct F32Params {
   float* out2;    // dV (bwd dkdv)
   float* lse;
   int tab_stride, B, H, T;
+  int Hkv, G;                 // key/value heads; query heads per key/value head
   float scale;
   uint8_t frozen[kMaxHeads];  // per head: 1 if frozen
 };
+
+// row offset of the key/value head that query head h of batch entry b reads
+__device__ __forceinline__ size_t kv_rows(const F32Params& p, int bh, int h) {
+  return ((size_t)(bh / p.H) * p.Hkv + h / p.G) * p.T;
+}
 
 template <int D>
 __global__ __launch_bounds__(R) void fwd_fp32_kernel(const F32Params p) {
@@ -41,7 +47,7 @@ __global__ __launch_bounds__(R) void fwd_fp32_kernel(const F32Params p) {
   const int tile = blockIdx.x, bh = blockIdx.y, h = bh % p.H;
   const int t = threadIdx.x, i = tile * R + t, T = p.T;
   const bool frz = p.frozen[h] != 0;
-  const size_t head = (size_t)bh * T;
+  const size_t head = (size_t)bh * T, kvh = kv_rows(p, bh, h);
   float q[D], o[D];
   for (int d = 0; d < D; ++d) o[d] = 0.f;
   float m = kNegInf, l = 0.f;
@@ -54,8 +60,8 @@ __global__ __launch_bounds__(R) void fwd_fp32_kernel(const F32Params p) {
     __syncthreads();
     for (int x = t; x < R * D; x += R) {
       const int r = x / D, d = x % D, j = j0 + r;
-      ks[r][d] = (!frz && j < T) ? p.k[(head + j) * D + d] : 0.f;
-      vs[r][d] = (j < T) ? p.v[(head + j) * D + d] : 0.f;
+      ks[r][d] = (!frz && j < T) ? p.k[(kvh + j) * D + d] : 0.f;
+      vs[r][d] = (j < T) ? p.v[(kvh + j) * D + d] : 0.f;
     }
     __syncthreads();
     if (i >= T) continue;
@@ -99,13 +105,13 @@ __global__ __launch_bounds__(R) void dkdv_fp32_kernel(const F32Params p) {
   const int tile = blockIdx.x, bh = blockIdx.y, h = bh % p.H;
   const int t = threadIdx.x, j = tile * R + t, T = p.T;
   const bool frz = p.frozen[h] != 0;
-  const size_t head = (size_t)bh * T;
+  const size_t head = (size_t)bh * T, kvh = kv_rows(p, bh, h);
   const float* al = p.alpha + (size_t)h * p.tab_stride;
   const float* rh = p.rho + (size_t)h * p.tab_stride;
   float kr[D], vr[D], dk[D], dv[D];
   for (int d = 0; d < D; ++d) {
-    kr[d] = (!frz && j < T) ? p.k[(head + j) * D + d] : 0.f;
-    vr[d] = (!frz && j < T) ? p.v[(head + j) * D + d] : 0.f;
+    kr[d] = (!frz && j < T) ? p.k[(kvh + j) * D + d] : 0.f;
+    vr[d] = (!frz && j < T) ? p.v[(kvh + j) * D + d] : 0.f;
     dk[d] = 0.f;
     dv[d] = 0.f;
   }
@@ -160,7 +166,7 @@ __global__ __launch_bounds__(R) void dq_fp32_kernel(const F32Params p) {
   const int tile = blockIdx.x, bh = blockIdx.y, h = bh % p.H;
   if (p.frozen[h]) return;
   const int t = threadIdx.x, i = tile * R + t, T = p.T;
-  const size_t head = (size_t)bh * T;
+  const size_t head = (size_t)bh * T, kvh = kv_rows(p, bh, h);
   float q[D], g[D], dq[D];
   for (int d = 0; d < D; ++d) {
     q[d] = (i < T) ? p.q[(head + i) * D + d] : 0.f;
@@ -174,8 +180,8 @@ __global__ __launch_bounds__(R) void dq_fp32_kernel(const F32Params p) {
     __syncthreads();
     for (int x = t; x < R * D; x += R) {
       const int r = x / D, d = x % D, j = j0 + r;
-      ks[r][d] = (j < T) ? p.k[(head + j) * D + d] : 0.f;
-      vs[r][d] = (j < T) ? p.v[(head + j) * D + d] : 0.f;
+      ks[r][d] = (j < T) ? p.k[(kvh + j) * D + d] : 0.f;
+      vs[r][d] = (j < T) ? p.v[(kvh + j) * D + d] : 0.f;
     }
     __syncthreads();
     if (i >= T) continue;
@@ -202,6 +208,8 @@ F32Params base_params(const AttnArgs& a) {
   p.B = a.B;
   p.H = a.H;
   p.T = a.T;
+  p.Hkv = a.Hkv;
+  p.G = a.G;
   p.scale = a.scale;
   for (int x = 0; x < kMaxHeads; ++x) p.frozen[x] = 0;
   for (int x = 0; x < a.heads.n_frz; ++x) p.frozen[a.heads.frz[x]] = 1;

@@ -66,18 +66,20 @@ def make_tables(rng: np.random.Generator, H: int, T: int):
 
 
 def make_layer(B: int, H: int, T: int, D: int, dtype: str = BF16, seed: int = 0,
-               n_frozen: int | None = None, frozen_heads=None) -> dict:
+               n_frozen: int | None = None, frozen_heads=None, kv_heads: int | None = None) -> dict:
     """Inputs of one hybrid attention layer.
 
-    Returns a dict with q, k, v, do ([B,H,T,D] float32 holding dtype-exact values),
-    alpha, rho ([H,T] float32), frozen (uint8 [H]), and the shape/dtype fields.
+    Returns a dict with q, do ([B,H,T,D]) and k, v ([B,H_kv,T,D]) float32 arrays holding
+    dtype-exact values, alpha, rho ([H,T] float32), frozen (uint8 [H]), and the shape/dtype
+    fields. H_kv = kv_heads (default H) key/value heads, each shared by H / H_kv query heads.
     Either n_frozen (seeded choice) or frozen_heads (explicit list) selects the frozen set.
     """
     rng = np.random.default_rng(seed)
-    shape = (B, H, T, D)
+    H_kv = H if kv_heads is None else kv_heads
+    shape, kv_shape = (B, H, T, D), (B, H_kv, T, D)
     q = _store(rng.standard_normal(shape, dtype=np.float32), dtype)
-    k = _store(rng.standard_normal(shape, dtype=np.float32), dtype)
-    v = _store(rng.standard_normal(shape, dtype=np.float32), dtype)
+    k = _store(rng.standard_normal(kv_shape, dtype=np.float32), dtype)
+    v = _store(rng.standard_normal(kv_shape, dtype=np.float32), dtype)
     do = _store(rng.standard_normal(shape, dtype=np.float32), dtype)
     alpha, rho = make_tables(rng, H, T)
     if frozen_heads is not None:
@@ -86,7 +88,7 @@ def make_layer(B: int, H: int, T: int, D: int, dtype: str = BF16, seed: int = 0,
     else:
         frozen = choose_frozen(rng, H, int(n_frozen or 0))
     return dict(q=q, k=k, v=v, do=do, alpha=alpha, rho=rho, frozen=frozen,
-                B=B, H=H, T=T, D=D, dtype=dtype, seed=seed)
+                B=B, H=H, H_kv=H_kv, T=T, D=D, dtype=dtype, seed=seed)
 
 
 def temperatures(rng: np.random.Generator, H: int, lo: float = 0.1, hi: float = 4.0):
@@ -125,6 +127,11 @@ WORKLOADS.update({
     "prefill_t512": dict(B=64, H=12, T=512, D=64, dtype=BF16, seed=5, n_frozen=3),
     "prefill_t2048": dict(B=64, H=12, T=2048, D=64, dtype=BF16, seed=6, n_frozen=6),
     "prefill_b1_t4096": dict(B=1, H=12, T=4096, D=64, dtype=BF16, seed=8, n_frozen=6),
+})
+# Grouped-query attention on the shape of a 4B-parameter model with shared key/value heads
+# (32 query heads over 8 key/value heads of width 128), at a 4096-token context.
+WORKLOADS.update({
+    "gqa_4b": dict(B=1, H=32, T=4096, D=128, dtype=BF16, seed=9, n_frozen=8, kv_heads=8),
 })
 PREFILL = dict(B=64, H=12, D=64, T=(512, 1024, 2048, 4096, 8192, 16384), n_frozen=(0, 3, 6),
                single=dict(B=1, T=4096), seed=7)

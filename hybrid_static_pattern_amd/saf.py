@@ -39,6 +39,7 @@ class AttnDesc(ctypes.Structure):
         ("B", ctypes.c_int32), ("H", ctypes.c_int32), ("T", ctypes.c_int32), ("D", ctypes.c_int32),
         ("io_dtype", ctypes.c_int), ("grad_dtype", ctypes.c_int), ("scale", ctypes.c_float),
         ("frozen_mask", ctypes.POINTER(ctypes.c_uint8)), ("tab_stride", ctypes.c_int32),
+        ("kv_heads", ctypes.c_int32),
     ]
 
 
@@ -150,13 +151,22 @@ def _mask(frozen, H):
     return m
 
 
+def _heads(v, frozen):
+    """(B, H, H_kv, T, D): H query heads from the frozen mask, H_kv key/value heads from v."""
+    B, H_kv, T, D = v.shape
+    H = int(np.asarray(frozen).reshape(-1).size)
+    if H_kv < 1 or H % H_kv:
+        raise ValueError(f"v has {H_kv} heads, which must divide the {H} query heads of the frozen mask")
+    return B, H, H_kv, T, D
+
+
 def _attn_desc(v, frozen, alpha, scale):
-    B, H, T, D = v.shape
+    B, H, H_kv, T, D = _heads(v, frozen)
     mask = _mask(frozen, H)
     tab = alpha.shape[-1] if alpha is not None else T
     desc = AttnDesc(B, H, T, D, _io_dtype(v), SAF_FP32,
                     float(scale if scale is not None else 1.0 / math.sqrt(D)),
-                    mask.ctypes.data_as(ctypes.POINTER(ctypes.c_uint8)), tab)
+                    mask.ctypes.data_as(ctypes.POINTER(ctypes.c_uint8)), tab, H_kv)
     return desc, mask
 
 
@@ -172,18 +182,19 @@ def _tables(alpha, rho, H, T, dev):
 
 
 def attn_fwd(q, k, v, frozen, alpha=None, rho=None, scale=None, o=None, lse=None):
-    """Hybrid forward (saf_attn_fwd). q, k, v: [B,H,T,D] bf16 or fp32 device tensors (q, k may
-    be None if every head is frozen); frozen: host sequence of H flags; alpha, rho: [H, >=T]
-    float32. Returns (o [B,H,T,D] in v's dtype, lse [B,H,T] float32)."""
+    """Hybrid forward (saf_attn_fwd). q: [B,H,T,D], k, v: [B,H_kv,T,D] (H_kv = H, or a divisor
+    of H for grouped-query attention), bf16 or fp32 device tensors (q, k may be None if every
+    head is frozen); frozen: host sequence of H flags; alpha, rho: [H, >=T] float32.
+    Returns (o [B,H,T,D] in v's dtype, lse [B,H,T] float32)."""
     lib = load()
-    B, H, T, D = v.shape
-    for name, t in (("q", q), ("k", k), ("v", v), ("o", o)):
-        _need(t, name, shape=(B, H, T, D), dtype=v.dtype, device=v.device)
+    B, H, H_kv, T, D = _heads(v, frozen)
+    for name, t, hh in (("q", q, H), ("k", k, H_kv), ("v", v, H_kv), ("o", o, H)):
+        _need(t, name, shape=(B, hh, T, D), dtype=v.dtype, device=v.device)
     _need(lse, "lse", shape=(B, H, T), dtype=torch.float32, device=v.device)
     _tables(alpha, rho, H, T, v.device)
     desc, mask = _attn_desc(v, frozen, alpha, scale)
     if o is None:
-        o = torch.empty_like(v)
+        o = torch.empty((B, H, T, D), dtype=v.dtype, device=v.device)
     if lse is None:
         lse = torch.empty((B, H, T), dtype=torch.float32, device=v.device)
     _check(lib.saf_attn_fwd(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(rho),
@@ -198,15 +209,16 @@ def attn_workspace_size(v, frozen, alpha=None, scale=None) -> int:
 
 def attn_bwd(q, k, v, o, do, lse, frozen, alpha=None, rho=None, scale=None,
              dq=None, dk=None, dv=None, workspace=None):
-    """Hybrid backward (saf_attn_bwd). Returns (dq, dk, dv), float32 [B,H,T,D]. dq and dk of
-    frozen heads are never written (they keep whatever the given buffers, or zeros, hold)."""
+    """Hybrid backward (saf_attn_bwd). Returns (dq [B,H,T,D], dk, dv [B,H_kv,T,D]), float32.
+    dq of frozen heads and dk of key/value heads read by frozen heads only are never written
+    (they keep whatever the given buffers, or zeros, hold)."""
     lib = load()
-    B, H, T, D = v.shape
-    for name, t in (("q", q), ("k", k), ("v", v), ("o", o), ("do", do)):
-        _need(t, name, shape=(B, H, T, D), dtype=v.dtype, device=v.device)
+    B, H, H_kv, T, D = _heads(v, frozen)
+    for name, t, hh in (("q", q, H), ("k", k, H_kv), ("v", v, H_kv), ("o", o, H), ("do", do, H)):
+        _need(t, name, shape=(B, hh, T, D), dtype=v.dtype, device=v.device)
     _need(lse, "lse", shape=(B, H, T), dtype=torch.float32, device=v.device)
-    for name, t in (("dq", dq), ("dk", dk), ("dv", dv)):
-        _need(t, name, shape=(B, H, T, D), dtype=torch.float32, device=v.device)
+    for name, t, hh in (("dq", dq, H), ("dk", dk, H_kv), ("dv", dv, H_kv)):
+        _need(t, name, shape=(B, hh, T, D), dtype=torch.float32, device=v.device)
     _tables(alpha, rho, H, T, v.device)
     desc, mask = _attn_desc(v, frozen, alpha, scale)
     need = int(lib.saf_attn_workspace_size(ctypes.byref(desc)))
@@ -216,9 +228,9 @@ def attn_bwd(q, k, v, o, do, lse, frozen, alpha=None, rho=None, scale=None,
     if dq is None:
         dq = torch.zeros((B, H, T, D), dtype=torch.float32, device=v.device)
     if dk is None:
-        dk = torch.zeros((B, H, T, D), dtype=torch.float32, device=v.device)
+        dk = torch.zeros((B, H_kv, T, D), dtype=torch.float32, device=v.device)
     if dv is None:
-        dv = torch.empty((B, H, T, D), dtype=torch.float32, device=v.device)
+        dv = torch.empty((B, H_kv, T, D), dtype=torch.float32, device=v.device)
     _check(lib.saf_attn_bwd(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(do), _ptr(lse),
                             _ptr(alpha), _ptr(rho), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(workspace),
                             workspace.numel() * workspace.element_size(), _stream(v)))

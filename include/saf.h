@@ -54,7 +54,12 @@ typedef enum { SAF_FP32 = 0, SAF_BF16 = 1 } saf_dtype;
  *               frozen-head logits alpha + rho are not scaled (Eq. (3)).
  *  frozen_mask  HOST array [H]; nonzero marks a frozen (static-pattern) head (the selected
  *               head set of part 二.1 / Algorithm 1).
- *  tab_stride   row stride, in elements, of alpha and rho (>= T). */
+ *  tab_stride   row stride, in elements, of alpha and rho (>= T).
+ *  kv_heads     number of key/value heads H_kv: 0 or H for ordinary multi-head attention,
+ *               or a divisor of H for grouped-query attention (the GQA path of part 二.4,
+ *               section 3.3 / Appendix D.2): query head h reads K and V of head h / (H/H_kv),
+ *               so a frozen head drops only its query and still mixes its group's V.
+ *               K, V, dK and dV are then [B, H_kv, T, D]; Q, O, dO, dQ stay [B, H, T, D]. */
 typedef struct {
   int32_t B, H, T, D;
   saf_dtype io_dtype;
@@ -62,6 +67,7 @@ typedef struct {
   float scale;
   const uint8_t* frozen_mask;
   int32_t tab_stride;
+  int32_t kv_heads;
 } saf_attn_desc;
 
 /* Hybrid forward (part 一; part 二.3 Eq. (3); part 二.4 and Fig. 2).
@@ -88,6 +94,9 @@ size_t saf_attn_workspace_size(const saf_attn_desc* desc);
  *                 gradient and there is no query or key); lse must hold log Z(i).
  * o and lse are the forward's outputs for the same inputs. dQ/dK slices of frozen heads
  * are never written; dV is written for every head. Gradients are float32.
+ * With shared key/value heads (kv_heads < H) the gradient of a shared K or V is the sum over
+ * the query heads of its group: dK[b, g] sums the group's ordinary heads (and is not written
+ * when every head of the group is frozen); dV[b, g] sums all of them.
  * workspace: device memory of at least saf_attn_workspace_size(desc) bytes, caller-owned,
  * contents need not be initialised and are garbage afterwards. */
 saf_status saf_attn_bwd(const saf_attn_desc* desc, const void* q, const void* k,

@@ -39,9 +39,9 @@ def test_status_strings(lib):
         assert lib.saf_status_string(st).decode().startswith("SAF_")
 
 
-def _desc(B=1, H=2, T=16, D=64, io=saf.SAF_BF16, grad=saf.SAF_FP32, scale=0.125, stride=16, mask=None):
+def _desc(B=1, H=2, T=16, D=64, io=saf.SAF_BF16, grad=saf.SAF_FP32, scale=0.125, stride=16, mask=None, kv=0):
     mask = np.zeros(H, np.uint8) if mask is None else mask
-    d = saf.AttnDesc(B, H, T, D, io, grad, scale, mask.ctypes.data_as(ctypes.POINTER(ctypes.c_uint8)), stride)
+    d = saf.AttnDesc(B, H, T, D, io, grad, scale, mask.ctypes.data_as(ctypes.POINTER(ctypes.c_uint8)), stride, kv)
     return d, mask
 
 
@@ -52,6 +52,7 @@ FAKE = ctypes.c_void_p(0x10000)  # aligned, never dereferenced: validation fails
     (dict(B=0), saf.SAF_EINVAL), (dict(T=0), saf.SAF_EINVAL), (dict(D=96), saf.SAF_EUNSUPPORTED),
     (dict(H=300, stride=16), saf.SAF_EUNSUPPORTED), (dict(grad=saf.SAF_BF16), saf.SAF_EUNSUPPORTED),
     (dict(scale=0.0), saf.SAF_EINVAL), (dict(io=7), saf.SAF_EINVAL),
+    (dict(H=6, kv=4), saf.SAF_EINVAL), (dict(H=2, kv=3), saf.SAF_EINVAL), (dict(kv=-1), saf.SAF_EINVAL),
 ])
 def test_fwd_rejects_bad_descriptor(lib, kw, status):
     d, mask = _desc(**kw)
@@ -82,6 +83,16 @@ def test_bwd_workspace_contract(lib):
                           FAKE, FAKE, FAKE, FAKE, need - 1, None)
     assert st == saf.SAF_EWORKSPACE
     assert lib.saf_attn_workspace_size(None) == 0
+
+
+def test_gqa_workspace_contract(lib):
+    """Shared key/value heads need two more [B, H, T, D] float32 arrays (per-query-head dK, dV)."""
+    d1, m1 = _desc(B=2, H=8, T=100, kv=8)
+    d2, m2 = _desc(B=2, H=8, T=100, kv=2)
+    n1, n2 = lib.saf_attn_workspace_size(ctypes.byref(d1)), lib.saf_attn_workspace_size(ctypes.byref(d2))
+    assert n2 - n1 >= 2 * 2 * 8 * 100 * 64 * 4
+    d0, m0 = _desc(B=2, H=8, T=100, kv=0)
+    assert lib.saf_attn_workspace_size(ctypes.byref(d0)) == n1
 
 
 def test_var_contract(lib):

@@ -30,9 +30,8 @@ def run(S, L, bwd=True, sentinel=float("nan")):
     o, lse = S.attn_fwd(q, k, g["v"], fz, g["alpha"], g["rho"])
     res = dict(o=o, lse=lse)
     if bwd:
-        shape = tuple(g["v"].shape)
-        dq = torch.full(shape, sentinel, dtype=torch.float32, device=dev())
-        dk = torch.full(shape, sentinel, dtype=torch.float32, device=dev())
+        dq = torch.full(tuple(g["do"].shape), sentinel, dtype=torch.float32, device=dev())
+        dk = torch.full(tuple(g["v"].shape), sentinel, dtype=torch.float32, device=dev())
         dq, dk, dv = S.attn_bwd(q, k, g["v"], o, g["do"], lse, fz, g["alpha"], g["rho"], dq=dq, dk=dk)
         res.update(dq=dq, dk=dk, dv=dv)
     torch.cuda.synchronize()
@@ -49,13 +48,17 @@ def compare_layer(L, out, bwd=True):
         return
     dq, dk, dv = saf_oracle.attn_bwd(L["q"], L["k"], L["v"], L["do"], L["frozen"], L["alpha"], L["rho"], scale)
     dyn = L["frozen"] == 0
+    # a key/value head gets dK from the ordinary query heads of its group (with H_kv = H,
+    # the group is the head itself)
+    G = len(dyn) // L["v"].shape[1]
+    kv_dyn = dyn.reshape(-1, G).any(axis=1)
     if dyn.any():
         check(out["dq"][:, dyn], dq[:, dyn], dt, "dQ")
-        check(out["dk"][:, dyn], dk[:, dyn], dt, "dK")
+        check(out["dk"][:, kv_dyn], dk[:, kv_dyn], dt, "dK")
     check(out["dv"], dv, dt, "dV")
-    frz = ~dyn
-    # dQ/dK slices of frozen heads are never written (NaN sentinels survive)
-    assert np.all(np.isnan(out["dq"][:, frz])) and np.all(np.isnan(out["dk"][:, frz]))
+    # dQ of frozen heads and dK of key/value heads without an ordinary query head are never
+    # written (NaN sentinels survive)
+    assert np.all(np.isnan(out["dq"][:, ~dyn])) and np.all(np.isnan(out["dk"][:, ~kv_dyn]))
 
 
 # ---------------------------------------------------------------- small layers
@@ -92,6 +95,36 @@ BF16_CASES = [
 def test_bf16_forward_backward(S, B, H, T, D, frozen):
     L = inputs.make_layer(B, H, T, D, dtype="bf16", seed=7, frozen_heads=frozen)
     compare_layer(L, run(S, L))
+
+
+# Shared key/value heads (grouped-query attention): B, H, H_kv, T, D, frozen heads, dtype
+GQA_CASES = [
+    (2, 4, 2, 300, 64, [1, 2], "bf16"),        # one frozen head in each group
+    (1, 6, 2, 257, 128, [0, 1, 2], "bf16"),    # group 0 all frozen: its dK is never written
+    (3, 4, 1, 130, 64, [3], "bf16"),           # one shared head (multi-query)
+    (1, 8, 2, 513, 64, [0, 5, 6, 7], "bf16"),  # crosses the 512-key dK/dV tile; folded 64 columns
+    (2, 4, 2, 70, 64, [1, 2], "fp32"),
+    (1, 4, 1, 33, 128, [0], "fp32"),
+    (2, 6, 3, 40, 64, [2, 3], "fp32"),         # group 1 all frozen
+]
+
+
+@pytest.mark.parametrize("B,H,H_kv,T,D,frozen,dt", GQA_CASES)
+def test_gqa_forward_backward(S, B, H, H_kv, T, D, frozen, dt):
+    L = inputs.make_layer(B, H, T, D, dtype=dt, seed=17, frozen_heads=frozen, kv_heads=H_kv)
+    compare_layer(L, run(S, L))
+
+
+def test_gqa_frozen_query_never_read(S):
+    """A frozen head of a shared group reads V of its group but never its own query."""
+    L = inputs.make_layer(1, 4, 100, 64, dtype="bf16", seed=18, frozen_heads=[1, 3], kv_heads=2)
+    ref = run(S, L)
+    L2 = dict(L)
+    L2["q"] = L["q"].copy()
+    L2["q"][:, [1, 3]] = np.nan
+    out = run(S, L2)
+    for key in ("o", "lse", "dv"):
+        assert np.array_equal(out[key], ref[key]), key
 
 
 # ---------------------------------------------------------------- closed forms on the GPU
@@ -298,6 +331,30 @@ def test_full_prefill_t512(S):
 
 def test_full_prefill_single_sequence(S):
     _full(S, "prefill_b1_t4096", [(0, first_frozen), (0, last_dynamic)])
+
+
+def test_full_gqa_4b_sampled(S):
+    """The shared-key/value shape (B=1, H=32 over 8 key/value heads, T=4096, D=128, r=25%):
+    two whole groups (four query heads each) against the oracle."""
+    L = inputs.make_layer(**dict(inputs.WORKLOADS["gqa_4b"]))
+    out = run(S, L)
+    scale = 1.0 / math.sqrt(L["D"])
+    G = L["H"] // L["H_kv"]
+    fz = L["frozen"]
+    groups = sorted({int(np.flatnonzero(fz)[0]) // G, int(np.flatnonzero(fz == 0)[-1]) // G})
+    for g in groups:
+        hs = slice(g * G, (g + 1) * G)
+        O, lse = saf_oracle.attn_fwd(L["q"][:, hs], L["k"][:, g:g + 1], L["v"][:, g:g + 1], fz[hs],
+                                     L["alpha"][hs], L["rho"][hs], scale)
+        dq, dk, dv = saf_oracle.attn_bwd(L["q"][:, hs], L["k"][:, g:g + 1], L["v"][:, g:g + 1], L["do"][:, hs],
+                                         fz[hs], L["alpha"][hs], L["rho"][hs], scale)
+        check(out["o"][:, hs], O, "bf16", f"O group {g}")
+        check(out["lse"][:, hs], lse, "bf16", f"lse group {g}", lse=True)
+        check(out["dv"][:, g:g + 1], dv, "bf16", f"dV group {g}")
+        dyn = fz[hs] == 0
+        if dyn.any():
+            check(out["dq"][:, hs][:, dyn], dq[:, dyn], "bf16", f"dQ group {g}")
+            check(out["dk"][:, g:g + 1], dk, "bf16", f"dK group {g}")
 
 
 def test_full_prefill_t2048_half_frozen(S):
