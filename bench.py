@@ -103,6 +103,7 @@ def main():
     ap.add_argument("--no-calibration", action="store_true", help="skip the calibration-score timing")
     ap.add_argument("--no-prefill", action="store_true", help="skip the causal-prefill timings")
     ap.add_argument("--no-fit", action="store_true", help="skip the compact-fit timing")
+    ap.add_argument("--no-gqa", action="store_true", help="skip the grouped-query-attention timing")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="first run one plain elementwise copy (torch.neg) of this many MiB, a "
                          "known-size reference for the FETCH_SIZE / WRITE_SIZE counters")
@@ -217,6 +218,9 @@ def main():
     if not args.no_fit:
         log("timing the compact pattern fit")
         out["fit"] = fit(torch, inputs, saf, args.no_cpu_baseline)
+    if not args.no_gqa:
+        log("timing the grouped-query-attention layer")
+        out["gqa"] = gqa(torch, inputs, saf, args.steps, args.warmup)
     if not args.no_prefill:
         log("timing the causal prefill workload")
         out["prefill"] = prefill(torch, inputs, saf, args.steps, args.warmup)
@@ -286,6 +290,61 @@ def prefill(torch, inputs, saf, steps, warmup):
     s = P["single"]
     out["single"] = {"B": s["B"], "T": s["T"], **run(s["B"], s["T"], P["seed"])}
     return out
+
+
+def gqa(torch, inputs, saf, steps, warmup):
+    """Forward + backward of the grouped-query layer inputs.WORKLOADS["gqa_4b"] (B=1, 32 query
+    heads over 8 key/value heads, T=4096, D=128, bf16) at r = 0, 25% and 50% (seeded frozen
+    sets), inputs drawn on the device. Reports ms per step, tokens/s, the speed-up over r = 0
+    and the per-kernel times of the r = 25% step (including the group sum of dK, dV)."""
+    spec = dict(inputs.WORKLOADS["gqa_4b"])
+    B, H, Hkv, T, D = spec["B"], spec["H"], spec["kv_heads"], spec["T"], spec["D"]
+    dev = torch.device("cuda:0")
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(spec["seed"])
+    rnd = lambda shape: torch.randn(shape, generator=gen, device=dev).to(torch.bfloat16)
+    q, do = rnd((B, H, T, D)), rnd((B, H, T, D))
+    k, v = rnd((B, Hkv, T, D)), rnd((B, Hkv, T, D))
+    alpha, rho = (torch.from_numpy(x).to(dev) for x in inputs.make_tables(np.random.default_rng(spec["seed"]), H, T))
+    o = torch.empty_like(q)
+    lse = torch.empty((B, H, T), dtype=torch.float32, device=dev)
+    dq = torch.zeros((B, H, T, D), dtype=torch.float32, device=dev)
+    dk, dv = (torch.zeros((B, Hkv, T, D), dtype=torch.float32, device=dev) for _ in range(2))
+    res = {}
+    for nf in (0, H // 4, H // 2):
+        m = np.zeros(H, np.uint8)
+        if nf:
+            m[np.sort(np.random.default_rng(spec["seed"]).choice(H, nf, replace=False))] = 1
+        ws = torch.empty(max(saf.attn_workspace_size(v, m, alpha), 1), dtype=torch.uint8, device=dev)
+
+        def step():
+            saf.attn_fwd(q, k, v, m, alpha, rho, o=o, lse=lse)
+            saf.attn_bwd(q, k, v, o, do, lse, m, alpha, rho, dq=dq, dk=dk, dv=dv, workspace=ws)
+
+        for _ in range(warmup):
+            step()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(steps):
+            step()
+        e1.record()
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / steps
+        key = f"r{round(100 * nf / H)}"
+        res[key] = {"ms_per_step": ms, "tokens_per_s": B * T / (ms * 1e-3),
+                    "tflops": layer_flops(B, T, D, H - nf, nf) / (ms * 1e-3) / 1e12}
+        if nf == H // 4:
+            saf.prof_enable(True)
+            step()
+            recs = saf.prof_read()
+            saf.prof_enable(False)
+            res[key]["kernels_ms"] = {n: t for n, t in recs}
+    for key in res:
+        if key != "r0":
+            res[key]["speedup_vs_r0"] = res["r0"]["ms_per_step"] / res[key]["ms_per_step"]
+    return {"workload": f"grouped-query layer fwd+bwd: B={B} H={H} over {Hkv} key/value heads, T={T}, D={D}, bf16",
+            **res}
 
 
 def calibration(torch, inputs, profiling, saf, steps, warmup):
