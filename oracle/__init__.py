@@ -7,5 +7,5 @@ none of them is "parity unpinned". compact_fit holds the fit of Eq. (3) to a tar
 pattern (its own pins: tests/oracle_pins_fit.py).
 """
 from .saf_oracle import (attn_bwd, attn_fwd, causal_mask, dynamic_probs, frozen_probs,  # noqa: F401
-                         mean_attention, n_selected, rank_heads, reconstruction_risk,
-                         select_heads, var_score, variance_score)
+                         kl_score, kl_score_of, mean_attention, n_selected, rank_heads,
+                         reconstruction_risk, select_heads, var_score, variance_score)

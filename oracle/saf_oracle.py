@@ -197,6 +197,34 @@ def var_score(q, k, scale: float):
     return A_hat, s_var, rank_heads(s_var)
 
 
+def kl_score_of(A_stack):
+    """Row-wise forward-KL score of one head (part 二.1 names it s^KL as the alternative
+    selector and prints no formula; read as the mean over sequences n and rows i of
+    KL(A^(n)_i || A-hat_i)): (1/(N T)) sum_n sum_i sum_{j<=i} A^(n)(i,j) log(A^(n)(i,j) / A-hat(i,j)),
+    with 0 log 0 = 0. A_stack: [N,T,T]. Returns s_kl and A-hat."""
+    A_stack = _f64(A_stack)
+    N, T, _ = A_stack.shape
+    A_hat = mean_attention(A_stack)
+    pos = A_stack > 0
+    ratio = np.where(pos, A_stack, 1.0) / np.where(pos, A_hat[None], 1.0)
+    terms = np.where(pos, A_stack * np.log(ratio), 0.0)
+    return float(terms.sum() / (N * T)), A_hat
+
+
+def kl_score(q, k, scale: float):
+    """The forward-KL selector for every head of one layer, like var_score: returns
+    A_hat [H,T,T], s_kl [H] and rank [H] (ascending s_kl, ties to the lower index)."""
+    N, H, T, _ = np.shape(q)
+    if N < 2:
+        raise ValueError("the score compares N >= 2 calibration sequences")
+    A_hat = np.empty((H, T, T))
+    s_kl = np.empty(H)
+    for h in range(H):
+        A_stack = np.stack([dynamic_probs(q[n, h], k[n, h], scale)[0] for n in range(N)])
+        s_kl[h], A_hat[h] = kl_score_of(A_stack)
+    return A_hat, s_kl, rank_heads(s_kl)
+
+
 def rank_heads(s_var):
     """Head indices sorted by ascending s_var, stable (lower index first on ties)."""
     return np.argsort(np.asarray(s_var), kind="stable").astype(np.int32)

@@ -307,6 +307,32 @@ def pin_var_T2_closed_form(orc):
     assert abs(s_var[0] - np.var(a, ddof=1) / 2) < 1e-15
 
 
+def pin_kl_score_closed_forms(orc):
+    """s^KL: 0 for identical inputs; the T = 2 closed form (row 0 is always [1]; row 1 is
+    (a_n, 1 - a_n) against the mean (a, 1 - a)) written with math.log; scipy's rel_entr on a
+    random stack; non-negative (Jensen)."""
+    from scipy.special import rel_entr
+    r = _rng(31)
+    N, T = 5, 2
+    a = r.uniform(0.05, 0.95, N)
+    stack = np.zeros((N, T, T))
+    stack[:, 0, 0] = 1.0
+    stack[:, 1, 0], stack[:, 1, 1] = a, 1 - a
+    s_kl, _ = orc.kl_score_of(stack)
+    ab = sum(a) / N
+    want = sum(x * math.log(x / ab) + (1 - x) * math.log((1 - x) / (1 - ab)) for x in a) / (N * T)
+    assert abs(s_kl - want) < 1e-15
+    same, _ = orc.kl_score_of(np.repeat(stack[:1], 4, axis=0))
+    assert same == 0.0
+    N, T = 6, 11
+    E = np.tril(r.uniform(0.0, 1.0, (N, T, T)))
+    E[:, 3, 1] = 0.0   # a zero weight in every sequence
+    A = E / E.sum(axis=2, keepdims=True)
+    s_kl, A_hat = orc.kl_score_of(A)
+    ref = sum(rel_entr(A[n], A_hat).sum() for n in range(N)) / (N * T)
+    assert abs(s_kl - ref) < 1e-14 and s_kl > 0
+
+
 def pin_mean_optimality(orc):
     """Appendix B.1: R_N(P) = R_N(A-hat) + ||P - A-hat||_F^2 / T^2 for any fixed P, and the
     minimum R_N(A-hat) equals (N-1)/N s_var."""

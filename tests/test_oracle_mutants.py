@@ -148,6 +148,21 @@ def _var_div_pairs(A_stack):
     return float(((A_stack - A_hat) ** 2).sum() / ((N - 1) * T * (T + 1) / 2)), A_hat
 
 
+def _kl_reverse(A_stack):
+    A_stack = np.asarray(A_stack, float)
+    N, T, _ = A_stack.shape
+    A_hat = A_stack.mean(0)
+    pos = A_hat > 0
+    terms = [np.where(pos, A_hat * np.log(np.where(pos, A_hat, 1) / np.where(pos, A_stack[n], 1)), 0)
+             for n in range(N)]
+    return float(np.sum(terms) / (N * T)), A_hat
+
+
+def _kl_by_t2(A_stack):
+    val, A_hat = so.__dict__["_orig_kl"](A_stack)
+    return val / np.shape(A_stack)[1], A_hat
+
+
 def _rank_desc(s):
     return np.argsort(-np.asarray(s), kind="stable").astype(np.int32)
 
@@ -171,6 +186,8 @@ MUTANTS = {
     "var: divides by N": ("variance_score", _var_div_n),
     "var: divides by causal pairs": ("variance_score", _var_div_pairs),
     "rank: descending": ("rank_heads", _rank_desc),
+    "kl: reverse direction KL(A-hat || A)": ("kl_score_of", _kl_reverse),
+    "kl: divides by N T^2": ("kl_score_of", _kl_by_t2),
 }
 
 
@@ -179,6 +196,7 @@ def test_pins_reject_mutant(name, monkeypatch):
     attr, fn = MUTANTS[name]
     monkeypatch.setitem(so.__dict__, "_orig_frozen", so.frozen_probs)
     monkeypatch.setitem(so.__dict__, "_orig_dynamic", so.dynamic_probs)
+    monkeypatch.setitem(so.__dict__, "_orig_kl", so.kl_score_of)
     monkeypatch.setattr(so, attr, fn)
     caught = []
     for pin in PINS:
