@@ -378,11 +378,21 @@ def calibration(torch, inputs, profiling, saf, steps, warmup):
     for name, t in recs:
         per.setdefault(name, []).append(t)
     kern = {n: float(np.mean(v)) for n, v in per.items()}
+    # the forward-KL selector (saf_kl_score): same passes, a log term instead of M2
+    run_kl = lambda: saf.kl_score(q, k, a_hat=a_hat, s_kl=s_var, rank=rank, workspace=ws)
+    run_kl()
+    torch.cuda.synchronize()
+    e0.record(st)
+    for _ in range(steps):
+        run_kl()
+    e1.record(st)
+    torch.cuda.synchronize()
+    kl_ms = e0.elapsed_time(e1) / steps
     samples = N * H * causal_pairs(T)
     wf = WELFORD_FLOP_PER_SAMPLE * samples / (kern["var_welford"] * 1e-3) / 1e12
     return {
         "workload": f"calibration: N={N} H={H} T={T} D={D} bf16, tau in [0.1, 4]",
-        "ms": ms, "sample_pairs_per_s": samples / (ms * 1e-3), "kernels_ms": kern,
+        "ms": ms, "sample_pairs_per_s": samples / (ms * 1e-3), "kernels_ms": kern, "kl_score_ms": kl_ms,
         "ranking": [int(x) for x in rank.cpu().numpy()],
         "roofline": {"kernel": "var_welford", "bound": "alu", "achieved": wf, "peak": PEAK_FP32_VALU_TFLOPS,
                      "unit": "TFLOP/s", "frac": wf / PEAK_FP32_VALU_TFLOPS,

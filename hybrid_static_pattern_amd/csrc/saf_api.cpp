@@ -251,8 +251,26 @@ saf_status saf_var_score(const saf_var_desc* desc, const void* q, const void* k,
   const size_t need = saf::var_workspace_bytes(a);
   if (ws_bytes < need) return fail(SAF_EWORKSPACE, "workspace has %zu bytes, needs %zu", ws_bytes, need);
   (void)hipGetLastError();
-  hipError_t e = saf::launch_var_score(a, q, k, a_hat, s_var, rank, workspace, static_cast<hipStream_t>(stream));
+  hipError_t e = saf::launch_var_score(a, q, k, a_hat, s_var, rank, workspace, static_cast<hipStream_t>(stream), false);
   if (e != hipSuccess) return hip_fail(e, "var_score launch");
+  return SAF_OK;
+}
+
+saf_status saf_kl_score(const saf_var_desc* desc, const void* q, const void* k, float* a_hat, double* s_kl,
+                        int32_t* rank, void* workspace, size_t ws_bytes, void* stream) {
+  saf::VarArgs a;
+  SAF_TRY(validate_var(desc, &a));
+  SAF_TRY(check_ptr(q, true, "q"));
+  SAF_TRY(check_ptr(k, true, "k"));
+  SAF_TRY(check_ptr(a_hat, true, "a_hat"));
+  SAF_TRY(check_ptr(s_kl, true, "s_kl"));
+  SAF_TRY(check_ptr(rank, true, "rank"));
+  SAF_TRY(check_ptr(workspace, true, "workspace"));
+  const size_t need = saf::var_workspace_bytes(a);
+  if (ws_bytes < need) return fail(SAF_EWORKSPACE, "workspace has %zu bytes, needs %zu", ws_bytes, need);
+  (void)hipGetLastError();
+  hipError_t e = saf::launch_var_score(a, q, k, a_hat, s_kl, rank, workspace, static_cast<hipStream_t>(stream), true);
+  if (e != hipSuccess) return hip_fail(e, "kl_score launch");
   return SAF_OK;
 }
 

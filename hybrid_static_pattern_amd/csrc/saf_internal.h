@@ -70,8 +70,10 @@ struct VarArgs {
   float scale;
 };
 size_t var_workspace_bytes(const VarArgs& a);
+// kl = false: the variance score s_var of Eq. (1); kl = true: the forward-KL score s^KL
+// (same A_hat, the score written to s_var and ranked).
 hipError_t launch_var_score(const VarArgs& a, const void* q, const void* k, float* a_hat,
-                            double* s_var, int32_t* rank, void* ws, hipStream_t s);
+                            double* s_var, int32_t* rank, void* ws, hipStream_t s, bool kl);
 
 // Compact pattern fit.
 struct FitArgs {

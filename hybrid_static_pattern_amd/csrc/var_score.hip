@@ -123,7 +123,12 @@ __global__ __launch_bounds__(NTH, 2) void var_lse_kernel(const VarParams p) {
   if (i < T && hh == 0) p.lse2[head + i] = mx_run + __log2f(lt);
 }
 
-template <int D>
+// KL = false: Welford's mean and M2, the tile's partial is sum M2 (Eq. (1)).
+// KL = true: the mean and, per lane, sum_n a log2 a (log2 a is the exponent itself); the
+// tile's partial is ln 2 [sum_n sum a log2 a / N - sum A_hat log2 A_hat], its share of
+// N T s^KL / N: since sum_n A^(n) = N A_hat entrywise,
+// sum_n KL(A^(n)_i || A_hat_i) = sum_n sum_j A^(n) log A^(n) - N sum_j A_hat log A_hat.
+template <int D, bool KL>
 __global__ __launch_bounds__(NTH, 2) void var_welford_kernel(const VarParams p) {
   __shared__ __attribute__((aligned(16))) KTile<D> stg[2];
   __shared__ float red[NTH / 64];
@@ -153,11 +158,12 @@ __global__ __launch_bounds__(NTH, 2) void var_welford_kernel(const VarParams p) 
     return;
   }
 
-  float mean[32], m2[32];
+  float mean[32], m2[KL ? 1 : 32];
+  float alog = 0.f;   // KL: sum over n and this lane's entries of a log2 a
 #pragma unroll
   for (int x = 0; x < 32; ++x) {
     mean[x] = 0.f;
-    m2[x] = 0.f;
+    if constexpr (!KL) m2[x] = 0.f;
   }
   const bool active = j0 <= i0w;     // wave has causal entries in this tile
   const bool diag = j0 + BN - 1 > i0w;
@@ -181,12 +187,17 @@ __global__ __launch_bounds__(NTH, 2) void var_welford_kernel(const VarParams p) 
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          float a = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kb][r], p.c, -l2));
+          const float z = __builtin_fmaf(s[kb][r], p.c, -l2);
+          float a = __builtin_amdgcn_exp2f(z);
           if (diag && j0 + kb * 32 + acc_pos(r, hh) > i) a = 0.f;
           const int x = kb * 16 + r;
           const float dlt = a - mean[x];
           mean[x] = __builtin_fmaf(dlt, rn, mean[x]);
-          m2[x] = __builtin_fmaf(dlt, a - mean[x], m2[x]);
+          if constexpr (KL) {
+            if (a > 0.f) alog = __builtin_fmaf(a, z, alog);
+          } else {
+            m2[x] = __builtin_fmaf(dlt, a - mean[x], m2[x]);
+          }
         }
     }
     wait_vm0();
@@ -210,8 +221,16 @@ __global__ __launch_bounds__(NTH, 2) void var_welford_kernel(const VarParams p) 
             if (jj + e < T) row[jj + e] = mv[e];
         }
       }
+    if constexpr (KL) {
+      float hl = 0.f;
 #pragma unroll
-    for (int x = 0; x < 32; ++x) sum += m2[x];
+      for (int x = 0; x < 32; ++x)
+        if (mean[x] > 0.f) hl = __builtin_fmaf(mean[x], __log2f(mean[x]), hl);
+      sum = kLn2 * (alog / (float)p.N - hl);
+    } else {
+#pragma unroll
+      for (int x = 0; x < 32; ++x) sum += m2[x];
+    }
   }
 #pragma unroll
   for (int o = 32; o >= 1; o >>= 1) sum += __shfl_xor(sum, o, 64);
@@ -220,6 +239,9 @@ __global__ __launch_bounds__(NTH, 2) void var_welford_kernel(const VarParams p) 
   if (t == 0) *part = red[0] + red[1] + red[2] + red[3];
 }
 
+// Sums each head's tile partials in float64 and ranks the heads by the score:
+// KL = false: s_var = sum M2 / ((N - 1) T^2); KL = true: s^KL = sum / T.
+template <bool KL>
 __global__ __launch_bounds__(256) void var_final_kernel(const VarParams p) {
   __shared__ double sv[kMaxHeads];
   const int h = threadIdx.x;
@@ -228,7 +250,7 @@ __global__ __launch_bounds__(256) void var_final_kernel(const VarParams p) {
     double acc = 0.0;
     const float* part = p.partial + (size_t)h * per;
     for (int x = 0; x < per; ++x) acc += (double)part[x];
-    const double v = acc / ((double)(p.N - 1) * (double)p.T * (double)p.T);
+    const double v = KL ? acc / (double)p.T : acc / ((double)(p.N - 1) * (double)p.T * (double)p.T);
     sv[h] = v;
     p.s_var[h] = v;
   }
@@ -251,7 +273,7 @@ size_t var_workspace_bytes(const VarArgs& a) {
 }
 
 hipError_t launch_var_score(const VarArgs& a, const void* q, const void* k, float* a_hat,
-                            double* s_var, int32_t* rank, void* ws, hipStream_t s) {
+                            double* s_var, int32_t* rank, void* ws, hipStream_t s, bool kl) {
   VarParams p;
   p.q = static_cast<const bf16*>(q);
   p.k = static_cast<const bf16*>(k);
@@ -274,15 +296,20 @@ hipError_t launch_var_score(const VarArgs& a, const void* q, const void* k, floa
   prof_end(s);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  prof_begin("var_welford", s);
-  if (a.D == 64)
-    hipLaunchKernelGGL(var_welford_kernel<64>, dim3(p.n_jt * p.n_it * a.H), dim3(NTH), 0, s, p);
-  else
-    hipLaunchKernelGGL(var_welford_kernel<128>, dim3(p.n_jt * p.n_it * a.H), dim3(NTH), 0, s, p);
+  const dim3 grid(p.n_jt * p.n_it * a.H), block(NTH);
+  prof_begin(kl ? "kl_welford" : "var_welford", s);
+  if (a.D == 64) {
+    if (kl) hipLaunchKernelGGL((var_welford_kernel<64, true>), grid, block, 0, s, p);
+    else hipLaunchKernelGGL((var_welford_kernel<64, false>), grid, block, 0, s, p);
+  } else {
+    if (kl) hipLaunchKernelGGL((var_welford_kernel<128, true>), grid, block, 0, s, p);
+    else hipLaunchKernelGGL((var_welford_kernel<128, false>), grid, block, 0, s, p);
+  }
   prof_end(s);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   prof_begin("var_final", s);
-  hipLaunchKernelGGL(var_final_kernel, dim3(1), dim3(256), 0, s, p);
+  if (kl) hipLaunchKernelGGL(var_final_kernel<true>, dim3(1), dim3(256), 0, s, p);
+  else hipLaunchKernelGGL(var_final_kernel<false>, dim3(1), dim3(256), 0, s, p);
   prof_end(s);
   return hipGetLastError();
 }

@@ -24,7 +24,7 @@ EXPORTS = (
     "saf_attn_fwd", "saf_attn_workspace_size", "saf_attn_bwd", "saf_var_workspace_size",
     "saf_var_score", "saf_select_heads", "saf_status_string", "saf_last_error",
     "saf_prof_enable", "saf_prof_read", "saf_pattern_stats", "saf_compact_marginals",
-    "saf_fit_workspace_size", "saf_compact_fit", "saf_select_fitted",
+    "saf_fit_workspace_size", "saf_compact_fit", "saf_select_fitted", "saf_kl_score",
 )
 
 
@@ -81,6 +81,7 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.saf_var_workspace_size.argtypes = [pv]
     lib.saf_var_workspace_size.restype = sz
     lib.saf_var_score.argtypes = [pv, vp, vp, vp, vp, vp, vp, sz, vp]
+    lib.saf_kl_score.argtypes = [pv, vp, vp, vp, vp, vp, vp, sz, vp]
     lib.saf_select_heads.argtypes = [ctypes.POINTER(ctypes.c_double), i32, ctypes.c_double, ctypes.POINTER(i32)]
     lib.saf_select_heads.restype = i32
     lib.saf_status_string.argtypes = [ctypes.c_int]
@@ -98,7 +99,7 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.saf_select_fitted.argtypes = [ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_float), i32,
                                       ctypes.c_double, ctypes.c_float, ctypes.POINTER(i32)]
     lib.saf_select_fitted.restype = i32
-    for fn in ("saf_attn_fwd", "saf_attn_bwd", "saf_var_score", "saf_prof_enable", "saf_pattern_stats",
+    for fn in ("saf_attn_fwd", "saf_attn_bwd", "saf_var_score", "saf_kl_score", "saf_prof_enable", "saf_pattern_stats",
                "saf_compact_marginals", "saf_compact_fit"):
         getattr(lib, fn).restype = ctypes.c_int
     _lib = lib
@@ -245,6 +246,16 @@ def var_workspace_size(N, H, T, D, scale=None) -> int:
 def var_score(q, k, scale=None, a_hat=None, s_var=None, rank=None, workspace=None):
     """Calibration score (saf_var_score). q, k: [N,H,T,D] bf16 device tensors. Returns
     (a_hat [H,T,T] float32, s_var [H] float64, rank [H] int32), all on the device."""
+    return _score(load().saf_var_score, q, k, scale, a_hat, s_var, rank, workspace)
+
+
+def kl_score(q, k, scale=None, a_hat=None, s_kl=None, rank=None, workspace=None):
+    """Forward-KL selector (saf_kl_score), arguments as var_score. Returns (a_hat, s_kl [H]
+    float64, rank [H] int32 by ascending s_kl)."""
+    return _score(load().saf_kl_score, q, k, scale, a_hat, s_kl, rank, workspace)
+
+
+def _score(entry, q, k, scale, a_hat, s_var, rank, workspace):
     lib = load()
     N, H, T, D = q.shape
     _need(q, "q", dtype=q.dtype)
@@ -262,8 +273,8 @@ def var_score(q, k, scale=None, a_hat=None, s_var=None, rank=None, workspace=Non
         s_var = torch.empty((H,), dtype=torch.float64, device=q.device)
     if rank is None:
         rank = torch.empty((H,), dtype=torch.int32, device=q.device)
-    _check(lib.saf_var_score(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(a_hat), _ptr(s_var), _ptr(rank),
-                             _ptr(workspace), workspace.numel() * workspace.element_size(), _stream(q)))
+    _check(entry(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(a_hat), _ptr(s_var), _ptr(rank),
+                 _ptr(workspace), workspace.numel() * workspace.element_size(), _stream(q)))
     return a_hat, s_var, rank
 
 

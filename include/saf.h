@@ -127,6 +127,16 @@ saf_status saf_var_score(const saf_var_desc* desc, const void* q, const void* k,
                          float* a_hat, double* s_var, int32_t* rank, void* workspace,
                          size_t ws_bytes, void* stream);
 
+/* The forward-KL selector s^KL that part 二.1 compares with Eq. (1) (the page prints no
+ * formula; read as the mean over sequences n and rows i of KL(A^(n)_i || A_hat_i)):
+ *   s_kl[h] = (1/(N T)) sum_n sum_i sum_{j<=i} A^(n)(i,j) log(A^(n)(i,j) / A_hat(i,j)),
+ * computed in the same pass as a_hat (sum_n A^(n) = N A_hat turns it into
+ * sum_n A log A - N A_hat log A_hat per entry). Arguments, workspace and a_hat as for
+ * saf_var_score; rank orders the heads by ascending s_kl. */
+saf_status saf_kl_score(const saf_var_desc* desc, const void* q, const void* k, float* a_hat,
+                        double* s_kl, int32_t* rank, void* workspace, size_t ws_bytes,
+                        void* stream);
+
 /* Host-only selection across layers (part 二.1): sorts n_heads scores (all L*H heads of a
  * model) ascending, ties to the lower index, and writes the first k = floor(r*n + 1/2)
  * indices to out[0..k-1] (out holds n_heads entries). Returns k, or -1 on bad arguments. */

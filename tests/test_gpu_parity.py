@@ -275,6 +275,48 @@ def test_var_score_identical_sequences(S):
     assert np.all(s_var.cpu().numpy() < 1e-12)
 
 
+def _check_kl(S, C, heads=None):
+    """Forward-KL selector: A_hat as for Eq. (1); s^KL within 1e-3 relative + 2e-5 absolute.
+    The kernel forms s^KL per entry as (1/N) sum_n A log A - A_hat log A_hat, two float32
+    sums of size ~T·H(row) per head whose difference is the score; their rounding bounds
+    the absolute part."""
+    scale = 1.0 / math.sqrt(C["D"])
+    a_hat, s_kl, rank = S.kl_score(up(C["q"], "bf16"), up(C["k"], "bf16"))
+    torch.cuda.synchronize()
+    a_hat, s_kl, rank = a_hat.cpu().numpy(), s_kl.cpu().numpy(), rank.cpu().numpy()
+    heads = range(C["H"]) if heads is None else heads
+    ref = {}
+    for h in heads:
+        A_hat, sk, _ = saf_oracle.kl_score(C["q"][:, h:h + 1], C["k"][:, h:h + 1], scale)
+        assert np.max(np.abs(a_hat[h] - A_hat[0])) <= 1e-5, h
+        assert abs(s_kl[h] - sk[0]) <= 1e-3 * sk[0] + 2e-5, (h, s_kl[h], sk[0])
+        ref[h] = sk[0]
+    assert list(rank) == list(np.argsort(s_kl, kind="stable"))
+    return ref, s_kl, rank
+
+
+def test_kl_score_small(S):
+    C = inputs.make_calibration(6, 4, 200, 64, seed=24)
+    ref, s_kl, rank = _check_kl(S, C)
+    gaps = np.diff(sorted(ref.values()))
+    if np.all(gaps > 4e-5):   # well separated: the ranking must match the oracle's
+        assert list(rank) == list(saf_oracle.rank_heads([ref[h] for h in range(4)]))
+
+
+def test_kl_score_d128_ragged(S):
+    C = inputs.make_calibration(3, 2, 67, 128, seed=25)
+    _check_kl(S, C)
+
+
+def test_kl_score_identical_sequences(S):
+    C = inputs.make_calibration(2, 3, 96, 64, seed=26)
+    for key in ("q", "k"):
+        C[key] = np.repeat(C[key][:1], 4, axis=0)
+    C["N"] = 4
+    a_hat, s_kl, rank = S.kl_score(up(C["q"], "bf16"), up(C["k"], "bf16"))
+    assert np.all(np.abs(s_kl.cpu().numpy()) < 2e-5)
+
+
 # ---------------------------------------------------------------- full-size workloads, sampled
 
 def _full(S, name, heads, bwd=True, n_frozen=None):
@@ -369,3 +411,9 @@ def test_full_calibration_sampled(S):
     # sharper heads (small temperature) score higher: the sampled order must agree
     order = sorted(heads, key=lambda h: ref[h])
     assert [h for h in rank if h in heads] == order
+
+
+def test_full_calibration_kl_sampled(S):
+    C = inputs.make_calibration(**inputs.CALIBRATION)
+    tau = C["tau"]
+    _check_kl(S, C, heads=[int(np.argmin(tau)), int(np.argmax(tau))])
