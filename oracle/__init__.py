@@ -8,4 +8,4 @@ pattern (its own pins: tests/oracle_pins_fit.py).
 """
 from .saf_oracle import (attn_bwd, attn_fwd, causal_mask, dynamic_probs, frozen_probs,  # noqa: F401
                          kl_score, kl_score_of, mean_attention, n_selected, rank_heads,
-                         reconstruction_risk, select_heads, var_score, variance_score)
+                         reconstruction_risk, select_heads, sharp_mean, var_score, variance_score)

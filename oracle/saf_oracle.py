@@ -225,6 +225,22 @@ def kl_score(q, k, scale: float):
     return A_hat, s_kl, rank_heads(s_kl)
 
 
+def sharp_mean(q, k, scale: float):
+    """The "sharp mean" candidate pattern of part 二.2: average the logits over the N
+    calibration sequences first, then take the causal softmax,
+        P_sharp = softmax_causal((1/N) sum_n scale Q_n K_n^T),
+    for every head. q, k: [N,H,T,D]. Returns P_sharp [H,T,T] (zeros above the diagonal)."""
+    q, k = _f64(q), _f64(k)
+    N, H, T, _ = q.shape
+    out = np.empty((H, T, T))
+    for h in range(H):
+        S = sum(scale * (q[n, h] @ k[n, h].T) for n in range(N)) / N
+        S = np.where(causal_mask(T), S, -np.inf)
+        E = np.exp(S - S.max(axis=1, keepdims=True))
+        out[h] = E / E.sum(axis=1, keepdims=True)
+    return out
+
+
 def rank_heads(s_var):
     """Head indices sorted by ascending s_var, stable (lower index first on ties)."""
     return np.argsort(np.asarray(s_var), kind="stable").astype(np.int32)

@@ -333,6 +333,32 @@ def pin_kl_score_closed_forms(orc):
     assert abs(s_kl - ref) < 1e-14 and s_kl > 0
 
 
+def pin_sharp_mean(orc):
+    """Sharp mean (part 二.2): one sequence gives that sequence's attention; the logits are
+    averaged before the softmax (pure-Python evaluation at T = 4 with two sequences); it
+    differs from the probability mean A-hat when the sequences differ."""
+    r = _rng(32)
+    N, H, T, D = 2, 2, 4, 3
+    q, k = r.standard_normal((N, H, T, D)), r.standard_normal((N, H, T, D))
+    scale = 0.6
+    P = orc.sharp_mean(q, k, scale)
+    for h in range(H):
+        for i in range(T):
+            logits = [sum(scale * sum(q[n, h, i, d] * k[n, h, j, d] for d in range(D)) for n in range(N)) / N
+                      for j in range(i + 1)]
+            mx = max(logits)
+            w = [math.exp(x - mx) for x in logits]
+            for j in range(T):
+                want = w[j] / sum(w) if j <= i else 0.0
+                assert abs(P[h, i, j] - want) < 1e-14
+    one = orc.sharp_mean(q[:1], k[:1], scale)
+    for h in range(H):
+        A, _ = orc.dynamic_probs(q[0, h], k[0, h], scale)
+        assert np.max(np.abs(one[h] - A)) < 1e-15
+    A_hat, _, _ = orc.var_score(q, k, scale)
+    assert np.max(np.abs(A_hat - P)) > 1e-3
+
+
 def pin_mean_optimality(orc):
     """Appendix B.1: R_N(P) = R_N(A-hat) + ||P - A-hat||_F^2 / T^2 for any fixed P, and the
     minimum R_N(A-hat) equals (N-1)/N s_var."""

@@ -163,6 +163,10 @@ def _kl_by_t2(A_stack):
     return val / np.shape(A_stack)[1], A_hat
 
 
+def _sharp_prob_mean(q, k, scale):
+    return so.var_score(q, k, scale)[0]
+
+
 def _rank_desc(s):
     return np.argsort(-np.asarray(s), kind="stable").astype(np.int32)
 
@@ -188,6 +192,7 @@ MUTANTS = {
     "rank: descending": ("rank_heads", _rank_desc),
     "kl: reverse direction KL(A-hat || A)": ("kl_score_of", _kl_reverse),
     "kl: divides by N T^2": ("kl_score_of", _kl_by_t2),
+    "sharp mean: probabilities averaged instead of logits": ("sharp_mean", _sharp_prob_mean),
 }
 
 
