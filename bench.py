@@ -388,11 +388,20 @@ def calibration(torch, inputs, profiling, saf, steps, warmup):
     e1.record(st)
     torch.cuda.synchronize()
     kl_ms = e0.elapsed_time(e1) / steps
+    # the sharp-mean candidate pattern (saf_sharp_mean), written over a_hat's buffer
+    saf.sharp_mean(q, k, out=a_hat)
+    torch.cuda.synchronize()
+    e0.record(st)
+    for _ in range(steps):
+        saf.sharp_mean(q, k, out=a_hat)
+    e1.record(st)
+    torch.cuda.synchronize()
+    sharp_ms = e0.elapsed_time(e1) / steps
     samples = N * H * causal_pairs(T)
     wf = WELFORD_FLOP_PER_SAMPLE * samples / (kern["var_welford"] * 1e-3) / 1e12
     return {
         "workload": f"calibration: N={N} H={H} T={T} D={D} bf16, tau in [0.1, 4]",
-        "ms": ms, "sample_pairs_per_s": samples / (ms * 1e-3), "kernels_ms": kern, "kl_score_ms": kl_ms,
+        "ms": ms, "sample_pairs_per_s": samples / (ms * 1e-3), "kernels_ms": kern, "kl_score_ms": kl_ms, "sharp_mean_ms": sharp_ms,
         "ranking": [int(x) for x in rank.cpu().numpy()],
         "roofline": {"kernel": "var_welford", "bound": "alu", "achieved": wf, "peak": PEAK_FP32_VALU_TFLOPS,
                      "unit": "TFLOP/s", "frac": wf / PEAK_FP32_VALU_TFLOPS,

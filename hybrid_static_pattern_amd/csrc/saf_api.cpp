@@ -274,6 +274,18 @@ saf_status saf_kl_score(const saf_var_desc* desc, const void* q, const void* k, 
   return SAF_OK;
 }
 
+saf_status saf_sharp_mean(const saf_var_desc* desc, const void* q, const void* k, float* p_sharp, void* stream) {
+  saf::VarArgs a;
+  SAF_TRY(validate_var(desc, &a));
+  SAF_TRY(check_ptr(q, true, "q"));
+  SAF_TRY(check_ptr(k, true, "k"));
+  SAF_TRY(check_ptr(p_sharp, true, "p_sharp"));
+  (void)hipGetLastError();
+  hipError_t e = saf::launch_sharp_mean(a, q, k, p_sharp, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "sharp_mean launch");
+  return SAF_OK;
+}
+
 int32_t saf_select_heads(const double* s_var_all, int32_t n_heads, double r, int32_t* out) {
   if (!s_var_all || !out || n_heads < 1 || !(r >= 0.0 && r <= 1.0)) {
     fail(SAF_EINVAL, "saf_select_heads: bad arguments");

@@ -74,6 +74,8 @@ size_t var_workspace_bytes(const VarArgs& a);
 // (same A_hat, the score written to s_var and ranked).
 hipError_t launch_var_score(const VarArgs& a, const void* q, const void* k, float* a_hat,
                             double* s_var, int32_t* rank, void* ws, hipStream_t s, bool kl);
+// Sharp mean pattern [H, T, T] float32 (no workspace).
+hipError_t launch_sharp_mean(const VarArgs& a, const void* q, const void* k, float* out, hipStream_t s);
 
 // Compact pattern fit.
 struct FitArgs {

@@ -33,6 +33,7 @@ struct VarParams {
   int32_t* rank;
   int N, H, T;
   float c;          // scale * log2(e)
+  float scale_n;    // scale / N (sharp mean)
   int n_it, n_jt;
 };
 
@@ -263,6 +264,73 @@ __global__ __launch_bounds__(256) void var_final_kernel(const VarParams p) {
   }
 }
 
+// Sharp mean (part 二.2): the logits are averaged over the N sequences first,
+// P_sharp = softmax_causal((1/N) sum_n scale Q_n K_n^T). sharp_logits_kernel accumulates the
+// S^T tile of every n in the same MFMA accumulators (K-dimension N D) and writes the mean
+// logits of the tile's causal entries into `out`; sharp_rows_kernel then turns each row into
+// its causal softmax in place and writes the zeros above the diagonal.
+template <int D>
+__global__ __launch_bounds__(NTH, 2) void sharp_logits_kernel(const VarParams p, float* out) {
+  __shared__ __attribute__((aligned(16))) KTile<D> stg[2];
+  const int jt = blockIdx.x % p.n_jt;
+  const int it = (blockIdx.x / p.n_jt) % p.n_it;
+  const int h = blockIdx.x / (p.n_jt * p.n_it);
+  const int lane = lane_id(), w = wave_id(), m = lane & 31, hh = lane >> 5;
+  const int T = p.T;
+  const int i0 = it * BM, i0w = i0 + 32 * w, i = i0w + m, j0 = jt * BN;
+  if (j0 > i0 + BM - 1) return;   // above the diagonal: written by the row kernel
+  const bool active = j0 <= i0w;
+  const size_t nh_stride = (size_t)p.H * T;
+  uint32_t koff[D / 16];
+  key_offsets<D>(m, hh, koff);
+  load_k<D>(p.k + ((size_t)h * T) * D, j0, T, stg[0]);
+  wait_vm0();
+  __syncthreads();
+  f32x16 acc[2] = {f32x16{}, f32x16{}};
+  for (int n = 0; n < p.N; ++n) {
+    const size_t head = (size_t)n * nh_stride + (size_t)h * T;
+    if (n + 1 < p.N) load_k<D>(p.k + (head + nh_stride) * D, j0, T, stg[(n + 1) & 1]);
+    if (active) {
+      bf16x8 qf[D / 16];
+      load_q<D>(p.q + head * D, i, T, hh, qf);
+      pipelined<D / 8>([&](int x) { return lds_row<D / 8>(stg[n & 1].k, (x & 1) * 32, koff[x >> 1]); },
+                       [&](int x, const bf16x8& a) { acc[x & 1] = mfma32(a, qf[x >> 1], acc[x & 1]); });
+    }
+    wait_vm0();
+    __syncthreads();
+  }
+  if (!active || i >= T) return;
+  const float f = p.scale_n;
+  float* row = out + ((size_t)h * T + i) * T;
+#pragma unroll
+  for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+    for (int sk = 0; sk < 2; ++sk) {
+      const int jj = j0 + kb * 32 + sk * 16 + hh * 8;
+#pragma unroll
+      for (int e = 0; e < 8; ++e)
+        if (jj + e <= i) row[jj + e] = acc[kb][sk * 8 + e] * f;
+    }
+}
+
+// one wave per row i: max and sum over j <= i of the mean logits, then the row in place
+__global__ __launch_bounds__(256) void sharp_rows_kernel(int H, int T, float* out) {
+  const int lane = threadIdx.x & 63;
+  const int i = blockIdx.x * 4 + (threadIdx.x >> 6), h = blockIdx.y;
+  if (i >= T) return;
+  float* row = out + ((size_t)h * T + i) * T;
+  float mx = -__builtin_huge_valf();
+  for (int j = lane; j <= i; j += 64) mx = fmaxf(mx, row[j]);
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) mx = fmaxf(mx, __shfl_xor(mx, o, 64));
+  float sum = 0.f;
+  for (int j = lane; j <= i; j += 64) sum += __builtin_amdgcn_exp2f((row[j] - mx) * kLog2e);
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) sum += __shfl_xor(sum, o, 64);
+  const float inv = 1.f / sum;
+  for (int j = lane; j < T; j += 64) row[j] = j <= i ? __builtin_amdgcn_exp2f((row[j] - mx) * kLog2e) * inv : 0.f;
+}
+
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 }  // namespace
@@ -270,6 +338,30 @@ size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 size_t var_workspace_bytes(const VarArgs& a) {
   const size_t n_it = (a.T + BM - 1) / BM, n_jt = (a.T + BN - 1) / BN;
   return align256((size_t)a.N * a.H * a.T * sizeof(float)) + align256((size_t)a.H * n_it * n_jt * sizeof(float));
+}
+
+hipError_t launch_sharp_mean(const VarArgs& a, const void* q, const void* k, float* out, hipStream_t s) {
+  VarParams p{};
+  p.q = static_cast<const bf16*>(q);
+  p.k = static_cast<const bf16*>(k);
+  p.N = a.N;
+  p.H = a.H;
+  p.T = a.T;
+  p.scale_n = a.scale / (float)a.N;
+  p.n_it = (a.T + BM - 1) / BM;
+  p.n_jt = (a.T + BN - 1) / BN;
+  prof_begin("sharp_logits", s);
+  if (a.D == 64)
+    hipLaunchKernelGGL(sharp_logits_kernel<64>, dim3(p.n_jt * p.n_it * a.H), dim3(NTH), 0, s, p, out);
+  else
+    hipLaunchKernelGGL(sharp_logits_kernel<128>, dim3(p.n_jt * p.n_it * a.H), dim3(NTH), 0, s, p, out);
+  prof_end(s);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  prof_begin("sharp_rows", s);
+  hipLaunchKernelGGL(sharp_rows_kernel, dim3((a.T + 3) / 4, a.H), dim3(256), 0, s, a.H, a.T, out);
+  prof_end(s);
+  return hipGetLastError();
 }
 
 hipError_t launch_var_score(const VarArgs& a, const void* q, const void* k, float* a_hat,

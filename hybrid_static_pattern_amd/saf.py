@@ -24,7 +24,7 @@ EXPORTS = (
     "saf_attn_fwd", "saf_attn_workspace_size", "saf_attn_bwd", "saf_var_workspace_size",
     "saf_var_score", "saf_select_heads", "saf_status_string", "saf_last_error",
     "saf_prof_enable", "saf_prof_read", "saf_pattern_stats", "saf_compact_marginals",
-    "saf_fit_workspace_size", "saf_compact_fit", "saf_select_fitted", "saf_kl_score",
+    "saf_fit_workspace_size", "saf_compact_fit", "saf_select_fitted", "saf_kl_score", "saf_sharp_mean",
 )
 
 
@@ -82,6 +82,7 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.saf_var_workspace_size.restype = sz
     lib.saf_var_score.argtypes = [pv, vp, vp, vp, vp, vp, vp, sz, vp]
     lib.saf_kl_score.argtypes = [pv, vp, vp, vp, vp, vp, vp, sz, vp]
+    lib.saf_sharp_mean.argtypes = [pv, vp, vp, vp, vp]
     lib.saf_select_heads.argtypes = [ctypes.POINTER(ctypes.c_double), i32, ctypes.c_double, ctypes.POINTER(i32)]
     lib.saf_select_heads.restype = i32
     lib.saf_status_string.argtypes = [ctypes.c_int]
@@ -99,7 +100,8 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.saf_select_fitted.argtypes = [ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_float), i32,
                                       ctypes.c_double, ctypes.c_float, ctypes.POINTER(i32)]
     lib.saf_select_fitted.restype = i32
-    for fn in ("saf_attn_fwd", "saf_attn_bwd", "saf_var_score", "saf_kl_score", "saf_prof_enable", "saf_pattern_stats",
+    for fn in ("saf_attn_fwd", "saf_attn_bwd", "saf_var_score", "saf_kl_score", "saf_sharp_mean",
+               "saf_prof_enable", "saf_pattern_stats",
                "saf_compact_marginals", "saf_compact_fit"):
         getattr(lib, fn).restype = ctypes.c_int
     _lib = lib
@@ -253,6 +255,21 @@ def kl_score(q, k, scale=None, a_hat=None, s_kl=None, rank=None, workspace=None)
     """Forward-KL selector (saf_kl_score), arguments as var_score. Returns (a_hat, s_kl [H]
     float64, rank [H] int32 by ascending s_kl)."""
     return _score(load().saf_kl_score, q, k, scale, a_hat, s_kl, rank, workspace)
+
+
+def sharp_mean(q, k, scale=None, out=None):
+    """Sharp-mean pattern (saf_sharp_mean). q, k: [N,H,T,D] bf16 device tensors. Returns
+    p_sharp [H,T,T] float32 on the device."""
+    lib = load()
+    N, H, T, D = q.shape
+    _need(q, "q", dtype=torch.bfloat16)
+    _need(k, "k", shape=(N, H, T, D), dtype=q.dtype, device=q.device)
+    _need(out, "out", shape=(H, T, T), dtype=torch.float32, device=q.device)
+    if out is None:
+        out = torch.empty((H, T, T), dtype=torch.float32, device=q.device)
+    desc = VarDesc(N, H, T, D, _io_dtype(q), float(scale if scale is not None else 1.0 / math.sqrt(D)))
+    _check(lib.saf_sharp_mean(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(out), _stream(q)))
+    return out
 
 
 def _score(entry, q, k, scale, a_hat, s_var, rank, workspace):

@@ -137,6 +137,14 @@ saf_status saf_kl_score(const saf_var_desc* desc, const void* q, const void* k, 
                         double* s_kl, int32_t* rank, void* workspace, size_t ws_bytes,
                         void* stream);
 
+/* The "sharp mean" candidate pattern of part 二.2 (the notes compare it with the
+ * probability mean a_hat): logits averaged over the N sequences, then the causal softmax,
+ *   p_sharp[h] = softmax_causal((1/N) sum_n scale Q_n K_n^T),
+ * written as [H, T, T] float32 with zeros above the diagonal. Arguments as for
+ * saf_var_score; no workspace. */
+saf_status saf_sharp_mean(const saf_var_desc* desc, const void* q, const void* k,
+                          float* p_sharp, void* stream);
+
 /* Host-only selection across layers (part 二.1): sorts n_heads scores (all L*H heads of a
  * model) ascending, ties to the lower index, and writes the first k = floor(r*n + 1/2)
  * indices to out[0..k-1] (out holds n_heads entries). Returns k, or -1 on bad arguments. */

@@ -317,6 +317,32 @@ def test_kl_score_identical_sequences(S):
     assert np.all(np.abs(s_kl.cpu().numpy()) < 2e-5)
 
 
+def _check_sharp(S, C, heads=None):
+    """Sharp mean: the mean logits accumulate N D bf16 products in float32 (relative rounding
+    ~1e-6 of the logits), so the pattern is held to 2e-5 absolute per entry."""
+    scale = 1.0 / math.sqrt(C["D"])
+    P = S.sharp_mean(up(C["q"], "bf16"), up(C["k"], "bf16"))
+    torch.cuda.synchronize()
+    P = P.cpu().numpy()
+    for h in (range(C["H"]) if heads is None else heads):
+        ref = saf_oracle.sharp_mean(C["q"][:, h:h + 1], C["k"][:, h:h + 1], scale)[0]
+        err = np.abs(P[h] - ref).max()
+        assert err <= 2e-5, (h, err)
+
+
+def test_sharp_mean_small(S):
+    _check_sharp(S, inputs.make_calibration(6, 4, 200, 64, seed=27))
+
+
+def test_sharp_mean_d128_ragged(S):
+    _check_sharp(S, inputs.make_calibration(3, 2, 67, 128, seed=28))
+
+
+def test_full_calibration_sharp_sampled(S):
+    C = inputs.make_calibration(**inputs.CALIBRATION)
+    _check_sharp(S, C, heads=[int(np.argmin(C["tau"])), int(np.argmax(C["tau"]))])
+
+
 # ---------------------------------------------------------------- full-size workloads, sampled
 
 def _full(S, name, heads, bwd=True, n_frozen=None):
