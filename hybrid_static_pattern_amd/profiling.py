@@ -1,9 +1,16 @@
-"""Turns rocprofv3 counter dumps into the HBM-traffic summaries kept under profiles/.
+"""Turns rocprofv3 output into the summaries kept under profiles/.
 
     python -m hybrid_static_pattern_amd.profiling traffic \
         --fetch gpurun_out/pmc_C/run_counter_collection.csv \
         --write gpurun_out/pmc_D/run_counter_collection.csv \
         --copy-mib 256 --command "<the rocprofv3 command lines>" --out profiles/
+
+    python -m hybrid_static_pattern_amd.profiling trace \
+        --stats gpurun_out/trace/run_kernel_stats.csv --title "..." --command "..." \
+        --out profiles/kernels_<workload>.md
+
+The trace summary is the kernel statistics table of `rocprofv3 --kernel-trace --stats`
+(calls, average / min / max microseconds, share of the total), one row per kernel.
 
 FETCH_SIZE and WRITE_SIZE are read per dispatch (KiB) for every libsaf kernel and scaled by
 the factor that makes the same counters match a plain elementwise copy of known size (the
@@ -120,9 +127,44 @@ def read_summary(kernel: str, outdir: str):
     return {k: (v if k == "source_hash" else float(v)) for k, v in d.items()}
 
 
+def pretty_kernel(full: str) -> str:
+    """Short, readable kernel name: namespaces and argument lists dropped, template kept."""
+    if "at::native" in full:
+        return "torch elementwise (setup)"
+    name = full.replace("void ", "").replace("saf::(anonymous namespace)::", "")
+    depth, out = 0, []
+    for ch in name:   # drop the parameter list (the outermost parentheses)
+        if ch == "(" and depth == 0 and out and out[-1] != "<":
+            break
+        depth += ch == "<"
+        depth -= ch == ">"
+        out.append(ch)
+    return "".join(out).strip()
+
+
+def trace_summary(stats_csv: str, title: str, command: str) -> str:
+    rows = []
+    with open(stats_csv) as f:
+        for r in csv.DictReader(f):
+            rows.append((pretty_kernel(r["Name"]), int(r["Calls"]), float(r["AverageNs"]) / 1e3,
+                         float(r["MinNs"]) / 1e3, float(r["MaxNs"]) / 1e3, float(r["Percentage"])))
+    rows.sort(key=lambda x: -x[5])
+    lines = [f"# Kernel trace: {title}", "", "Command (repository root R on the MI355X box):", "", "```",
+             command, "```", "", "rocprofv3 kernel statistics (`run_kernel_stats.csv`):", "",
+             "| kernel | calls | average us | min us | max us | share |", "|---|---|---|---|---|---|"]
+    for name, calls, avg, mn, mx, pct in rows:
+        lines.append(f"| {name} | {calls} | {avg:.1f} | {mn:.1f} | {mx:.1f} | {pct:.1f}% |")
+    return "\n".join(lines) + "\n"
+
+
 def main():
     ap = argparse.ArgumentParser()
     sub = ap.add_subparsers(dest="cmd", required=True)
+    tr = sub.add_parser("trace")
+    tr.add_argument("--stats", required=True)
+    tr.add_argument("--title", required=True)
+    tr.add_argument("--command", default="")
+    tr.add_argument("--out", required=True)
     t = sub.add_parser("traffic")
     t.add_argument("--fetch", required=True)
     t.add_argument("--write", required=True)
@@ -130,6 +172,11 @@ def main():
     t.add_argument("--command", default="")
     t.add_argument("--out", default=os.path.join(os.path.dirname(PKG), "profiles"))
     a = ap.parse_args()
+    if a.cmd == "trace":
+        with open(a.out, "w") as f:
+            f.write(trace_summary(a.stats, a.title, a.command))
+        print(f"wrote {a.out}")
+        return
     data = traffic(a.fetch, a.write, a.copy_mib)
     write_summaries(data, a.out, a.command)
     for k, d in data.items():
