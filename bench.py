@@ -276,8 +276,9 @@ def prefill(torch, inputs, saf, steps, warmup):
             torch.cuda.synchronize()
             ms = e0.elapsed_time(e1) / steps
             nf = int(m.sum())
-            res[f"r{round(100 * nf / H)}"] = {"ms": ms, "tokens_per_s": B * T / (ms * 1e-3),
-                                               "tflops": (4 * (H - nf) + 2 * nf) * B * D * causal_pairs(T) / (ms * 1e-3) / 1e12}
+            tf = (4 * (H - nf) + 2 * nf) * B * D * causal_pairs(T) / (ms * 1e-3) / 1e12
+            res[f"r{round(100 * nf / H)}"] = {"ms": ms, "tokens_per_s": B * T / (ms * 1e-3), "tflops": tf,
+                                               "mfma_frac": tf / PEAK_BF16_TFLOPS}
         for key in list(res):
             if key != "r0":
                 res[key]["speedup_vs_r0"] = res["r0"]["ms"] / res[key]["ms"]
@@ -340,6 +341,11 @@ def gqa(torch, inputs, saf, steps, warmup):
             recs = saf.prof_read()
             saf.prof_enable(False)
             res[key]["kernels_ms"] = {n: t for n, t in recs}
+            kf = kernel_flops(B, T, D, H - nf, nf)
+            dk = res[key]["kernels_ms"]["dkdv"]
+            res[key]["roofline"] = {"kernel": "dkdv", "bound": "mfma", "achieved": kf["dkdv"] / (dk * 1e-3) / 1e12,
+                                    "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                                    "frac": kf["dkdv"] / (dk * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, "traffic": None}
     for key in res:
         if key != "r0":
             res[key]["speedup_vs_r0"] = res["r0"]["ms_per_step"] / res[key]["ms_per_step"]
