@@ -29,9 +29,11 @@ namespace {
 
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kNegInf = -INFINITY;
-constexpr int FW = 4;      // waves per workgroup in the per-line kernels
+constexpr int LW = 16;     // waves per workgroup in the per-line kernels
+constexpr int OPW = 2;     // outputs (rows, columns or distances) per wave in the per-line kernels
 constexpr int SW = 16;     // waves per workgroup in the statistics kernel
-constexpr int U = 16;      // keys (or terms) per lane loaded before use in the per-line kernels
+constexpr int C = 2048;    // keys (or terms) per LDS chunk in the per-line kernels
+constexpr int U = 8;       // keys (or terms) per lane read before use in the per-line kernels
 
 __device__ __forceinline__ float wave_max(float x) {
 #pragma unroll
@@ -83,38 +85,72 @@ __global__ __launch_bounds__(64 * SW) void stats_kernel(int T, const float* __re
   }
 }
 
-// log Z(i) = log sum_{j<=i} exp(alpha(j) + rho(i-j)) for row i = FW blockIdx.x + wave.
-// The row is taken in chunks of 64 U keys: each lane first loads its U logits of the chunk
-// (U independent loads in flight, instead of one round trip per key), then the chunk's max
-// over the wave raises the running shift and the lane's partial sum is rescaled once.
-__global__ __launch_bounds__(64 * FW) void logz_kernel(int T, const float* __restrict__ alpha,
+// log Z(i) = log sum_{j<=i} exp(alpha(j) + rho(i-j)) for the OPW LW rows of a block, OPW per
+// wave (rows i0 + w + LW r). The rows share their keys: chunks of C keys of alpha, and the
+// window of rho the rows need for them (C + OPW LW - 1 distances), are staged in LDS once for
+// the block. Each lane keeps its own running max and sum over the keys it takes (64 U at a
+// time, U logits read before use, one rescale per group), and the lanes are combined once at
+// the end, so a row costs two cross-lane reductions whatever its length.
+__global__ __launch_bounds__(64 * LW) void logz_kernel(int T, const float* __restrict__ alpha,
                                                        const float* __restrict__ rho,
                                                        float* __restrict__ logz) {
-  const int h = blockIdx.y, lane = threadIdx.x & 63;
-  const int i = blockIdx.x * FW + (threadIdx.x >> 6);
-  if (i >= T) return;
+  constexpr int NR = OPW * LW;   // rows per block
+  __shared__ float sal[C];
+  __shared__ float srh[C + NR];
+  const int h = blockIdx.y, lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int i0 = blockIdx.x * NR;
+  const int i_last = min(i0 + NR, T) - 1;
   const float* al = alpha + (size_t)h * T;
   const float* rh = rho + (size_t)h * T;
-  float mx = kNegInf, s = 0.f;
-  for (int j0 = 0; j0 <= i; j0 += 64 * U) {
-    float x[U];
+  float mx[OPW], s[OPW];
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const int j = j0 + 64 * u + lane;
-      x[u] = j <= i ? al[j] + rh[i - j] : kNegInf;
-    }
-    float cm = x[0];
-#pragma unroll
-    for (int u = 1; u < U; ++u) cm = fmaxf(cm, x[u]);
-    const float m_new = fmaxf(mx, wave_max(cm));   // finite: key j0 <= i is in the chunk
-    float cs = 0.f;
-#pragma unroll
-    for (int u = 0; u < U; ++u) cs += __builtin_amdgcn_exp2f((x[u] - m_new) * kLog2e);
-    s = s * __builtin_amdgcn_exp2f((mx - m_new) * kLog2e) + cs;
-    mx = m_new;
+  for (int r = 0; r < OPW; ++r) {
+    mx[r] = kNegInf;
+    s[r] = 0.f;
   }
-  s = wave_sum(s);
-  if (lane == 0) logz[(size_t)h * T + i] = mx + logf(s);
+  for (int j0 = 0; j0 <= i_last; j0 += C) {
+    __syncthreads();   // the previous chunk is no longer read
+    // sal[y] = alpha(j0 + y); srh[y] = rho(d) with d = i0 - j0 - C + 1 + y, so that row i and
+    // key j read srh[(i - i0) + C - 1 - (j - j0)]
+    for (int y = threadIdx.x; y < C + NR - 1; y += 64 * LW) {
+      if (y < C) sal[y] = (j0 + y <= i_last) ? al[j0 + y] : 0.f;
+      const int d = i0 - j0 - C + 1 + y;
+      srh[y] = (d >= 0 && d < T) ? rh[d] : 0.f;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int r = 0; r < OPW; ++r) {
+      const int i = i0 + w + LW * r;
+      if (i > i_last) continue;
+      const float* rw = srh + (i - i0) + C - 1;
+      for (int k0 = 0; k0 < C && j0 + k0 <= i; k0 += 64 * U) {
+        float x[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+          const int k = k0 + 64 * u + lane;   // key j0 + k
+          x[u] = j0 + k <= i ? sal[k] + rw[-k] : kNegInf;
+        }
+        float cm = x[0];
+#pragma unroll
+        for (int u = 1; u < U; ++u) cm = fmaxf(cm, x[u]);
+        if (cm == kNegInf) continue;   // no key of this group for this lane
+        const float m_new = fmaxf(mx[r], cm);
+        float cs = 0.f;
+#pragma unroll
+        for (int u = 0; u < U; ++u) cs += __builtin_amdgcn_exp2f((x[u] - m_new) * kLog2e);
+        s[r] = s[r] * __builtin_amdgcn_exp2f((mx[r] - m_new) * kLog2e) + cs;
+        mx[r] = m_new;
+      }
+    }
+  }
+#pragma unroll
+  for (int r = 0; r < OPW; ++r) {
+    const int i = i0 + w + LW * r;
+    if (i > i_last) continue;
+    const float m_row = wave_max(mx[r]);   // finite: lane 0 holds key 0
+    const float sr = wave_sum(mx[r] == kNegInf ? 0.f : s[r] * __builtin_amdgcn_exp2f((mx[r] - m_row) * kLog2e));
+    if (lane == 0) logz[(size_t)h * T + i] = m_row + logf(sr);
+  }
 }
 
 struct AdamStep {
@@ -123,14 +159,17 @@ struct AdamStep {
   float inv_t;         // 1 / T
 };
 
-// Marginals of P for outputs o = FW blockIdx.x + wave in [0, 2T): o < T is column x = o
-// (own = alpha(x), other = rho), o >= T is distance x = o - T (own = rho(x), other = alpha).
-// Both are S(x) = sum_{t=0}^{T-1-x} exp(other(t) + own(x) - log Z(x + t)).
-// ADAM = false writes S into colP / distP. ADAM = true takes one Adam step on own(x) with
-// gradient (S - target(x)) / T and writes the new value to the other parameter buffer (the
-// current values are still being read by other waves); m and v are [H, 2T].
+// Marginals of P. Blocks [0, nb) take columns x (own = alpha(x), other = rho), blocks
+// [nb, 2 nb) distances x (own = rho(x), other = alpha), OPW LW consecutive x per block, OPW
+// per wave (x0 + w + LW r). Both are S(x) = sum_{t=0}^{T-1-x} exp(other(t) + own(x) - log Z(x + t));
+// chunks of C values of `other` and the C + OPW LW - 1 values of log Z the block's outputs
+// need are staged in LDS once for the block. ADAM = false writes S into colP / distP.
+// ADAM = true takes one Adam step on own(x) with gradient (S - target(x)) / T and writes the
+// new value to the other parameter buffer (the current values are still being read by other
+// blocks); m and v are [H, 2T], the alpha part first. Adam's operands are read before the
+// sums so that their latency overlaps the staging.
 template <bool ADAM>
-__global__ __launch_bounds__(64 * FW) void marg_kernel(int T, const float* __restrict__ alpha,
+__global__ __launch_bounds__(64 * LW) void marg_kernel(int T, int nb, const float* __restrict__ alpha,
                                                        const float* __restrict__ rho,
                                                        const float* __restrict__ logz,
                                                        float* __restrict__ out_col,    // colP, or new alpha
@@ -139,40 +178,73 @@ __global__ __launch_bounds__(64 * FW) void marg_kernel(int T, const float* __res
                                                        const float* __restrict__ dist,
                                                        float* __restrict__ m, float* __restrict__ v,
                                                        AdamStep st) {
-  const int h = blockIdx.y, lane = threadIdx.x & 63;
-  const int o = blockIdx.x * FW + (threadIdx.x >> 6);
-  if (o >= 2 * T) return;
-  const bool is_col = o < T;
-  const int x = is_col ? o : o - T;
+  constexpr int NX = OPW * LW;   // outputs per block
+  __shared__ float soth[C];
+  __shared__ float slz[C + NX];
+  const int h = blockIdx.y, lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const bool is_col = (int)blockIdx.x < nb;
+  const int x0 = (is_col ? blockIdx.x : blockIdx.x - nb) * NX;
   const size_t hb = (size_t)h * T;
   const float* own = (is_col ? alpha : rho) + hb;
   const float* oth = (is_col ? rho : alpha) + hb;
-  const float* lz = logz + hb + x;
-  const float ox = own[x];
-  float s = 0.f;
-  for (int t0 = 0; t0 < T - x; t0 += 64 * U) {   // U loads of each array in flight per lane
-    float e[U];
+  const float* lz = logz + hb;
+  float ox[OPW], s[OPW], tg[OPW], mo[OPW], vo[OPW];
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const int t = t0 + 64 * u + lane;
-      e[u] = t < T - x ? oth[t] + ox - lz[t] : kNegInf;
+  for (int r = 0; r < OPW; ++r) {
+    const int x = x0 + w + LW * r;
+    ox[r] = x < T ? own[x] : 0.f;
+    s[r] = 0.f;
+    if constexpr (ADAM) {
+      if (lane == 0 && x < T) {
+        const size_t k = (size_t)h * 2 * T + (is_col ? x : T + x);
+        tg[r] = (is_col ? col : dist)[hb + x];
+        mo[r] = m[k];
+        vo[r] = v[k];
+      }
     }
-#pragma unroll
-    for (int u = 0; u < U; ++u) s += __builtin_amdgcn_exp2f(e[u] * kLog2e);
   }
-  s = wave_sum(s);
-  if (lane != 0) return;
-  float* out = (is_col ? out_col : out_dist) + hb;
-  if constexpr (!ADAM) {
-    out[x] = s;
-  } else {
-    const float g = (s - (is_col ? col : dist)[hb + x]) * st.inv_t;
-    const size_t k = (size_t)h * 2 * T + o;
-    const float mm = st.beta1 * m[k] + (1.f - st.beta1) * g;
-    const float vv = st.beta2 * v[k] + (1.f - st.beta2) * g * g;
-    m[k] = mm;
-    v[k] = vv;
-    out[x] = ox - st.lr * (mm / st.bc1) / (sqrtf(vv / st.bc2) + st.eps);
+  for (int t0 = 0; t0 < T - x0; t0 += C) {
+    __syncthreads();   // the previous chunk is no longer read
+    for (int y = threadIdx.x; y < C + NX - 1; y += 64 * LW) {
+      if (y < C) soth[y] = (t0 + y < T) ? oth[t0 + y] : 0.f;
+      slz[y] = (x0 + t0 + y < T) ? lz[x0 + t0 + y] : 0.f;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int r = 0; r < OPW; ++r) {
+      const int x = x0 + w + LW * r;
+      const float* lw = slz + w + LW * r;   // log Z(x + t) = lw[t - t0]
+      const int n_t = min(C, T - x - t0);   // terms of this chunk for output x
+      for (int k0 = 0; k0 < n_t; k0 += 64 * U) {
+        float e[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+          const int k = k0 + 64 * u + lane;
+          e[u] = k < n_t ? soth[k] + ox[r] - lw[k] : kNegInf;
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u) s[r] += __builtin_amdgcn_exp2f(e[u] * kLog2e);
+      }
+    }
+  }
+#pragma unroll
+  for (int r = 0; r < OPW; ++r) {
+    const int x = x0 + w + LW * r;
+    if (x >= T) continue;
+    const float sum = wave_sum(s[r]);
+    if (lane != 0) continue;
+    float* out = (is_col ? out_col : out_dist) + hb;
+    if constexpr (!ADAM) {
+      out[x] = sum;
+    } else {
+      const float g = (sum - tg[r]) * st.inv_t;
+      const size_t k = (size_t)h * 2 * T + (is_col ? x : T + x);
+      const float mm = st.beta1 * mo[r] + (1.f - st.beta1) * g;
+      const float vv = st.beta2 * vo[r] + (1.f - st.beta2) * g * g;
+      m[k] = mm;
+      v[k] = vv;
+      out[x] = ox[r] - st.lr * (mm / st.bc1) / (sqrtf(vv / st.bc2) + st.eps);
+    }
   }
 }
 
@@ -224,11 +296,12 @@ hipError_t launch_pattern_stats(int H, int T, const float* a, float* col, float*
 
 hipError_t launch_compact_marginals(int H, int T, const float* alpha, const float* rho, float* logz,
                                     float* col_p, float* dist_p, hipStream_t s) {
+  const int nb = (T + OPW * LW - 1) / (OPW * LW);
   prof_begin("fit_logz", s);
-  hipLaunchKernelGGL(logz_kernel, dim3((T + FW - 1) / FW, H), dim3(64 * FW), 0, s, T, alpha, rho, logz);
+  hipLaunchKernelGGL(logz_kernel, dim3(nb, H), dim3(64 * LW), 0, s, T, alpha, rho, logz);
   prof_end(s);
   prof_begin("fit_marginals", s);
-  hipLaunchKernelGGL(marg_kernel<false>, dim3((2 * T + FW - 1) / FW, H), dim3(64 * FW), 0, s, T, alpha,
+  hipLaunchKernelGGL(marg_kernel<false>, dim3(2 * nb, H), dim3(64 * LW), 0, s, T, nb, alpha,
                      rho, (const float*)logz, col_p, dist_p, (const float*)nullptr, (const float*)nullptr,
                      (float*)nullptr, (float*)nullptr, AdamStep{});
   prof_end(s);
@@ -249,7 +322,8 @@ hipError_t launch_compact_fit(const FitArgs& f, const float* col, const float* d
   hipLaunchKernelGGL(fill_kernel, dim3(elementwise_blocks(4 * n)), dim3(256), 0, s, m, 4 * n, 0.f);
   float* cur[2] = {alpha, rho};
   float* nxt[2] = {alt_alpha, alt_rho};
-  const dim3 lz_grid((T + FW - 1) / FW, H), mg_grid((2 * T + FW - 1) / FW, H), blk(64 * FW);
+  const int nb = (T + OPW * LW - 1) / (OPW * LW);
+  const dim3 lz_grid(nb, H), mg_grid(2 * nb, H), blk(64 * LW);
   double p1 = 1.0, p2 = 1.0;
   for (int t = 1; t <= f.steps; ++t) {
     p1 *= f.beta1;
@@ -259,7 +333,7 @@ hipError_t launch_compact_fit(const FitArgs& f, const float* col, const float* d
     hipLaunchKernelGGL(logz_kernel, lz_grid, blk, 0, s, T, (const float*)cur[0], (const float*)cur[1], logz);
     prof_end(s);
     prof_begin("fit_adam", s);
-    hipLaunchKernelGGL(marg_kernel<true>, mg_grid, blk, 0, s, T, (const float*)cur[0], (const float*)cur[1],
+    hipLaunchKernelGGL(marg_kernel<true>, mg_grid, blk, 0, s, T, nb, (const float*)cur[0], (const float*)cur[1],
                        (const float*)logz, nxt[0], nxt[1], col, dist, m, v, st);
     prof_end(s);
     std::swap(cur[0], nxt[0]);
