@@ -115,6 +115,16 @@ def test_gqa_forward_backward(S, B, H, H_kv, T, D, frozen, dt):
     compare_layer(L, run(S, L))
 
 
+def test_max_head_count(S):
+    """H = 256, the most heads a layer may have (the head lists are 8-bit), a quarter frozen,
+    with and without shared key/value heads."""
+    fz = [h for h in range(256) if h % 4 == 1]
+    L = inputs.make_layer(1, 256, 65, 64, dtype="bf16", seed=19, frozen_heads=fz)
+    compare_layer(L, run(S, L))
+    L = inputs.make_layer(1, 256, 40, 64, dtype="bf16", seed=20, frozen_heads=fz, kv_heads=32)
+    compare_layer(L, run(S, L))
+
+
 def test_gqa_frozen_query_never_read(S):
     """A frozen head of a shared group reads V of its group but never its own query."""
     L = inputs.make_layer(1, 4, 100, 64, dtype="bf16", seed=18, frozen_heads=[1, 3], kv_heads=2)
