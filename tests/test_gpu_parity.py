@@ -52,10 +52,11 @@ def compare_layer(L, out, bwd=True):
     # the group is the head itself)
     G = len(dyn) // L["v"].shape[1]
     kv_dyn = dyn.reshape(-1, G).any(axis=1)
+    n_dyn = int(dyn.reshape(-1, G).sum(axis=1).max())   # most ordinary heads sharing one K
     if dyn.any():
         check(out["dq"][:, dyn], dq[:, dyn], dt, "dQ")
-        check(out["dk"][:, kv_dyn], dk[:, kv_dyn], dt, "dK")
-    check(out["dv"], dv, dt, "dV")
+        check(out["dk"][:, kv_dyn], dk[:, kv_dyn], dt, "dK", terms=n_dyn)
+    check(out["dv"], dv, dt, "dV", terms=G)
     # dQ of frozen heads and dK of key/value heads without an ordinary query head are never
     # written (NaN sentinels survive)
     assert np.all(np.isnan(out["dq"][:, ~dyn])) and np.all(np.isnan(out["dk"][:, ~kv_dyn]))
@@ -428,11 +429,11 @@ def test_full_gqa_4b_sampled(S):
                                          fz[hs], L["alpha"][hs], L["rho"][hs], scale)
         check(out["o"][:, hs], O, "bf16", f"O group {g}")
         check(out["lse"][:, hs], lse, "bf16", f"lse group {g}", lse=True)
-        check(out["dv"][:, g:g + 1], dv, "bf16", f"dV group {g}")
+        check(out["dv"][:, g:g + 1], dv, "bf16", f"dV group {g}", terms=G)
         dyn = fz[hs] == 0
         if dyn.any():
             check(out["dq"][:, hs][:, dyn], dq[:, dyn], "bf16", f"dQ group {g}")
-            check(out["dk"][:, g:g + 1], dk, "bf16", f"dK group {g}")
+            check(out["dk"][:, g:g + 1], dk, "bf16", f"dK group {g}", terms=int(dyn.sum()))
 
 
 def test_full_prefill_t2048_half_frozen(S):
