@@ -104,6 +104,7 @@ def main():
     ap.add_argument("--no-prefill", action="store_true", help="skip the causal-prefill timings")
     ap.add_argument("--no-fit", action="store_true", help="skip the compact-fit timing")
     ap.add_argument("--no-gqa", action="store_true", help="skip the grouped-query-attention timing")
+    ap.add_argument("--no-l124m", action="store_true", help="skip the 124M-shaped layer timing")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="first run one plain elementwise copy (torch.neg) of this many MiB, a "
                          "known-size reference for the FETCH_SIZE / WRITE_SIZE counters")
@@ -212,6 +213,29 @@ def main():
                              "tflops": layer_flops(B, T, D, H - nf, nf) / (ms2 * 1e-3) / 1e12}
         out["sweep"] = sweep
         out["speedup_vs_r0"] = sweep["r0"]["ms_per_step"] / ms
+    # the frozen path alone: every head of the same layer frozen
+    log("timing the frozen path (every head frozen)")
+    m_all = np.ones(H, np.uint8)
+    ms_f, recs_f = timed(m_all, args.steps, args.warmup, prof=True)
+    kf = {}
+    for name, t in recs_f:
+        kf.setdefault(name, []).append(t)
+    kf = {name: float(np.mean(ts)) for name, ts in kf.items()}
+    bh_td = B * H * T * D
+    fwd_bytes = bh_td * 2 * 2 + B * H * T * 4            # V read, O written (bf16), log Z written
+    bwd_bytes = bh_td * 2 + B * H * T * 4 + bh_td * 4    # dO and log Z read, dV written (fp32)
+    frz_flops = 2 * B * H * D * causal_pairs(T)
+    out["frozen_path"] = {
+        "workload": f"{args.workload} with all {H} heads frozen", "ms_per_step": ms_f, "kernels_ms": kf,
+        "fwd": {"hbm_gb_per_s": fwd_bytes / (kf["hybrid_fwd"] * 1e-3) / 1e9, "bytes": fwd_bytes,
+                "tflops": frz_flops / (kf["hybrid_fwd"] * 1e-3) / 1e12},
+        "bwd": {"hbm_gb_per_s": bwd_bytes / (kf["dkdv"] * 1e-3) / 1e9, "bytes": bwd_bytes,
+                "tflops": frz_flops / (kf["dkdv"] * 1e-3) / 1e12},
+        "speedup_vs_r0": (out["sweep"]["r0"]["ms_per_step"] / ms_f) if "sweep" in out else None,
+    }
+    if not args.no_l124m:
+        log("timing the 124M-shaped layer")
+        out["l124m"] = l124m(torch, inputs, saf, args.steps, args.warmup)
     if not args.no_calibration:
         log("timing the calibration score")
         out["calibration"] = calibration(torch, inputs, profiling, saf, args.steps, args.warmup)
@@ -290,6 +314,54 @@ def prefill(torch, inputs, saf, steps, warmup):
         out["by_T"][str(T)] = run(P["B"], T, P["seed"] + T)
     s = P["single"]
     out["single"] = {"B": s["B"], "T": s["T"], **run(s["B"], s["T"], P["seed"])}
+    return out
+
+
+def l124m(torch, inputs, saf, steps, warmup):
+    """The 124M-shaped layer (B=8, H=12, T=4096, D=64, bf16): forward alone at r = 25% (the
+    prefill configuration) and forward + backward at r = 25% and r = 0, inputs drawn on the
+    device (seeded N(0, 1) in bf16, alpha / rho from inputs.make_tables, the frozen heads of
+    inputs.WORKLOADS["l124m_fwdbwd"])."""
+    spec = dict(inputs.WORKLOADS["l124m_fwdbwd"])
+    B, H, T, D = spec["B"], spec["H"], spec["T"], spec["D"]
+    dev = torch.device("cuda:0")
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(spec["seed"])
+    q, k, v, do = (torch.randn((B, H, T, D), generator=gen, device=dev).to(torch.bfloat16) for _ in range(4))
+    rng = np.random.default_rng(spec["seed"])
+    alpha, rho = (torch.from_numpy(x).to(dev) for x in inputs.make_tables(rng, H, T))
+    m25 = inputs.choose_frozen(rng, H, spec["n_frozen"])
+    o = torch.empty_like(q)
+    lse = torch.empty((B, H, T), dtype=torch.float32, device=dev)
+    dq, dk, dv = (torch.zeros((B, H, T, D), dtype=torch.float32, device=dev) for _ in range(3))
+    ws = torch.empty(max(saf.attn_workspace_size(v, m25, alpha), 1), dtype=torch.uint8, device=dev)
+
+    def run(mask, bwd):
+        def step():
+            saf.attn_fwd(q, k, v, mask, alpha, rho, o=o, lse=lse)
+            if bwd:
+                saf.attn_bwd(q, k, v, o, do, lse, mask, alpha, rho, dq=dq, dk=dk, dv=dv, workspace=ws)
+        for _ in range(warmup):
+            step()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(steps):
+            step()
+        e1.record()
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / steps
+        nf = int(mask.sum())
+        flops = layer_flops(B, T, D, H - nf, nf) if bwd else (4 * (H - nf) + 2 * nf) * B * D * causal_pairs(T)
+        tf = flops / (ms * 1e-3) / 1e12
+        return {"ms": ms, "tokens_per_s": B * T / (ms * 1e-3), "tflops": tf, "mfma_frac": tf / PEAK_BF16_TFLOPS}
+
+    zero = np.zeros(H, np.uint8)
+    out = {"workload": f"124M-shaped layer: B={B} H={H} T={T} D={D} bf16, r=25% = {int(m25.sum())} frozen heads",
+           "fwd_r25": run(m25, False), "fwd_r0": run(zero, False),
+           "fwdbwd_r25": run(m25, True), "fwdbwd_r0": run(zero, True)}
+    out["fwd_r25"]["speedup_vs_r0"] = out["fwd_r0"]["ms"] / out["fwd_r25"]["ms"]
+    out["fwdbwd_r25"]["speedup_vs_r0"] = out["fwdbwd_r0"]["ms"] / out["fwdbwd_r25"]["ms"]
     return out
 
 
