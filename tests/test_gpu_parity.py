@@ -116,6 +116,30 @@ def test_gqa_forward_backward(S, B, H, H_kv, T, D, frozen, dt):
     compare_layer(L, run(S, L))
 
 
+def _random_cases(n, seed=123):
+    """Seeded random layer shapes: ragged lengths, both widths, shared key/value heads, any
+    frozen subset (all, none or some), both storage types."""
+    r = np.random.default_rng(seed)
+    cases = []
+    for x in range(n):
+        H = int(r.integers(1, 9))
+        divisors = [d for d in range(1, H + 1) if H % d == 0]
+        H_kv = int(r.choice(divisors))
+        T = int(r.choice([int(r.integers(1, 64)), int(r.integers(64, 300)), int(r.integers(300, 700))]))
+        D = int(r.choice([64, 128]))
+        B = int(r.integers(1, 4))
+        frozen = [h for h in range(H) if r.random() < 0.4]
+        dt = "fp32" if r.random() < 0.3 else "bf16"
+        cases.append((B, H, H_kv, T, D, frozen, dt, 1000 + x))
+    return cases
+
+
+@pytest.mark.parametrize("B,H,H_kv,T,D,frozen,dt,seed", _random_cases(16))
+def test_random_layers(S, B, H, H_kv, T, D, frozen, dt, seed):
+    L = inputs.make_layer(B, H, T, D, dtype=dt, seed=seed, frozen_heads=frozen, kv_heads=H_kv)
+    compare_layer(L, run(S, L))
+
+
 def test_max_head_count(S):
     """H = 256, the most heads a layer may have (the head lists are 8-bit), a quarter frozen,
     with and without shared key/value heads."""
