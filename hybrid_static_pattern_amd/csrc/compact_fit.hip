@@ -12,10 +12,11 @@
 // both marginals of P; the mean row KL reported at the end is CE minus the target's mean
 // row entropy, whose per-column shares the statistics pass also produces.
 //
-// Every kernel gives one wave to one output (a row, a column or a distance) and spreads
-// the sum over that output's line of the causal triangle across the 64 lanes: the reads of
-// alpha, rho and log Z along a line are consecutive, L2-resident floats, and the work per
-// step (1.5 T(T+1) exps per head) is spread over 3 T waves per head instead of T threads.
+// The per-step kernels give each wave two outputs (rows, columns or distances) and spread
+// the sum over an output's line of the causal triangle across the 64 lanes; the 32 outputs
+// of a workgroup are consecutive, so the stretch of alpha, rho or log Z their lines read is
+// staged in LDS once for the workgroup and read there as consecutive floats. The work per
+// step (1.5 T(T+1) exps per head) is spread over 1.5 T waves per head instead of T threads.
 // Exponents are shifted by the row's max (log Z) or are never positive (the marginals, since
 // log Z(i) bounds every logit of row i), so no exp overflows.
 #include <hip/hip_runtime.h>
