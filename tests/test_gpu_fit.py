@@ -199,3 +199,42 @@ def test_full_calibration_fit_sampled(S):
     alpha, rho, kl = gpu_fit(S, A)
     check_fit(A_s, alpha[h_s], rho[h_s], kl[h_s], name="sampled head")
     assert np.all(kl[np.arange(C["H"]) != h_s] < 1e-3)
+
+
+# ---------------------------------------------------------------- the method end to end
+
+def test_calibrate_fit_select_and_run(S):
+    """Algorithm 1's flow on one layer, each side on its own: the calibration score, the
+    compact fit of every head, the selection with the fit's acceptance test (r = 50%), and
+    the hybrid layer run with the selected heads frozen on their fitted tables. The GPU's
+    outputs are checked against the oracle's, which fits its own tables. With r = 75% three
+    heads are wanted; at a 0.5-nat threshold the sharpest head's fit is skipped (the heads'
+    KLs are about 0.004, 0.05, 0.66 and 1.47 here), so two are kept."""
+    N, H, T, D, B = 8, 4, 128, 64, 2
+    scale = 1.0 / math.sqrt(D)
+    cal = inputs.make_calibration(N, H, T, D, seed=56)
+    L = inputs.make_layer(B, H, T, D, dtype="bf16", seed=57, frozen_heads=[])
+    # oracle side
+    A_ref, s_ref, _ = saf_oracle.var_score(cal["q"], cal["k"], scale)
+    fits = [cf.fit_pattern(A_ref[h]) for h in range(H)]
+    kl_ref = np.array([f[2] for f in fits])
+    sel_ref = cf.select_fitted(s_ref, kl_ref, 0.75, max_kl=0.5)
+    # GPU side
+    up = lambda x: torch.from_numpy(x).to(dev()).to(torch.bfloat16)
+    a_hat, s_var, _ = S.var_score(up(cal["q"]), up(cal["k"]))
+    col, dist, ent = S.pattern_stats(a_hat)
+    alpha, rho, kl = S.compact_fit(col, dist, ent)
+    sel = S.select_fitted(s_var.cpu().numpy(), kl.cpu().numpy(), 0.75, max_kl=0.5)
+    # the selections agree unless a KL sits at the threshold or two scores tie within error
+    clear = np.min(np.abs(kl_ref - 0.5)) > 1e-3 and np.min(np.diff(np.sort(s_ref)) / np.max(s_ref)) > 1e-3
+    if clear:
+        assert list(sel) == list(sel_ref), (sel, sel_ref)
+    frozen = np.zeros(H, np.uint8)
+    frozen[sel] = 1
+    o, lse = S.attn_fwd(up(L["q"]), up(L["k"]), up(L["v"]), frozen, alpha, rho)
+    torch.cuda.synchronize()
+    a_tab = np.stack([f[0] for f in fits])
+    r_tab = np.stack([f[1] for f in fits])
+    O, _ = saf_oracle.attn_fwd(L["q"], L["k"], L["v"], frozen, a_tab, r_tab, scale)
+    err = np.abs(o.float().cpu().numpy() - O)
+    assert err.max() <= 2e-2 and err.mean() <= 2e-3, (err.max(), err.mean())
