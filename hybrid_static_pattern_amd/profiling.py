@@ -142,7 +142,22 @@ def pretty_kernel(full: str) -> str:
     return "".join(out).strip()
 
 
-def trace_summary(stats_csv: str, title: str, command: str) -> str:
+def live_timings(bench_log: str) -> dict:
+    """kernels_ms of the JSON line that the traced bench.py printed (its live HIP-event
+    averages over the timed steps), or {} when there is none."""
+    import json
+    d = {}
+    with open(bench_log) as f:
+        for line in f:
+            if line.startswith("{"):
+                try:
+                    d = json.loads(line).get("kernels_ms", {}) or {}
+                except ValueError:
+                    pass
+    return d
+
+
+def trace_summary(stats_csv: str, title: str, command: str, bench_log: str | None = None) -> str:
     rows = []
     with open(stats_csv) as f:
         for r in csv.DictReader(f):
@@ -154,6 +169,12 @@ def trace_summary(stats_csv: str, title: str, command: str) -> str:
              "| kernel | calls | average us | min us | max us | share |", "|---|---|---|---|---|---|"]
     for name, calls, avg, mn, mx, pct in rows:
         lines.append(f"| {name} | {calls} | {avg:.1f} | {mn:.1f} | {mx:.1f} | {pct:.1f}% |")
+    live = live_timings(bench_log) if bench_log else {}
+    if live:
+        lines += ["", "Live HIP-event averages that the same traced bench.py run printed for its timed steps",
+                  "(the trace's averages above also count the warm-up calls):", "",
+                  "| kernel | average us |", "|---|---|"]
+        lines += [f"| {k} | {1e3 * v:.1f} |" for k, v in live.items()]
     return "\n".join(lines) + "\n"
 
 
@@ -165,6 +186,7 @@ def main():
     tr.add_argument("--title", required=True)
     tr.add_argument("--command", default="")
     tr.add_argument("--out", required=True)
+    tr.add_argument("--bench-log", default=None, help="stdout of the traced bench.py (for its live timings)")
     t = sub.add_parser("traffic")
     t.add_argument("--fetch", required=True)
     t.add_argument("--write", required=True)
@@ -174,7 +196,7 @@ def main():
     a = ap.parse_args()
     if a.cmd == "trace":
         with open(a.out, "w") as f:
-            f.write(trace_summary(a.stats, a.title, a.command))
+            f.write(trace_summary(a.stats, a.title, a.command, a.bench_log))
         print(f"wrote {a.out}")
         return
     data = traffic(a.fetch, a.write, a.copy_mib)
