@@ -8,8 +8,9 @@
  *
  * Conventions shared by every entry point
  * ---------------------------------------
- *  - Tensors Q, K, V, O, dO, dQ, dK, dV are [B, H, T, D], contiguous, D fastest.
- *    lse is [B, H, T] float32. alpha and rho are [H, tab_stride] float32 (row h is used
+ *  - Tensors Q, K, V, O, dO, dQ, dK, dV are [B, H, T, D], contiguous, D fastest (K, V, dK
+ *    and dV have kv_heads heads instead of H when key/value heads are shared, see
+ *    saf_attn_desc). lse is [B, H, T] float32. alpha and rho are [H, tab_stride] float32 (row h is used
  *    only when head h is frozen; entries 0..T-1 are read).
  *  - Device pointers are HIP device (or managed) memory; `frozen_mask` is HOST memory.
  *    The caller owns every buffer. The library allocates no device memory and keeps no
@@ -19,7 +20,8 @@
  *    and never synchronises. Argument errors return before anything is enqueued.
  *    A failed launch returns SAF_EHIP; faults during execution surface at the
  *    caller's next synchronisation.
- *  - Device pointers must be 16-byte aligned. D must be 64 or 128.
+ *  - Device pointers must be 16-byte aligned. D must be 64 or 128 for the attention and
+ *    calibration entry points.
  *  - Status codes: SAF_EINVAL (bad pointer, size or alignment), SAF_EUNSUPPORTED
  *    (D or a dtype combination the kernels do not implement), SAF_EWORKSPACE
  *    (workspace smaller than the matching *_workspace_size), SAF_EHIP (launch error).
