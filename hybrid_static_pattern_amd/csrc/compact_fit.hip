@@ -34,7 +34,8 @@ constexpr int LW = 16;     // waves per workgroup in the per-line kernels
 constexpr int OPW = 2;     // outputs (rows, columns or distances) per wave in the per-line kernels
 constexpr int SW = 16;     // waves per workgroup in the statistics kernel
 constexpr int C = 2048;    // keys (or terms) per LDS chunk in the per-line kernels
-constexpr int U = 8;       // keys (or terms) per lane read before use in the per-line kernels
+constexpr int U2 = 2;      // 16-byte reads per lane and table before use in the per-line kernels
+constexpr float kLn2 = 0.6931471805599453f;
 
 __device__ __forceinline__ float wave_max(float x) {
 #pragma unroll
@@ -89,15 +90,18 @@ __global__ __launch_bounds__(64 * SW) void stats_kernel(int T, const float* __re
 // log Z(i) = log sum_{j<=i} exp(alpha(j) + rho(i-j)) for the OPW LW rows of a block, OPW per
 // wave (rows i0 + w + LW r). The rows share their keys: chunks of C keys of alpha, and the
 // window of rho the rows need for them (C + OPW LW - 1 distances), are staged in LDS once for
-// the block. Each lane keeps its own running max and sum over the keys it takes (64 U at a
-// time, U logits read before use, one rescale per group), and the lanes are combined once at
-// the end, so a row costs two cross-lane reductions whatever its length.
+// the block, in log2 units. A lane takes 4 consecutive keys per 16-byte read of each table:
+// the 4 distances of 4 consecutive keys are consecutive too, but where they start depends on
+// the row, so the rho window is staged 4 times, shifted by 0..3 entries, and each row reads
+// the copy that makes its reads 16-byte aligned. Each lane keeps its own running max and sum
+// (one rescale per group of 4 U2 keys); the lanes are combined once per row.
 __global__ __launch_bounds__(64 * LW) void logz_kernel(int T, const float* __restrict__ alpha,
                                                        const float* __restrict__ rho,
                                                        float* __restrict__ logz) {
   constexpr int NR = OPW * LW;   // rows per block
-  __shared__ float sal[C];
-  __shared__ float srh[C + NR];
+  constexpr int GK = 256 * U2;   // keys per group (4 per lane and read)
+  __shared__ float4 sal[C / 4];
+  __shared__ __attribute__((aligned(16))) float srh[4][C + NR + 4];
   const int h = blockIdx.y, lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int i0 = blockIdx.x * NR;
   const int i_last = min(i0 + NR, T) - 1;
@@ -111,35 +115,52 @@ __global__ __launch_bounds__(64 * LW) void logz_kernel(int T, const float* __res
   }
   for (int j0 = 0; j0 <= i_last; j0 += C) {
     __syncthreads();   // the previous chunk is no longer read
-    // sal[y] = alpha(j0 + y); srh[y] = rho(d) with d = i0 - j0 - C + 1 + y, so that row i and
-    // key j read srh[(i - i0) + C - 1 - (j - j0)]
-    for (int y = threadIdx.x; y < C + NR - 1; y += 64 * LW) {
-      if (y < C) sal[y] = (j0 + y <= i_last) ? al[j0 + y] : 0.f;
+    // sal = alpha(j0 + y); copy c of the window: srh[c][y] = rho(d) with
+    // d = i0 - j0 - C + 1 + y + c, so that row i and key j read position (i - i0) + C - 1 - (j - j0) - c
+    float* sa = reinterpret_cast<float*>(sal);
+    for (int y = threadIdx.x; y < C + NR + 3; y += 64 * LW) {
+      if (y < C) sa[y] = (j0 + y <= i_last) ? al[j0 + y] * kLog2e : 0.f;
       const int d = i0 - j0 - C + 1 + y;
-      srh[y] = (d >= 0 && d < T) ? rh[d] : 0.f;
+      const float v = (d >= 0 && d < T) ? rh[d] * kLog2e : 0.f;
+#pragma unroll
+      for (int c = 0; c < 4; ++c)
+        if (y - c >= 0 && y - c < C + NR + 4) srh[c][y - c] = v;
     }
     __syncthreads();
 #pragma unroll
     for (int r = 0; r < OPW; ++r) {
       const int i = i0 + w + LW * r;
       if (i > i_last) continue;
-      const float* rw = srh + (i - i0) + C - 1;
-      for (int k0 = 0; k0 < C && j0 + k0 <= i; k0 += 64 * U) {
-        float x[U];
+      const int c = (i - i0) & 3;
+      // keys k .. k + 3 (k a multiple of 4) read rho at positions yl .. yl + 3 of copy c,
+      // yl = (i - i0) + C - 4 - k - c, in reverse key order
+      const float* rw = srh[c] + (i - i0) + C - 4 - c;
+      for (int k0 = 0; k0 < C && j0 + k0 <= i; k0 += GK) {
+        float x[4 * U2];
 #pragma unroll
-        for (int u = 0; u < U; ++u) {
-          const int k = k0 + 64 * u + lane;   // key j0 + k
-          x[u] = j0 + k <= i ? sal[k] + rw[-k] : kNegInf;
+        for (int u = 0; u < U2; ++u) {
+          const int k = k0 + 256 * u + 4 * lane;
+          const float4 av = sal[k >> 2];
+          const float4 rv = *reinterpret_cast<const float4*>(rw - k);
+          x[4 * u + 0] = av.x + rv.w;
+          x[4 * u + 1] = av.y + rv.z;
+          x[4 * u + 2] = av.z + rv.y;
+          x[4 * u + 3] = av.w + rv.x;
+          if (j0 + k0 + GK - 1 > i) {   // the row ends in this group: mask keys past it
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+              if (j0 + k + e > i) x[4 * u + e] = kNegInf;
+          }
         }
         float cm = x[0];
 #pragma unroll
-        for (int u = 1; u < U; ++u) cm = fmaxf(cm, x[u]);
+        for (int e = 1; e < 4 * U2; ++e) cm = fmaxf(cm, x[e]);
         if (cm == kNegInf) continue;   // no key of this group for this lane
         const float m_new = fmaxf(mx[r], cm);
         float cs = 0.f;
 #pragma unroll
-        for (int u = 0; u < U; ++u) cs += __builtin_amdgcn_exp2f((x[u] - m_new) * kLog2e);
-        s[r] = s[r] * __builtin_amdgcn_exp2f((mx[r] - m_new) * kLog2e) + cs;
+        for (int e = 0; e < 4 * U2; ++e) cs += __builtin_amdgcn_exp2f(x[e] - m_new);
+        s[r] = s[r] * __builtin_amdgcn_exp2f(mx[r] - m_new) + cs;
         mx[r] = m_new;
       }
     }
@@ -149,8 +170,8 @@ __global__ __launch_bounds__(64 * LW) void logz_kernel(int T, const float* __res
     const int i = i0 + w + LW * r;
     if (i > i_last) continue;
     const float m_row = wave_max(mx[r]);   // finite: lane 0 holds key 0
-    const float sr = wave_sum(mx[r] == kNegInf ? 0.f : s[r] * __builtin_amdgcn_exp2f((mx[r] - m_row) * kLog2e));
-    if (lane == 0) logz[(size_t)h * T + i] = m_row + logf(sr);
+    const float sr = wave_sum(mx[r] == kNegInf ? 0.f : s[r] * __builtin_amdgcn_exp2f(mx[r] - m_row));
+    if (lane == 0) logz[(size_t)h * T + i] = (m_row + __log2f(sr)) * kLn2;
   }
 }
 
@@ -164,11 +185,12 @@ struct AdamStep {
 // [nb, 2 nb) distances x (own = rho(x), other = alpha), OPW LW consecutive x per block, OPW
 // per wave (x0 + w + LW r). Both are S(x) = sum_{t=0}^{T-1-x} exp(other(t) + own(x) - log Z(x + t));
 // chunks of C values of `other` and the C + OPW LW - 1 values of log Z the block's outputs
-// need are staged in LDS once for the block. ADAM = false writes S into colP / distP.
-// ADAM = true takes one Adam step on own(x) with gradient (S - target(x)) / T and writes the
-// new value to the other parameter buffer (the current values are still being read by other
-// blocks); m and v are [H, 2T], the alpha part first. Adam's operands are read before the
-// sums so that their latency overlaps the staging.
+// need are staged in LDS once for the block, in log2 units, log Z 4 times shifted by 0..3 so
+// that every output reads it 16 bytes at a time (4 consecutive t per read, as for `other`).
+// ADAM = false writes S into colP / distP. ADAM = true takes one Adam step on own(x) with
+// gradient (S - target(x)) / T and writes the new value to the other parameter buffer (the
+// current values are still being read by other blocks); m and v are [H, 2T], the alpha part
+// first. Adam's operands are read before the sums so that their latency overlaps the staging.
 template <bool ADAM>
 __global__ __launch_bounds__(64 * LW) void marg_kernel(int T, int nb, const float* __restrict__ alpha,
                                                        const float* __restrict__ rho,
@@ -180,8 +202,9 @@ __global__ __launch_bounds__(64 * LW) void marg_kernel(int T, int nb, const floa
                                                        float* __restrict__ m, float* __restrict__ v,
                                                        AdamStep st) {
   constexpr int NX = OPW * LW;   // outputs per block
-  __shared__ float soth[C];
-  __shared__ float slz[C + NX];
+  constexpr int GK = 256 * U2;   // terms per group (4 per lane and read)
+  __shared__ float4 soth[C / 4];
+  __shared__ __attribute__((aligned(16))) float slz[4][C + NX + 4];
   const int h = blockIdx.y, lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const bool is_col = (int)blockIdx.x < nb;
   const int x0 = (is_col ? blockIdx.x : blockIdx.x - nb) * NX;
@@ -206,25 +229,38 @@ __global__ __launch_bounds__(64 * LW) void marg_kernel(int T, int nb, const floa
   }
   for (int t0 = 0; t0 < T - x0; t0 += C) {
     __syncthreads();   // the previous chunk is no longer read
-    for (int y = threadIdx.x; y < C + NX - 1; y += 64 * LW) {
-      if (y < C) soth[y] = (t0 + y < T) ? oth[t0 + y] : 0.f;
-      slz[y] = (x0 + t0 + y < T) ? lz[x0 + t0 + y] : 0.f;
+    // soth = other(t0 + y); copy c: slz[c][y] = log Z(x0 + t0 + y + c)
+    float* so = reinterpret_cast<float*>(soth);
+    for (int y = threadIdx.x; y < C + NX + 3; y += 64 * LW) {
+      if (y < C) so[y] = (t0 + y < T) ? oth[t0 + y] * kLog2e : 0.f;
+      const float lv = (x0 + t0 + y < T) ? lz[x0 + t0 + y] * kLog2e : 0.f;
+#pragma unroll
+      for (int c = 0; c < 4; ++c)
+        if (y - c >= 0 && y - c < C + NX + 4) slz[c][y - c] = lv;
     }
     __syncthreads();
 #pragma unroll
     for (int r = 0; r < OPW; ++r) {
       const int x = x0 + w + LW * r;
-      const float* lw = slz + w + LW * r;   // log Z(x + t) = lw[t - t0]
-      const int n_t = min(C, T - x - t0);   // terms of this chunk for output x
-      for (int k0 = 0; k0 < n_t; k0 += 64 * U) {
-        float e[U];
+      const float o2 = ox[r] * kLog2e;
+      const int c = (x - x0) & 3;
+      const float* lw = slz[c] + (x - x0) - c;   // log Z(x + t0 + k) = lw[k], 16-byte aligned for k % 4 == 0
+      const int n_t = min(C, T - x - t0);        // terms of this chunk for output x
+      for (int k0 = 0; k0 < n_t; k0 += GK) {
 #pragma unroll
-        for (int u = 0; u < U; ++u) {
-          const int k = k0 + 64 * u + lane;
-          e[u] = k < n_t ? soth[k] + ox[r] - lw[k] : kNegInf;
+        for (int u = 0; u < U2; ++u) {
+          const int k = k0 + 256 * u + 4 * lane;
+          const float4 ov = soth[k >> 2];
+          const float4 zv = *reinterpret_cast<const float4*>(lw + k);
+          float e[4] = {ov.x + o2 - zv.x, ov.y + o2 - zv.y, ov.z + o2 - zv.z, ov.w + o2 - zv.w};
+          if (k0 + GK > n_t) {   // the line ends in this group
+#pragma unroll
+            for (int q = 0; q < 4; ++q)
+              if (k + q >= n_t) e[q] = kNegInf;
+          }
+#pragma unroll
+          for (int q = 0; q < 4; ++q) s[r] += __builtin_amdgcn_exp2f(e[q]);
         }
-#pragma unroll
-        for (int u = 0; u < U; ++u) s[r] += __builtin_amdgcn_exp2f(e[u] * kLog2e);
       }
     }
   }
