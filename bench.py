@@ -414,10 +414,11 @@ def gqa(torch, inputs, saf, steps, warmup):
             saf.prof_enable(False)
             res[key]["kernels_ms"] = {n: t for n, t in recs}
             kf = kernel_flops(B, T, D, H - nf, nf)
-            dk = res[key]["kernels_ms"]["dkdv"]
-            res[key]["roofline"] = {"kernel": "dkdv", "bound": "mfma", "achieved": kf["dkdv"] / (dk * 1e-3) / 1e12,
+            t_dkdv = res[key]["kernels_ms"]["dkdv"]
+            tf_dkdv = kf["dkdv"] / (t_dkdv * 1e-3) / 1e12
+            res[key]["roofline"] = {"kernel": "dkdv", "bound": "mfma", "achieved": tf_dkdv,
                                     "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                                    "frac": kf["dkdv"] / (dk * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, "traffic": None}
+                                    "frac": tf_dkdv / PEAK_BF16_TFLOPS, "traffic": None}
     for key in res:
         if key != "r0":
             res[key]["speedup_vs_r0"] = res["r0"]["ms_per_step"] / res[key]["ms_per_step"]
