@@ -105,6 +105,7 @@ def main():
     ap.add_argument("--no-fit", action="store_true", help="skip the compact-fit timing")
     ap.add_argument("--no-gqa", action="store_true", help="skip the grouped-query-attention timing")
     ap.add_argument("--no-l124m", action="store_true", help="skip the 124M-shaped layer timing")
+    ap.add_argument("--no-frozen-path", action="store_true", help="skip the every-head-frozen timing")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="first run one plain elementwise copy (torch.neg) of this many MiB, a "
                          "known-size reference for the FETCH_SIZE / WRITE_SIZE counters")
@@ -214,25 +215,8 @@ def main():
         out["sweep"] = sweep
         out["speedup_vs_r0"] = sweep["r0"]["ms_per_step"] / ms
     # the frozen path alone: every head of the same layer frozen
-    log("timing the frozen path (every head frozen)")
-    m_all = np.ones(H, np.uint8)
-    ms_f, recs_f = timed(m_all, args.steps, args.warmup, prof=True)
-    kf = {}
-    for name, t in recs_f:
-        kf.setdefault(name, []).append(t)
-    kf = {name: float(np.mean(ts)) for name, ts in kf.items()}
-    bh_td = B * H * T * D
-    fwd_bytes = bh_td * 2 * 2 + B * H * T * 4            # V read, O written (bf16), log Z written
-    bwd_bytes = bh_td * 2 + B * H * T * 4 + bh_td * 4    # dO and log Z read, dV written (fp32)
-    frz_flops = 2 * B * H * D * causal_pairs(T)
-    out["frozen_path"] = {
-        "workload": f"{args.workload} with all {H} heads frozen", "ms_per_step": ms_f, "kernels_ms": kf,
-        "fwd": {"hbm_gb_per_s": fwd_bytes / (kf["hybrid_fwd"] * 1e-3) / 1e9, "bytes": fwd_bytes,
-                "tflops": frz_flops / (kf["hybrid_fwd"] * 1e-3) / 1e12},
-        "bwd": {"hbm_gb_per_s": bwd_bytes / (kf["dkdv"] * 1e-3) / 1e9, "bytes": bwd_bytes,
-                "tflops": frz_flops / (kf["dkdv"] * 1e-3) / 1e12},
-        "speedup_vs_r0": (out["sweep"]["r0"]["ms_per_step"] / ms_f) if "sweep" in out else None,
-    }
+    if not args.no_frozen_path:
+        out["frozen_path"] = frozen_path(timed, args, B, H, T, D, out)
     if not args.no_l124m:
         log("timing the 124M-shaped layer")
         out["l124m"] = l124m(torch, inputs, saf, args.steps, args.warmup)
@@ -315,6 +299,30 @@ def prefill(torch, inputs, saf, steps, warmup):
     s = P["single"]
     out["single"] = {"B": s["B"], "T": s["T"], **run(s["B"], s["T"], P["seed"])}
     return out
+
+
+def frozen_path(timed, args, B, H, T, D, out):
+    """The same layer with every head frozen: per kernel, the bytes the frozen items must move
+    and the P-hat V FLOPs over the kernel's time."""
+    log("timing the frozen path (every head frozen)")
+    m_all = np.ones(H, np.uint8)
+    ms_f, recs_f = timed(m_all, args.steps, args.warmup, prof=True)
+    kf = {}
+    for name, t in recs_f:
+        kf.setdefault(name, []).append(t)
+    kf = {name: float(np.mean(ts)) for name, ts in kf.items()}
+    bh_td = B * H * T * D
+    fwd_bytes = bh_td * 2 * 2 + B * H * T * 4            # V read, O written (bf16), log Z written
+    bwd_bytes = bh_td * 2 + B * H * T * 4 + bh_td * 4    # dO and log Z read, dV written (fp32)
+    frz_flops = 2 * B * H * D * causal_pairs(T)
+    return {
+        "workload": f"{args.workload} with all {H} heads frozen", "ms_per_step": ms_f, "kernels_ms": kf,
+        "fwd": {"hbm_gb_per_s": fwd_bytes / (kf["hybrid_fwd"] * 1e-3) / 1e9, "bytes": fwd_bytes,
+                "tflops": frz_flops / (kf["hybrid_fwd"] * 1e-3) / 1e12},
+        "bwd": {"hbm_gb_per_s": bwd_bytes / (kf["dkdv"] * 1e-3) / 1e9, "bytes": bwd_bytes,
+                "tflops": frz_flops / (kf["dkdv"] * 1e-3) / 1e12},
+        "speedup_vs_r0": (out["sweep"]["r0"]["ms_per_step"] / ms_f) if "sweep" in out else None,
+    }
 
 
 def l124m(torch, inputs, saf, steps, warmup):
