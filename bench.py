@@ -106,6 +106,8 @@ def main():
     ap.add_argument("--no-gqa", action="store_true", help="skip the grouped-query-attention timing")
     ap.add_argument("--no-l124m", action="store_true", help="skip the 124M-shaped layer timing")
     ap.add_argument("--no-frozen-path", action="store_true", help="skip the every-head-frozen timing")
+    ap.add_argument("--frozen", type=int, default=None,
+                    help="number of frozen heads of the main step (default: the workload's own)")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="first run one plain elementwise copy (torch.neg) of this many MiB, a "
                          "known-size reference for the FETCH_SIZE / WRITE_SIZE counters")
@@ -129,6 +131,9 @@ def main():
         torch.cuda.synchronize()
         del src, dst
     spec = dict(inputs.WORKLOADS[args.workload])
+    if args.frozen is not None:   # another replacement ratio for the main step (profiling runs)
+        spec["n_frozen"] = args.frozen
+        spec.pop("frozen_heads", None)
     L = inputs.make_layer(**spec)
     B, H, T, D = L["B"], L["H"], L["T"], L["D"]
     dev = torch.device("cuda:0")

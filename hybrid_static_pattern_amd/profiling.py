@@ -94,14 +94,18 @@ def traffic(fetch_csv: str, write_csv: str, copy_mib: int):
     return out
 
 
-def summary_path(outdir: str, kernel: str) -> str:
-    return os.path.join(outdir, f"traffic_{kernel}_{KERNEL_WORKLOAD.get(kernel, DEFAULT_WORKLOAD)}.txt")
+def summary_path(outdir: str, kernel: str, workload: str | None = None) -> str:
+    wl = workload or KERNEL_WORKLOAD.get(kernel, DEFAULT_WORKLOAD)
+    return os.path.join(outdir, f"traffic_{kernel}_{wl}.txt")
 
 
-def write_summaries(data: dict, outdir: str, command: str) -> None:
+def write_summaries(data: dict, outdir: str, command: str, workload: str | None = None,
+                    kernels=None) -> None:
     for k, d in data.items():
-        with open(summary_path(outdir, k), "w") as f:
-            wl = KERNEL_WORKLOAD.get(k, DEFAULT_WORKLOAD)
+        if kernels and k not in kernels:
+            continue
+        with open(summary_path(outdir, k, workload), "w") as f:
+            wl = workload or KERNEL_WORKLOAD.get(k, DEFAULT_WORKLOAD)
             f.write(f"# HBM traffic of {k} per launch, workload {wl}\n")
             f.write("# FETCH_SIZE and WRITE_SIZE (KiB per dispatch) scaled by the factor that makes the\n")
             f.write("# same counters read a plain device copy of known size correctly.\n")
@@ -178,9 +182,50 @@ def trace_summary(stats_csv: str, title: str, command: str, bench_log: str | Non
     return "\n".join(lines) + "\n"
 
 
+def mfma_summary(runs, command: str, n_simd: int = 1024, peak_clock_ghz: float = 2.4) -> str:
+    """MFMA utilisation per kernel from one `rocprofv3 --pmc SQ_VALU_MFMA_BUSY_CYCLES
+    SQ_INSTS_VALU_MFMA_MOPS_BF16 SQ_BUSY_CU_CYCLES GRBM_GUI_ACTIVE` run per label.
+    GRBM_GUI_ACTIVE is summed over the 8 XCDs, so /8 is the shader cycles of the dispatch; the
+    MFMA-busy fraction is SQ_VALU_MFMA_BUSY_CYCLES over those cycles times the SIMD count,
+    and against the published clock the same busy cycles over duration x 2.4 GHz x SIMDs.
+    Executed bf16 FLOPs are SQ_INSTS_VALU_MFMA_MOPS_BF16 x 512."""
+    lines = ["# MFMA utilisation from counters (1B-shape layer, B=2, H=16, T=8192, d_h=128, bf16)", "",
+             "Command (repository root R on the MI355X box):", "", "```", command, "```", "",
+             "Counters are collected per dispatch (the kernels run slower under collection than in",
+             "`bench.py`). Clock = GRBM_GUI_ACTIVE / 8 XCDs / duration.", "",
+             "| run | kernel | dispatches | ms | clock GHz | MFMA busy (of active cycles) | MFMA busy (of 2.4 GHz) | executed bf16 TFLOP/s |",
+             "|---|---|---|---|---|---|---|---|"]
+    for label, path in runs:
+        cnt = collections.defaultdict(lambda: collections.defaultdict(float))
+        dur = collections.defaultdict(dict)
+        with open(path) as f:
+            for r in csv.DictReader(f):
+                k = short_name(r["Kernel_Name"])
+                if k not in KERNEL_SOURCES:
+                    continue
+                cnt[k][r["Counter_Name"]] += float(r["Counter_Value"])
+                dur[k][r["Dispatch_Id"]] = (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) * 1e-9
+        for k in cnt:
+            n = len(dur[k])
+            t = sum(dur[k].values()) / n
+            c = {name: v / n for name, v in cnt[k].items()}
+            cyc = c.get("GRBM_GUI_ACTIVE", 0.0) / 8
+            busy = c.get("SQ_VALU_MFMA_BUSY_CYCLES", 0.0)
+            if busy == 0:
+                continue
+            lines.append(f"| {label} | {k} | {n} | {t * 1e3:.3f} | {cyc / t / 1e9:.2f} | {busy / (cyc * n_simd):.3f} | "
+                         f"{busy / (t * peak_clock_ghz * 1e9 * n_simd):.3f} | "
+                         f"{c.get('SQ_INSTS_VALU_MFMA_MOPS_BF16', 0.0) * 512 / t / 1e12:.0f} |")
+    return "\n".join(lines) + "\n"
+
+
 def main():
     ap = argparse.ArgumentParser()
     sub = ap.add_subparsers(dest="cmd", required=True)
+    mf = sub.add_parser("mfma")
+    mf.add_argument("--run", action="append", required=True, help="LABEL=path/to/run_counter_collection.csv")
+    mf.add_argument("--command", default="")
+    mf.add_argument("--out", required=True)
     tr = sub.add_parser("trace")
     tr.add_argument("--stats", required=True)
     tr.add_argument("--title", required=True)
@@ -193,14 +238,22 @@ def main():
     t.add_argument("--copy-mib", type=int, required=True)
     t.add_argument("--command", default="")
     t.add_argument("--out", default=os.path.join(os.path.dirname(PKG), "profiles"))
+    t.add_argument("--workload", default=None, help="workload name in the summaries' file names")
+    t.add_argument("--kernels", default=None, help="comma-separated kernels to write (default: all)")
     a = ap.parse_args()
+    if a.cmd == "mfma":
+        runs = [tuple(x.rsplit("=", 1)) for x in a.run]
+        with open(a.out, "w") as f:
+            f.write(mfma_summary(runs, a.command))
+        print(f"wrote {a.out}")
+        return
     if a.cmd == "trace":
         with open(a.out, "w") as f:
             f.write(trace_summary(a.stats, a.title, a.command, a.bench_log))
         print(f"wrote {a.out}")
         return
     data = traffic(a.fetch, a.write, a.copy_mib)
-    write_summaries(data, a.out, a.command)
+    write_summaries(data, a.out, a.command, a.workload, a.kernels.split(",") if a.kernels else None)
     for k, d in data.items():
         print(f"{k}: fetch {d['fetch_bytes'] / 1e6:.1f} MB, write {d['write_bytes'] / 1e6:.1f} MB per launch")
 
