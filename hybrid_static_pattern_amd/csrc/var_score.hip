@@ -47,6 +47,34 @@ __device__ __forceinline__ void load_k(const bf16* K, int j0, int T, KTile<D>& t
   tile_load<D / 8, BN>(tile.k, [&](int row, int c) { return K + (size_t)min(j0 + row, T - 1) * D + c * 8; });
 }
 
+// One sequence's operands of a (128-query, 64-key) tile for the kernels that loop over the
+// sequences: its key rows, its query rows and (Welford) the rows' normalisers, all loaded
+// straight into LDS a sequence ahead. Loading the query fragments into registers instead
+// would make the wait for them (the counter of outstanding loads retires in order) also wait
+// for the next sequence's tile loads issued before the use.
+template <int D>
+struct SeqTile {
+  bf16 k[BN * D];   // key rows, swizzled (swz<D/8>)
+  bf16 q[BM * D];   // query rows, swizzled
+  float l2[BM];     // row normalisers, log2 units (rows past T repeat row T - 1)
+};
+
+template <int D>
+__device__ __forceinline__ void load_seq(const bf16* Q, const bf16* K, const float* l2, int i0, int j0, int T,
+                                         bool with_l2, SeqTile<D>& tile) {
+  load_k<D>(K, j0, T, *reinterpret_cast<KTile<D>*>(tile.k));
+  tile_load<D / 8, BM>(tile.q, [&](int row, int c) { return Q + (size_t)min(i0 + row, T - 1) * D + c * 8; });
+  const int w = wave_id();
+  if (with_l2 && w < BM / 64) g2lds4(l2 + min(i0 + 64 * w + lane_id(), T - 1), lds_addr(&tile.l2[64 * w]));
+}
+
+// this lane's query fragments (row 32 w + m of the tile, k-halves hh) from LDS
+template <int D>
+__device__ __forceinline__ void lds_q(const SeqTile<D>& tile, int row, int hh, bf16x8 (&qf)[D / 16]) {
+#pragma unroll
+  for (int kk = 0; kk < D / 16; ++kk) qf[kk] = lds_row<D / 8>(tile.q, 0, row_off<D / 8>(row, 2 * kk + hh));
+}
+
 // S^T tile (64 keys x this lane's query) for the 64-key tile held in LDS; koff: per-lane
 // offsets of the pi-ordered key rows, one per k-step.
 template <int D>
@@ -131,7 +159,7 @@ __global__ __launch_bounds__(NTH, 2) void var_lse_kernel(const VarParams p) {
 // sum_n KL(A^(n)_i || A_hat_i) = sum_n sum_j A^(n) log A^(n) - N sum_j A_hat log A_hat.
 template <int D, bool KL>
 __global__ __launch_bounds__(NTH, 2) void var_welford_kernel(const VarParams p) {
-  __shared__ __attribute__((aligned(16))) KTile<D> stg[2];
+  __shared__ __attribute__((aligned(16))) SeqTile<D> stg[2];
   __shared__ float red[NTH / 64];
   const int jt = blockIdx.x % p.n_jt;
   const int it = (blockIdx.x / p.n_jt) % p.n_it;
@@ -171,18 +199,22 @@ __global__ __launch_bounds__(NTH, 2) void var_welford_kernel(const VarParams p) 
   const size_t nh_stride = (size_t)p.H * T;
   uint32_t koff[D / 16];
   key_offsets<D>(m, hh, koff);
-  load_k<D>(p.k + ((size_t)h * T) * D, j0, T, stg[0]);
+  auto load = [&](int n, SeqTile<D>& tile) {
+    const size_t head = (size_t)n * nh_stride + (size_t)h * T;
+    load_seq<D>(p.q + head * D, p.k + head * D, p.lse2 + head, i0, j0, T, true, tile);
+  };
+  load(0, stg[0]);
   wait_vm0();
   __syncthreads();
   for (int n = 0; n < p.N; ++n) {
-    const size_t head = (size_t)n * nh_stride + (size_t)h * T;
-    if (n + 1 < p.N) load_k<D>(p.k + (head + nh_stride) * D, j0, T, stg[(n + 1) & 1]);
+    if (n + 1 < p.N) load(n + 1, stg[(n + 1) & 1]);
     if (active) {
+      const SeqTile<D>& cur = stg[n & 1];
       bf16x8 qf[D / 16];
-      load_q<D>(p.q + head * D, i, T, hh, qf);
-      const float l2 = (i < T) ? p.lse2[head + i] : __builtin_huge_valf();
+      lds_q<D>(cur, 32 * w + m, hh, qf);
+      const float l2 = (i < T) ? cur.l2[32 * w + m] : __builtin_huge_valf();
       f32x16 s[2];
-      scores<D>(stg[n & 1].k, qf, koff, s);
+      scores<D>(cur.k, qf, koff, s);
       const float rn = 1.f / (float)(n + 1);
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
@@ -271,7 +303,7 @@ __global__ __launch_bounds__(256) void var_final_kernel(const VarParams p) {
 // its causal softmax in place and writes the zeros above the diagonal.
 template <int D>
 __global__ __launch_bounds__(NTH, 2) void sharp_logits_kernel(const VarParams p, float* out) {
-  __shared__ __attribute__((aligned(16))) KTile<D> stg[2];
+  __shared__ __attribute__((aligned(16))) SeqTile<D> stg[2];
   const int jt = blockIdx.x % p.n_jt;
   const int it = (blockIdx.x / p.n_jt) % p.n_it;
   const int h = blockIdx.x / (p.n_jt * p.n_it);
@@ -283,16 +315,19 @@ __global__ __launch_bounds__(NTH, 2) void sharp_logits_kernel(const VarParams p,
   const size_t nh_stride = (size_t)p.H * T;
   uint32_t koff[D / 16];
   key_offsets<D>(m, hh, koff);
-  load_k<D>(p.k + ((size_t)h * T) * D, j0, T, stg[0]);
+  auto load = [&](int n, SeqTile<D>& tile) {
+    const size_t head = (size_t)n * nh_stride + (size_t)h * T;
+    load_seq<D>(p.q + head * D, p.k + head * D, nullptr, i0, j0, T, false, tile);
+  };
+  load(0, stg[0]);
   wait_vm0();
   __syncthreads();
   f32x16 acc[2] = {f32x16{}, f32x16{}};
   for (int n = 0; n < p.N; ++n) {
-    const size_t head = (size_t)n * nh_stride + (size_t)h * T;
-    if (n + 1 < p.N) load_k<D>(p.k + (head + nh_stride) * D, j0, T, stg[(n + 1) & 1]);
+    if (n + 1 < p.N) load(n + 1, stg[(n + 1) & 1]);
     if (active) {
       bf16x8 qf[D / 16];
-      load_q<D>(p.q + head * D, i, T, hh, qf);
+      lds_q<D>(stg[n & 1], 32 * w + m, hh, qf);
       pipelined<D / 8>([&](int x) { return lds_row<D / 8>(stg[n & 1].k, (x & 1) * 32, koff[x >> 1]); },
                        [&](int x, const bf16x8& a) { acc[x & 1] = mfma32(a, qf[x >> 1], acc[x & 1]); });
     }
