@@ -61,9 +61,11 @@ def layer_flops(B, T, D, n_dyn, n_frz):
     return (14 * B * n_dyn + 4 * B * n_frz) * D * pc
 
 
-def cpu_baseline(L, n_dyn, n_frz):
+def cpu_baseline(L, n_dyn, n_frz, budget_s: float = 10.0):
     """The CPU oracle (numpy float64, dense T x T) timed on a bounded sample of the workload:
-    one ordinary and one frozen (b, h) of the layer, forward + backward, scaled to the layer."""
+    whole (b, h) heads of the layer, forward + backward, ordinary and frozen in turn until about
+    budget_s seconds of CPU work are spent; the mean time per head of each kind is scaled to
+    the layer's head counts."""
     from oracle import saf_oracle
     try:
         import threadpoolctl
@@ -72,23 +74,31 @@ def cpu_baseline(L, n_dyn, n_frz):
         threads = 1
     scale = 1.0 / math.sqrt(L["D"])
     B, T = L["B"], L["T"]
-    t_head = {}
-    for kind, sel in (("dyn", L["frozen"] == 0), ("frz", L["frozen"] != 0)):
-        if not sel.any():
-            continue
-        h = int(np.flatnonzero(sel)[0])
-        s = lambda x: x[0:1, h:h + 1]
-        fz, al, rh = L["frozen"][h:h + 1], L["alpha"][h:h + 1], L["rho"][h:h + 1]
-        t0 = time.perf_counter()
-        saf_oracle.attn_fwd(s(L["q"]), s(L["k"]), s(L["v"]), fz, al, rh, scale)
-        saf_oracle.attn_bwd(s(L["q"]), s(L["k"]), s(L["v"]), s(L["do"]), fz, al, rh, scale)
-        t_head[kind] = time.perf_counter() - t0
-        log(f"oracle {kind} head: {t_head[kind]:.1f} s")
+    heads = {kind: [int(h) for h in np.flatnonzero(sel)]
+             for kind, sel in (("dyn", L["frozen"] == 0), ("frz", L["frozen"] != 0))}
+    times = {kind: [] for kind in heads if heads[kind]}
+    spent, i = 0.0, 0
+    while times and (spent < budget_s or any(not t for t in times.values())) and i < 64:
+        for kind in times:
+            hs = heads[kind]
+            h, b = hs[i % len(hs)], (i // len(hs)) % B
+            s = lambda x: x[b:b + 1, h:h + 1]
+            fz, al, rh = L["frozen"][h:h + 1], L["alpha"][h:h + 1], L["rho"][h:h + 1]
+            t0 = time.perf_counter()
+            saf_oracle.attn_fwd(s(L["q"]), s(L["k"]), s(L["v"]), fz, al, rh, scale)
+            saf_oracle.attn_bwd(s(L["q"]), s(L["k"]), s(L["v"]), s(L["do"]), fz, al, rh, scale)
+            times[kind].append(time.perf_counter() - t0)
+            spent += times[kind][-1]
+        i += 1
+    t_head = {kind: float(np.mean(t)) for kind, t in times.items()}
+    for kind, t in times.items():
+        log(f"oracle {kind} heads: {len(t)} in {sum(t):.1f} s")
     layer_s = B * n_dyn * t_head.get("dyn", 0.0) + B * n_frz * t_head.get("frz", 0.0)
+    counts = ", ".join(f"{len(t)} {'ordinary' if k == 'dyn' else 'frozen'}" for k, t in times.items())
     return {
         "value": B * T / layer_s, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
-        "sample": (f"one ordinary and one frozen (b,h) head at T={T} (fwd+bwd, float64, dense TxT), "
-                   f"{sum(t_head.values()):.1f} s measured, scaled to the layer's {B * n_dyn} ordinary "
+        "sample": (f"{counts} (b,h) heads at T={T} (fwd+bwd, float64, dense TxT), "
+                   f"{spent:.1f} s measured, mean per head scaled to the layer's {B * n_dyn} ordinary "
                    f"and {B * n_frz} frozen heads; BLAS threads={threads}, host cores="
                    f"{len(os.sched_getaffinity(0))}, numpy elementwise ops single-threaded"),
     }
