@@ -373,6 +373,16 @@ def test_sharp_mean_d128_ragged(S):
     _check_sharp(S, inputs.make_calibration(3, 2, 67, 128, seed=28))
 
 
+@pytest.mark.parametrize("N,D", [(2, 64), (3, 64), (2, 128)])
+def test_calibration_fewer_sequences_than_stages(S, N, D):
+    """N at or below the depth of the kernels' sequence pipeline (the loads run ahead of the
+    sequence in use, and those past the last sequence re-read it): all three scores."""
+    C = inputs.make_calibration(N, 2, 130, D, seed=40 + N + D)
+    _check_var(S, C)
+    _check_kl(S, C)
+    _check_sharp(S, C)
+
+
 def test_full_calibration_sharp_sampled(S):
     C = inputs.make_calibration(**inputs.CALIBRATION)
     _check_sharp(S, C, heads=[int(np.argmin(C["tau"])), int(np.argmax(C["tau"]))])
