@@ -571,15 +571,22 @@ def fit(torch, inputs, saf, no_cpu):
     al_m, rh_m = (torch.zeros((L_layers * H, T), dtype=torch.float32, device=dev) for _ in range(2))
     kl_m = torch.empty((L_layers * H,), dtype=torch.float32, device=dev)
     ws_m = torch.empty(saf.fit_workspace_size(L_layers * H, T, steps), dtype=torch.uint8, device=dev)
-    saf.compact_fit(col_m, dist_m, ent_m, alpha=al_m, rho=rh_m, kl=kl_m, steps=steps, workspace=ws_m)
-    torch.cuda.synchronize()
-    al_m.zero_()
-    rh_m.zero_()
-    e0.record(st)
-    saf.compact_fit(col_m, dist_m, ent_m, alpha=al_m, rho=rh_m, kl=kl_m, steps=steps, workspace=ws_m)
-    e1.record(st)
-    torch.cuda.synchronize()
-    ms_model = e0.elapsed_time(e1)
+
+    def time_model(schedule):
+        saf.compact_fit(col_m, dist_m, ent_m, alpha=al_m, rho=rh_m, kl=kl_m, steps=steps, workspace=ws_m,
+                        schedule=schedule)
+        torch.cuda.synchronize()
+        al_m.zero_()
+        rh_m.zero_()
+        e0.record(st)
+        saf.compact_fit(col_m, dist_m, ent_m, alpha=al_m, rho=rh_m, kl=kl_m, steps=steps, workspace=ws_m,
+                        schedule=schedule)
+        e1.record(st)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1)
+
+    ms_model_step = time_model(saf.SAF_FIT_PER_STEP)
+    ms_model = time_model(saf.SAF_FIT_AUTO)    # 144 heads: one workgroup per head
     exps_model = steps * 3 * causal_pairs(T) * L_layers * H
     out = {
         "workload": f"compact fit of the calibration heads: H={H} T={T}, {steps} Adam steps, targets from "
@@ -587,9 +594,11 @@ def fit(torch, inputs, saf, no_cpu):
         "ms": ms, "ms_per_step": ms / steps, "kernels": kern,
         "kl": [float(x) for x in kl_h],
         "selected_r25": [int(x) for x in saf.select_fitted(s_var.cpu().numpy(), kl_h, 0.25)],
-        "model_144_heads": {"ms": ms_model, "ms_per_head": ms_model / (L_layers * H),
+        "model_144_heads": {"schedule": "automatic (one workgroup per head)",
+                            "ms": ms_model, "ms_per_head": ms_model / (L_layers * H),
                             "texp_per_s": exps_model / (ms_model * 1e-3) / 1e12,
-                            "frac": exps_model / (ms_model * 1e-3) / PEAK_EXP_PER_S},
+                            "frac": exps_model / (ms_model * 1e-3) / PEAK_EXP_PER_S,
+                            "per_step_schedule_ms": ms_model_step},
         "roofline": {"kernel": "fit_logz + fit_adam", "bound": "alu", "achieved": achieved / 1e12,
                      "peak": PEAK_EXP_PER_S / 1e12, "unit": "Texp/s", "frac": achieved / PEAK_EXP_PER_S,
                      "traffic": None},

@@ -116,15 +116,27 @@ __global__ __launch_bounds__(64 * LW) void logz_kernel(int T, const float* __res
   for (int j0 = 0; j0 <= i_last; j0 += C) {
     __syncthreads();   // the previous chunk is no longer read
     // sal = alpha(j0 + y); copy c of the window: srh[c][y] = rho(d) with
-    // d = i0 - j0 - C + 1 + y + c, so that row i and key j read position (i - i0) + C - 1 - (j - j0) - c
+    // d = i0 - j0 - C + 1 + y + c, so that row i and key j read position (i - i0) + C - 1 - (j - j0) - c.
+    // All of a thread's loads are issued before the first store, so the block waits for
+    // memory once per chunk.
     float* sa = reinterpret_cast<float*>(sal);
-    for (int y = threadIdx.x; y < C + NR + 3; y += 64 * LW) {
-      if (y < C) sa[y] = (j0 + y <= i_last) ? al[j0 + y] * kLog2e : 0.f;
-      const int d = i0 - j0 - C + 1 + y;
-      const float v = (d >= 0 && d < T) ? rh[d] * kLog2e : 0.f;
+    constexpr int NY = (C + NR + 3 + 64 * LW - 1) / (64 * LW);
+    float va[NY], vr[NY];
 #pragma unroll
-      for (int c = 0; c < 4; ++c)
-        if (y - c >= 0 && y - c < C + NR + 4) srh[c][y - c] = v;
+    for (int q = 0; q < NY; ++q) {
+      const int y = threadIdx.x + 64 * LW * q, d = i0 - j0 - C + 1 + y;
+      va[q] = (y < C && j0 + y <= i_last) ? al[j0 + y] : 0.f;
+      vr[q] = (y < C + NR + 3 && d >= 0 && d < T) ? rh[d] : 0.f;
+    }
+#pragma unroll
+    for (int q = 0; q < NY; ++q) {
+      const int y = threadIdx.x + 64 * LW * q;
+      if (y < C) sa[y] = va[q] * kLog2e;
+      if (y < C + NR + 3) {
+#pragma unroll
+        for (int c = 0; c < 4; ++c)
+          if (y - c >= 0) srh[c][y - c] = vr[q] * kLog2e;
+      }
     }
     __syncthreads();
 #pragma unroll
@@ -229,14 +241,26 @@ __global__ __launch_bounds__(64 * LW) void marg_kernel(int T, int nb, const floa
   }
   for (int t0 = 0; t0 < T - x0; t0 += C) {
     __syncthreads();   // the previous chunk is no longer read
-    // soth = other(t0 + y); copy c: slz[c][y] = log Z(x0 + t0 + y + c)
+    // soth = other(t0 + y); copy c: slz[c][y] = log Z(x0 + t0 + y + c); loads first, as in
+    // logz_kernel
     float* so = reinterpret_cast<float*>(soth);
-    for (int y = threadIdx.x; y < C + NX + 3; y += 64 * LW) {
-      if (y < C) so[y] = (t0 + y < T) ? oth[t0 + y] * kLog2e : 0.f;
-      const float lv = (x0 + t0 + y < T) ? lz[x0 + t0 + y] * kLog2e : 0.f;
+    constexpr int NY = (C + NX + 3 + 64 * LW - 1) / (64 * LW);
+    float ov[NY], lv[NY];
 #pragma unroll
-      for (int c = 0; c < 4; ++c)
-        if (y - c >= 0 && y - c < C + NX + 4) slz[c][y - c] = lv;
+    for (int q = 0; q < NY; ++q) {
+      const int y = threadIdx.x + 64 * LW * q;
+      ov[q] = (y < C && t0 + y < T) ? oth[t0 + y] : 0.f;
+      lv[q] = (y < C + NX + 3 && x0 + t0 + y < T) ? lz[x0 + t0 + y] : 0.f;
+    }
+#pragma unroll
+    for (int q = 0; q < NY; ++q) {
+      const int y = threadIdx.x + 64 * LW * q;
+      if (y < C) so[y] = ov[q] * kLog2e;
+      if (y < C + NX + 3) {
+#pragma unroll
+        for (int c = 0; c < 4; ++c)
+          if (y - c >= 0) slz[c][y - c] = lv[q] * kLog2e;
+      }
     }
     __syncthreads();
 #pragma unroll
@@ -317,6 +341,232 @@ __global__ void copy_kernel(float* __restrict__ dst, const float* __restrict__ s
     dst[x] = src[x];
 }
 
+// ---------------------------------------------------------------- one workgroup per head
+//
+// The whole fit of one head in one workgroup of 16 waves, its state in LDS: alpha and rho
+// (log2 units, two buffers: a step reads one and writes the other), log Z, and Adam's
+// moments, the parameters in natural units and the targets. A step is two phases with a
+// barrier after each, so no launch and no round trip through memory separates them. Used
+// when there are enough heads to occupy the CUs (the per-step launches above spread one
+// head over many CUs instead).
+//
+// Both phases give each 16-lane group four consecutive rows (or outputs) and each lane 8
+// consecutive keys (or terms) at a time: the 32 terms a lane forms per iteration then come
+// from 5 16-byte LDS reads (2 of one table, 3 of the other, whose 11 entries cover the 4 x 8
+// sums of the two indices), so the exps, not LDS bandwidth, bound the phases; and the
+// cross-lane reductions stay within 16-lane DPP rows (four data-parallel-primitive moves
+// instead of LDS permutes).
+//
+// Table padding replaces masks: rho has 8 entries of -inf before distance 0 and -inf past
+// T - 1 (keys after their row get -inf), log Z has +inf past row T - 1 (terms past the end
+// of a column or distance line get exp2(-inf) = 0), alpha has 0 past T - 1 (only ever added
+// to a -inf); no sum of two infinities of opposite sign arises.
+constexpr int HW = 16;            // waves per workgroup
+constexpr int RPAD = 8;           // -inf entries before rho(0)
+constexpr int TPAD = 16;          // entries past T - 1 in each table
+
+struct AdamHyper {
+  float lr, beta1, beta2, eps;
+};
+
+// Reductions over the 16 lanes of a DPP row (lanes 16 r .. 16 r + 15), every lane getting
+// the result: the quad permutations [1,0,3,2] and [2,3,0,1] combine lanes within quads, the
+// half-row mirror (lane l <-> 7 - l in each 8) pairs the two quads of a half, the row mirror
+// (l <-> 15 - l) the two halves.
+template <int CTRL>
+__device__ __forceinline__ float dpp_mov(float x) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), CTRL, 0xF, 0xF, false));
+}
+__device__ __forceinline__ float row16_sum(float x) {
+  x += dpp_mov<0xB1>(x);
+  x += dpp_mov<0x4E>(x);
+  x += dpp_mov<0x141>(x);
+  return x + dpp_mov<0x140>(x);
+}
+__device__ __forceinline__ float row16_max(float x) {
+  x = fmaxf(x, dpp_mov<0xB1>(x));
+  x = fmaxf(x, dpp_mov<0x4E>(x));
+  x = fmaxf(x, dpp_mov<0x141>(x));
+  return fmaxf(x, dpp_mov<0x140>(x));
+}
+
+template <int TMAX>
+struct HeadFit {
+  float a2[2][TMAX + TPAD];         // alpha * log2(e)
+  float r2[2][RPAD + TMAX + TPAD];  // rho * log2(e), rho(d) at RPAD + d
+  float z2[TMAX + TPAD];            // log2 Z
+  float par[2 * TMAX];              // alpha, then rho (natural units)
+  float mom[2 * TMAX], vel[2 * TMAX], tgt[2 * TMAX];   // Adam moments; col, then dist
+  double red[HW];
+};
+
+template <int TMAX>
+__global__ __launch_bounds__(64 * HW) void fit_head_kernel(int T, int steps, AdamHyper hp,
+                                                           const float* __restrict__ col,
+                                                           const float* __restrict__ dist,
+                                                           const float* __restrict__ ent,
+                                                           float* __restrict__ alpha,
+                                                           float* __restrict__ rho,
+                                                           float* __restrict__ kl) {
+  __shared__ __attribute__((aligned(16))) HeadFit<TMAX> sm;
+  const int h = blockIdx.x, tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int qd = lane >> 4, kl16 = lane & 15;
+  const size_t hb = (size_t)h * T;
+  const float inv_t = 1.f / T;
+
+  for (int x = tid; x < TMAX + TPAD; x += 64 * HW) {
+    const float a = x < T ? alpha[hb + x] : 0.f;
+    const float r = x < T ? rho[hb + x] : kNegInf;
+    sm.a2[0][x] = x < T ? a * kLog2e : 0.f;
+    sm.a2[1][x] = 0.f;
+    sm.r2[0][RPAD + x] = x < T ? r * kLog2e : kNegInf;
+    sm.r2[1][RPAD + x] = kNegInf;
+    sm.z2[x] = __builtin_huge_valf();
+    if (x < T) {
+      sm.par[x] = a;
+      sm.par[T + x] = r;
+      sm.tgt[x] = col[hb + x];
+      sm.tgt[T + x] = dist[hb + x];
+      sm.mom[x] = sm.mom[T + x] = 0.f;
+      sm.vel[x] = sm.vel[T + x] = 0.f;
+    }
+  }
+  if (tid < RPAD) sm.r2[0][tid] = sm.r2[1][tid] = kNegInf;
+  __syncthreads();
+
+  const int nb = (T + 15) / 16;   // 16-row (16-output) blocks
+  // Block j of wave w: the waves take the blocks in rounds of HW, in reverse order every
+  // other round, so that the lengths (which grow or shrink with the block index) even out.
+  auto block_of = [&](int j) { return HW * j + ((j & 1) ? HW - 1 - w : w); };
+
+  // log2 Z(i) of every row from tables a, r
+  auto logz_phase = [&](const float* a, const float* r) {
+    for (int j = 0, u = block_of(0); u < nb; u = block_of(++j)) {
+      const int i0 = 16 * u + 4 * qd;          // this lane group's rows i0 .. i0 + 3
+      const int kend = min(16 * u + 15, T - 1);
+      float mx[4] = {kNegInf, kNegInf, kNegInf, kNegInf}, s[4] = {0.f, 0.f, 0.f, 0.f};
+      for (int k0 = 0; k0 <= kend; k0 += 128) {
+        const int k = k0 + 8 * kl16;           // keys k .. k + 7
+        if (k > i0 + 3 || i0 >= T) continue;   // none of them in this lane's rows
+        const float4 a0 = *reinterpret_cast<const float4*>(a + k);
+        const float4 a1 = *reinterpret_cast<const float4*>(a + k + 4);
+        // distances (i0 + q) - (k + e) = b + 8 + q - e with b = i0 - k - 8 >= -8, a multiple of 4
+        const float* rb = r + RPAD + (i0 - k - 8);
+        const float4 w0 = *reinterpret_cast<const float4*>(rb);
+        const float4 w1 = *reinterpret_cast<const float4*>(rb + 4);
+        const float4 w2 = *reinterpret_cast<const float4*>(rb + 8);
+        const float av[8] = {a0.x, a0.y, a0.z, a0.w, a1.x, a1.y, a1.z, a1.w};
+        const float wv[12] = {w0.x, w0.y, w0.z, w0.w, w1.x, w1.y, w1.z, w1.w, w2.x, w2.y, w2.z, w2.w};
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          float x[8];
+          float cm = kNegInf;
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            x[e] = av[e] + wv[8 + q - e];
+            cm = fmaxf(cm, x[e]);
+          }
+          // no branch for a row none of whose keys is here (cm = -inf): the reference is
+          // then 0, so its exps are exp2(-inf) = 0 and the running sum keeps its value 0
+          const float m_new = fmaxf(mx[q], cm);
+          const float ref = m_new == kNegInf ? 0.f : m_new;
+          float cs = 0.f;
+#pragma unroll
+          for (int e = 0; e < 8; ++e) cs += __builtin_amdgcn_exp2f(x[e] - ref);
+          s[q] = s[q] * __builtin_amdgcn_exp2f(mx[q] - ref) + cs;
+          mx[q] = m_new;
+        }
+      }
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const float m = row16_max(mx[q]);
+        const float t = row16_sum((mx[q] == kNegInf) ? 0.f : s[q] * __builtin_amdgcn_exp2f(mx[q] - m));
+        if (kl16 == 0 && i0 + q < T) sm.z2[i0 + q] = m + __log2f(t);
+      }
+    }
+  };
+
+  int cur = 0;
+  double p1 = 1.0, p2 = 1.0;
+  for (int step = 1; step <= steps; ++step) {
+    p1 *= hp.beta1;
+    p2 *= hp.beta2;
+    const float bc1 = (float)(1.0 - p1), bc2 = (float)(1.0 - p2);
+    const float* a = sm.a2[cur];
+    const float* r = sm.r2[cur];
+    logz_phase(a, r);
+    __syncthreads();
+    // marginals: output block u < nb: columns x = 16 u + 4 qd + c, sum over t of
+    // exp2(rho2(t) + alpha2(x) - z2(x + t)); block u >= nb: distances, alpha and rho swapped
+    for (int j = 0, u = block_of(0); u < 2 * nb; u = block_of(++j)) {
+      const bool is_col = u < nb;
+      const int x0 = 16 * (is_col ? u : u - nb) + 4 * qd;
+      const float* own = is_col ? a : r + RPAD;
+      const float* oth = is_col ? r + RPAD : a;
+      const int tend = T - 1 - 16 * (is_col ? u : u - nb);   // longest line of the block
+      float ov[4], s[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int c = 0; c < 4; ++c) ov[c] = own[x0 + c];
+      for (int t0 = 0; t0 <= tend; t0 += 128) {
+        const int t = t0 + 8 * kl16;           // terms t .. t + 7
+        if (t > T - 1 - x0) continue;          // past the longest of this lane group's lines
+        const float4 o0 = *reinterpret_cast<const float4*>(oth + t);
+        const float4 o1 = *reinterpret_cast<const float4*>(oth + t + 4);
+        const float* zb = sm.z2 + x0 + t;      // z2(x0 + c + t + e) = zb[c + e]
+        const float4 z0 = *reinterpret_cast<const float4*>(zb);
+        const float4 z1 = *reinterpret_cast<const float4*>(zb + 4);
+        const float4 z3 = *reinterpret_cast<const float4*>(zb + 8);
+        const float tv[8] = {o0.x, o0.y, o0.z, o0.w, o1.x, o1.y, o1.z, o1.w};
+        const float zv[12] = {z0.x, z0.y, z0.z, z0.w, z1.x, z1.y, z1.z, z1.w, z3.x, z3.y, z3.z, z3.w};
+#pragma unroll
+        for (int c = 0; c < 4; ++c)
+#pragma unroll
+          for (int e = 0; e < 8; ++e) s[c] += __builtin_amdgcn_exp2f(tv[e] + ov[c] - zv[c + e]);
+      }
+#pragma unroll
+      for (int c = 0; c < 4; ++c) s[c] = row16_sum(s[c]);
+      if (kl16 == 0) {
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+          const int x = x0 + c;
+          if (x >= T) continue;
+          const int k = is_col ? x : T + x;
+          const float g = (s[c] - sm.tgt[k]) * inv_t;
+          const float mm = hp.beta1 * sm.mom[k] + (1.f - hp.beta1) * g;
+          const float vv = hp.beta2 * sm.vel[k] + (1.f - hp.beta2) * g * g;
+          sm.mom[k] = mm;
+          sm.vel[k] = vv;
+          const float nv = sm.par[k] - hp.lr * (mm / bc1) / (sqrtf(vv / bc2) + hp.eps);
+          sm.par[k] = nv;
+          if (is_col) sm.a2[cur ^ 1][x] = nv * kLog2e;
+          else sm.r2[cur ^ 1][RPAD + x] = nv * kLog2e;
+        }
+      }
+    }
+    __syncthreads();
+    cur ^= 1;
+  }
+
+  logz_phase(sm.a2[cur], sm.r2[cur]);
+  __syncthreads();
+  // the fitted tables, and the mean row KL (1/T) [sum log Z - alpha.col - rho.dist - sum ent]
+  double acc = 0.0;
+  for (int x = tid; x < T; x += 64 * HW) {
+    const float a = sm.par[x], r = sm.par[T + x];
+    alpha[hb + x] = a;
+    rho[hb + x] = r;
+    acc += (double)(sm.z2[x] * kLn2) - (double)a * sm.tgt[x] - (double)r * sm.tgt[T + x] - (double)ent[hb + x];
+  }
+  acc = wave_sum(acc);
+  if (lane == 0) sm.red[w] = acc;
+  __syncthreads();
+  if (tid == 0) {
+    double t = 0.0;
+    for (int x = 0; x < HW; ++x) t += sm.red[x];
+    kl[h] = (float)(t / T);
+  }
+}
+
 int elementwise_blocks(size_t n) { return (int)std::min<size_t>((n + 255) / 256, 4096); }
 
 size_t pad64(size_t n) { return (n + 63) / 64 * 64; }
@@ -347,9 +597,26 @@ hipError_t launch_compact_marginals(int H, int T, const float* alpha, const floa
 
 size_t fit_workspace_floats(int H, int T) { return 7 * pad64((size_t)H * T); }
 
+bool fit_per_head(const FitArgs& f) {
+  if (f.schedule == kFitPerHead) return true;
+  return f.schedule == kFitAuto && f.T <= kFitHeadMaxT && (f.H >= kFitHeadMinHeads || f.T <= kFitHeadShortT);
+}
+
 hipError_t launch_compact_fit(const FitArgs& f, const float* col, const float* dist, const float* ent,
                               float* alpha, float* rho, float* kl, float* ws, hipStream_t s) {
   const int H = f.H, T = f.T;
+  if (fit_per_head(f)) {
+    const AdamHyper hp{f.lr, f.beta1, f.beta2, f.eps};
+    prof_begin("fit_head", s);
+    if (T <= 1024)
+      hipLaunchKernelGGL(fit_head_kernel<1024>, dim3(H), dim3(64 * HW), 0, s, T, f.steps, hp, col, dist, ent,
+                         alpha, rho, kl);
+    else
+      hipLaunchKernelGGL(fit_head_kernel<kFitHeadMaxT>, dim3(H), dim3(64 * HW), 0, s, T, f.steps, hp, col, dist,
+                         ent, alpha, rho, kl);
+    prof_end(s);
+    return hipGetLastError();
+  }
   const size_t n = pad64((size_t)H * T);
   float* logz = ws;
   float* alt_alpha = ws + n;

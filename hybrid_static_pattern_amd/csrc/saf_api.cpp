@@ -341,7 +341,12 @@ static saf_status validate_fit(const saf_fit_desc* d, saf::FitArgs* f) {
   if (!(d->beta1 >= 0.f && d->beta1 < 1.f) || !(d->beta2 >= 0.f && d->beta2 < 1.f))
     return fail(SAF_EINVAL, "beta1 and beta2 must lie in [0, 1)");
   if (!(d->eps >= 0.f) || !std::isfinite(d->eps)) return fail(SAF_EINVAL, "eps must be finite and >= 0");
-  *f = saf::FitArgs{d->H, d->T, d->steps, d->lr, d->beta1, d->beta2, d->eps};
+  if (d->schedule < saf::kFitAuto || d->schedule > saf::kFitPerHead)
+    return fail(SAF_EINVAL, "schedule must be SAF_FIT_AUTO, SAF_FIT_PER_STEP or SAF_FIT_PER_HEAD (got %d)",
+                d->schedule);
+  if (d->schedule == saf::kFitPerHead && d->T > saf::kFitHeadMaxT)
+    return fail(SAF_EUNSUPPORTED, "SAF_FIT_PER_HEAD needs T <= %d (got %d)", saf::kFitHeadMaxT, d->T);
+  *f = saf::FitArgs{d->H, d->T, d->steps, d->lr, d->beta1, d->beta2, d->eps, d->schedule};
   return SAF_OK;
 }
 

@@ -78,10 +78,22 @@ hipError_t launch_var_score(const VarArgs& a, const void* q, const void* k, floa
 hipError_t launch_sharp_mean(const VarArgs& a, const void* q, const void* k, float* out, hipStream_t s);
 
 // Compact pattern fit.
+// Fit schedules (the values of saf_fit_desc.schedule) and the per-head kernel's limits: it
+// keeps a whole head in one workgroup's LDS (T <= kFitHeadMaxT) and is chosen automatically
+// for kFitHeadMinHeads heads or more, or for lines of at most kFitHeadShortT. Measured at
+// T = 1024 (400 steps): the per-step launches take about 2.7 ms + 0.44 ms per head, the
+// per-head kernel 36 ms for up to 256 heads (one workgroup per CU), both scaling with T^2
+// above their launch costs.
+constexpr int kFitAuto = 0, kFitPerStep = 1, kFitPerHead = 2;
+constexpr int kFitHeadMaxT = 2048;
+constexpr int kFitHeadMinHeads = 80;
+constexpr int kFitHeadShortT = 256;
 struct FitArgs {
   int H, T, steps;
   float lr, beta1, beta2, eps;
+  int schedule;
 };
+bool fit_per_head(const FitArgs& f);
 hipError_t launch_pattern_stats(int H, int T, const float* a, float* col, float* dist, float* ent,
                                 hipStream_t s);
 hipError_t launch_compact_marginals(int H, int T, const float* alpha, const float* rho, float* logz,

@@ -54,12 +54,15 @@ class FitDesc(ctypes.Structure):
     _fields_ = [
         ("H", ctypes.c_int32), ("T", ctypes.c_int32), ("steps", ctypes.c_int32),
         ("lr", ctypes.c_float), ("beta1", ctypes.c_float), ("beta2", ctypes.c_float), ("eps", ctypes.c_float),
+        ("schedule", ctypes.c_int32),
     ]
 
 
 # Fit settings: 400 Adam steps (the page); lr, betas and eps are a reading (the page names
 # only the optimiser); acceptance at a mean row KL of 0.2 nat (the page).
 FIT_STEPS, FIT_LR, FIT_BETA1, FIT_BETA2, FIT_EPS, FIT_MAX_KL = 400, 0.1, 0.9, 0.999, 1e-8, 0.2
+# saf_fit_schedule
+SAF_FIT_AUTO, SAF_FIT_PER_STEP, SAF_FIT_PER_HEAD = 0, 1, 2
 
 _lib = None
 
@@ -339,19 +342,21 @@ def compact_marginals(alpha, rho, logz=None, col=None, dist=None):
     return tuple(outs)
 
 
-def _fit_desc(H, T, steps, lr, beta1, beta2, eps):
-    return FitDesc(H, T, int(steps), float(lr), float(beta1), float(beta2), float(eps))
+def _fit_desc(H, T, steps, lr, beta1, beta2, eps, schedule=SAF_FIT_AUTO):
+    return FitDesc(H, T, int(steps), float(lr), float(beta1), float(beta2), float(eps), int(schedule))
 
 
-def fit_workspace_size(H, T, steps=FIT_STEPS, lr=FIT_LR, beta1=FIT_BETA1, beta2=FIT_BETA2, eps=FIT_EPS) -> int:
-    d = _fit_desc(H, T, steps, lr, beta1, beta2, eps)
+def fit_workspace_size(H, T, steps=FIT_STEPS, lr=FIT_LR, beta1=FIT_BETA1, beta2=FIT_BETA2, eps=FIT_EPS,
+                       schedule=SAF_FIT_AUTO) -> int:
+    d = _fit_desc(H, T, steps, lr, beta1, beta2, eps, schedule)
     return int(load().saf_fit_workspace_size(ctypes.byref(d)))
 
 
 def compact_fit(col, dist, ent, alpha=None, rho=None, kl=None, steps=FIT_STEPS, lr=FIT_LR,
-                beta1=FIT_BETA1, beta2=FIT_BETA2, eps=FIT_EPS, workspace=None):
+                beta1=FIT_BETA1, beta2=FIT_BETA2, eps=FIT_EPS, workspace=None, schedule=SAF_FIT_AUTO):
     """Fits alpha, rho [H,T] to targets with statistics (col, dist, ent) (saf_compact_fit).
     alpha, rho: the starting point, updated in place (zeros, the uniform pattern, when None).
+    schedule: SAF_FIT_AUTO, SAF_FIT_PER_STEP or SAF_FIT_PER_HEAD.
     Returns (alpha, rho, kl [H] float32: mean row KL of each fitted pattern)."""
     lib = load()
     _need(col, "col", dtype=torch.float32)
@@ -364,7 +369,7 @@ def compact_fit(col, dist, ent, alpha=None, rho=None, kl=None, steps=FIT_STEPS, 
     _need(kl, "kl", shape=(H,), dtype=torch.float32, device=dev)
     if dist is None or ent is None:
         raise ValueError("dist and ent are required")
-    d = _fit_desc(H, T, steps, lr, beta1, beta2, eps)
+    d = _fit_desc(H, T, steps, lr, beta1, beta2, eps, schedule)
     need = int(lib.saf_fit_workspace_size(ctypes.byref(d)))
     if workspace is None:
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)

@@ -176,14 +176,24 @@ saf_status saf_pattern_stats(int32_t H, int32_t T, const float* a, float* col, f
 saf_status saf_compact_marginals(int32_t H, int32_t T, const float* alpha, const float* rho,
                                  float* logz, float* col, float* dist, void* stream);
 
+/* How saf_compact_fit spreads the work (the results agree to float32 rounding):
+ * SAF_FIT_PER_STEP launches two kernels per Adam step over all heads, each head spread over
+ * many CUs, its state in the workspace; SAF_FIT_PER_HEAD runs the whole fit in one launch,
+ * one workgroup per head with the head's state in LDS (T <= 2048; the workspace is not
+ * used); SAF_FIT_AUTO takes SAF_FIT_PER_HEAD when T <= 2048 and there are 80 heads or more
+ * or T <= 256, SAF_FIT_PER_STEP otherwise. */
+typedef enum { SAF_FIT_AUTO = 0, SAF_FIT_PER_STEP = 1, SAF_FIT_PER_HEAD = 2 } saf_fit_schedule;
+
 /* One fit of H patterns of length T: `steps` Adam steps (the page uses 400) with learning
  * rate lr, moment decays beta1 and beta2 and denominator offset eps (a reading, since the
  * page names only the optimiser: 0.1, 0.9, 0.999, 1e-8). lr > 0, 0 <= beta < 1, eps >= 0,
- * steps >= 0, H in [1, 65535], T >= 1, H * T <= 2^31. */
+ * steps >= 0, H in [1, 65535], T >= 1, H * T <= 2^31; schedule a saf_fit_schedule value
+ * (SAF_EINVAL otherwise; SAF_EUNSUPPORTED for SAF_FIT_PER_HEAD with T > 2048). */
 typedef struct {
   int32_t H, T;
   int32_t steps;
   float lr, beta1, beta2, eps;
+  int32_t schedule;
 } saf_fit_desc;
 
 /* Workspace bytes saf_compact_fit needs (0 on a NULL or invalid descriptor). */

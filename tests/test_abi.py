@@ -133,6 +133,17 @@ def test_fit_contract(lib):
                                    None) == saf.SAF_EINVAL
     assert lib.saf_compact_fit(ctypes.byref(good), FAKE, FAKE, None, FAKE, FAKE, FAKE, FAKE, need,
                                None) == saf.SAF_EINVAL
+    # schedules: unknown values are rejected, the per-head one needs T <= 2048
+    for sched in (-1, 3):
+        bad = saf.FitDesc(3, 100, 400, 0.1, 0.9, 0.999, 1e-8, sched)
+        assert lib.saf_fit_workspace_size(ctypes.byref(bad)) == 0
+        assert lib.saf_compact_fit(ctypes.byref(bad), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 1 << 30,
+                                   None) == saf.SAF_EINVAL
+    long_t = saf.FitDesc(3, 2049, 400, 0.1, 0.9, 0.999, 1e-8, saf.SAF_FIT_PER_HEAD)
+    assert lib.saf_compact_fit(ctypes.byref(long_t), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 1 << 30,
+                               None) == saf.SAF_EUNSUPPORTED
+    assert lib.saf_fit_workspace_size(ctypes.byref(saf.FitDesc(3, 2049, 400, 0.1, 0.9, 0.999, 1e-8,
+                                                               saf.SAF_FIT_PER_STEP))) > 0
 
 
 def test_select_fitted_matches_oracle(lib):

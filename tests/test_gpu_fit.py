@@ -65,12 +65,17 @@ def to_dev(x):
     return torch.from_numpy(np.ascontiguousarray(x, np.float32)).to(dev())
 
 
-def gpu_fit(S, A, steps=cf.FIT_STEPS, alpha0=None, rho0=None):
+# Both schedules of saf_compact_fit: two launches per Adam step over all heads, and one
+# workgroup per head for the whole fit (taken automatically from 80 heads on, or for T <= 256).
+SCHEDULES = [1, 2]
+
+
+def gpu_fit(S, A, steps=cf.FIT_STEPS, alpha0=None, rho0=None, schedule=0):
     a = to_dev(A)
     col, dist, ent = S.pattern_stats(a)
     alpha = None if alpha0 is None else to_dev(alpha0)
     rho = None if rho0 is None else to_dev(rho0)
-    alpha, rho, kl = S.compact_fit(col, dist, ent, alpha=alpha, rho=rho, steps=steps)
+    alpha, rho, kl = S.compact_fit(col, dist, ent, alpha=alpha, rho=rho, steps=steps, schedule=schedule)
     torch.cuda.synchronize()
     return alpha.cpu().numpy(), rho.cpu().numpy(), kl.cpu().numpy()
 
@@ -122,49 +127,55 @@ def test_compact_marginals(S, H, T):
 
 # ---------------------------------------------------------------- the fit
 
-def test_fit_mean_attention_targets(S):
+@pytest.mark.parametrize("sched", SCHEDULES)
+def test_fit_mean_attention_targets(S, sched):
     A = mean_attention_targets(4, 3, 160, seed=51)
-    alpha, rho, kl = gpu_fit(S, A)
+    alpha, rho, kl = gpu_fit(S, A, schedule=sched)
     for h in range(3):
         check_fit(A[h], alpha[h], rho[h], kl[h], name=f"head {h}")
 
 
-def test_fit_odd_step_count(S):
-    """An odd number of steps ends in the workspace copy of the tables (copied back)."""
+@pytest.mark.parametrize("sched", SCHEDULES)
+def test_fit_odd_step_count(S, sched):
+    """An odd number of steps ends in the second buffer of the tables (the workspace copy,
+    copied back, or the second LDS buffer)."""
     A = mean_attention_targets(3, 2, 97, seed=52)
-    alpha, rho, kl = gpu_fit(S, A, steps=37)
+    alpha, rho, kl = gpu_fit(S, A, steps=37, schedule=sched)
     for h in range(2):
         check_fit(A[h], alpha[h], rho[h], kl[h], steps=37, name=f"head {h}")
 
 
-def test_fit_recovers_representable_pattern(S):
+@pytest.mark.parametrize("sched", SCHEDULES)
+def test_fit_recovers_representable_pattern(S, sched):
     A = np.stack([representable_target(256, 61), representable_target(256, 62)])
-    alpha, rho, kl = gpu_fit(S, A)
+    alpha, rho, kl = gpu_fit(S, A, schedule=sched)
     for h in range(2):
         check_fit(A[h], alpha[h], rho[h], kl[h], name=f"head {h}")
         assert kl[h] < 1e-4
         assert np.abs(saf_oracle.frozen_probs(alpha[h], rho[h])[0] - A[h]).max() < 1e-3
 
 
-def test_fit_fixed_points_and_trivial_sizes(S):
+@pytest.mark.parametrize("sched", SCHEDULES)
+def test_fit_fixed_points_and_trivial_sizes(S, sched):
     """The uniform causal target is the starting pattern. In float32 its gradient is rounding
     noise, which Adam normalises into small steps along directions the pattern hardly depends
     on (a float32 replay moves alpha, rho by ~1e-2): the pattern must stay uniform and the KL
     ~0. At T = 1 the gradient is exactly 0 and nothing moves."""
     T = 200
     uniform = f32(np.tril(np.ones((T, T))) / np.arange(1, T + 1)[:, None])
-    alpha, rho, kl = gpu_fit(S, uniform[None])
+    alpha, rho, kl = gpu_fit(S, uniform[None], schedule=sched)
     assert np.abs(saf_oracle.frozen_probs(alpha[0], rho[0])[0] - uniform).max() < 1e-4
     assert abs(kl[0]) < 1e-5
-    alpha, rho, kl = gpu_fit(S, np.ones((2, 1, 1), np.float32))
+    alpha, rho, kl = gpu_fit(S, np.ones((2, 1, 1), np.float32), schedule=sched)
     assert np.all(alpha == 0) and np.all(rho == 0) and np.all(np.abs(kl) < 1e-7)
 
 
-def test_fit_zero_steps_reports_kl_of_start(S):
+@pytest.mark.parametrize("sched", SCHEDULES)
+def test_fit_zero_steps_reports_kl_of_start(S, sched):
     A = mean_attention_targets(3, 2, 90, seed=53)
     r = np.random.default_rng(54)
     a0, r0 = f32(0.3 * r.standard_normal((2, 90))), f32(0.3 * r.standard_normal((2, 90)))
-    alpha, rho, kl = gpu_fit(S, A, steps=0, alpha0=a0, rho0=r0)
+    alpha, rho, kl = gpu_fit(S, A, steps=0, alpha0=a0, rho0=r0, schedule=sched)
     assert np.array_equal(alpha, a0) and np.array_equal(rho, r0)
     for h in range(2):
         ref = cf.row_kl(a0[h], r0[h], A[h])
@@ -183,9 +194,35 @@ def test_fit_selection_end_to_end(S):
         assert list(S.select_fitted(s_var, kl, 0.5, thr)) == list(cf.select_fitted(s_var, kl_ref, 0.5, thr))
 
 
+@pytest.mark.parametrize("T,steps", [(1025, 40), (2048, 25)])
+def test_fit_per_head_long_lines(S, T, steps):
+    """The per-head schedule at the lengths of its larger LDS layout (T in (1024, 2048])."""
+    A = np.stack([representable_target(T, 63), mean_attention_targets(2, 1, T, seed=64)[0]])
+    alpha, rho, kl = gpu_fit(S, A, steps=steps, schedule=2)
+    for h in range(2):
+        check_fit(A[h], alpha[h], rho[h], kl[h], steps=steps, name=f"T={T} head {h}")
+
+
+def test_fit_many_heads_schedules_agree(S):
+    """80 heads (the automatic choice is then the per-head schedule): both schedules agree on
+    every fitted pattern, and two sampled heads match the oracle's fit."""
+    H, T = 80, 320
+    A = mean_attention_targets(3, H, T, seed=65)
+    a_auto, r_auto, kl_auto = gpu_fit(S, A)
+    a_step, r_step, kl_step = gpu_fit(S, A, schedule=1)
+    for h in range(H):
+        P_auto = saf_oracle.frozen_probs(a_auto[h], r_auto[h])[0]
+        P_step = saf_oracle.frozen_probs(a_step[h], r_step[h])[0]
+        assert np.abs(P_auto - P_step).max() <= P_ABS, h
+        assert abs(kl_auto[h] - kl_step[h]) <= KL_ABS + KL_REL * abs(kl_step[h]), h
+    for h in (0, 57):
+        check_fit(A[h], a_auto[h], r_auto[h], kl_auto[h], name=f"head {h}")
+
+
 # ---------------------------------------------------------------- full size, sampled
 
-def test_full_calibration_fit_sampled(S):
+@pytest.mark.parametrize("sched", SCHEDULES)
+def test_full_calibration_fit_sampled(S, sched):
     """The calibration shape (N=64, H=12, T=1024): one head's mean attention from the oracle,
     fitted on the GPU together with eleven more targets, against the oracle's fit."""
     C = inputs.CALIBRATION
@@ -196,7 +233,7 @@ def test_full_calibration_fit_sampled(S):
     A_s = f32(A_s[0])
     fill = [representable_target(T, 70 + h) for h in range(C["H"] - 1)]
     A = np.stack(fill[:h_s] + [A_s] + fill[h_s:])
-    alpha, rho, kl = gpu_fit(S, A)
+    alpha, rho, kl = gpu_fit(S, A, schedule=sched)
     check_fit(A_s, alpha[h_s], rho[h_s], kl[h_s], name="sampled head")
     assert np.all(kl[np.arange(C["H"]) != h_s] < 1e-3)
 
