@@ -438,6 +438,15 @@ def test_full_1b_half_frozen(S):
     _full(S, "l1b_fwdbwd", [(0, first_frozen)], n_frozen=8)
 
 
+def test_full_1b_all_frozen(S):
+    """Every head frozen (the frozen path the bench times alone): no ordinary item at all."""
+    _full(S, "l1b_fwdbwd", [(1, first_frozen), (0, lambda fz: 15)], n_frozen=16)
+
+
+def test_full_1b_all_dynamic(S):
+    _full(S, "l1b_fwdbwd", [(1, last_dynamic)], n_frozen=0)
+
+
 def test_full_prefill_t512(S):
     _full(S, "prefill_t512", [(63, first_frozen), (0, last_dynamic)], bwd=False)
 
