@@ -81,14 +81,16 @@ def test_fp32_forward_backward(S, B, H, T, D, frozen):
 BF16_CASES = [
     (2, 4, 300, 64, [1, 3]),      # several tiles, ragged tail
     (1, 3, 257, 128, [0]),        # ragged; folded columns 128 < 256
-    (3, 2, 130, 128, [1]),        # folded columns 384: two chunks, the second partial
+    (3, 2, 130, 128, [1]),        # folded columns 384: three forward items of 128, two dV items of 256
     (8, 2, 129, 64, [0]),         # folded columns 512: two full chunks
     (1, 2, 1, 64, [1]),           # T = 1
     (2, 3, 64, 64, []),           # all ordinary (r = 0)
     (2, 2, 200, 128, [0, 1]),     # all frozen: q, k are NULL
     (1, 2, 513, 128, [1]),        # crosses the 512-key boundary of the dK/dV tiles
     (1, 2, 700, 64, [0]),         # folded columns 64 (the narrowest frozen item), ragged
-    (3, 2, 150, 64, [1]),         # folded columns 192 in a 256-column item
+    (3, 2, 150, 64, [1]),         # folded columns 192 (two 128-column forward items at T <= 512)
+    (3, 2, 600, 64, [1]),         # folded columns 192 in a 256-column item (T > 512)
+    (5, 2, 520, 128, [0]),        # folded columns 640: three 256-column items, the last partial
 ]
 
 
