@@ -343,31 +343,53 @@ __global__ void copy_kernel(float* __restrict__ dst, const float* __restrict__ s
 
 // ---------------------------------------------------------------- one workgroup per head
 //
-// The whole fit of one head in one workgroup of 16 waves, its state in LDS: alpha and rho
-// (log2 units, two buffers: a step reads one and writes the other), log Z, and Adam's
-// moments, the parameters in natural units and the targets. A step is two phases with a
-// barrier after each, so no launch and no round trip through memory separates them. Used
-// when there are enough heads to occupy the CUs (the per-step launches above spread one
-// head over many CUs instead).
+// The whole fit of one head in one workgroup of 16 waves, its state in LDS: the parameters
+// (natural units), Adam's moments, the targets, the tables derived from the parameters at
+// the start of each step, and log Z. A step is four phases separated by barriers (ranges of
+// the parameters, tables, log Z, marginals with the Adam update), with no launch and no
+// round trip through memory between them. Used when there are enough heads to occupy the
+// CUs, or for short lines (the per-step launches spread one head over many CUs instead).
 //
-// Both phases give each 16-lane group four consecutive rows (or outputs) and each lane 8
-// consecutive keys (or terms) at a time: the 32 terms a lane forms per iteration then come
-// from 5 16-byte LDS reads (2 of one table, 3 of the other, whose 11 entries cover the 4 x 8
-// sums of the two indices), so the exps, not LDS bandwidth, bound the phases; and the
-// cross-lane reductions stay within 16-lane DPP rows (four data-parallel-primitive moves
-// instead of LDS permutes).
+// Factored terms. A term of log Z(i) or of a marginal is exp(alpha(j) + rho(i-j) - log Z(i)),
+// a product of one factor per table. With A(j) = exp2(alpha2(j) - max alpha2), R(d) =
+// exp2(rho2(d) - max rho2) (log2 units) and Zi(i) = exp2(max alpha2 + max rho2 - log2 Z(i)):
+//   log2 Z(i) = max alpha2 + max rho2 + log2 sum_{j<=i} A(j) R(i-j),  Zi(i) = 1 / that sum,
+//   colP(x)   = A(x) sum_t R(t) Zi(x+t),   distP(d) = R(d) sum_t A(t) Zi(d+t),
+// one fused multiply-add per term and no exp. This is exact up to rounding as long as no
+// factor or partial product leaves float32's normal range: with spreads (max - min, log2
+// units) sa of alpha and sr of rho, A R >= 2^-(sa+sr), Zi >= 1/T, R(t) Zi(x+t) <= 2^sa and
+// A(t) Zi(d+t) <= 2^sr (log Z(i) bounds each of its own terms), so sa + sr <= 96 keeps every
+// value within [2^-107, 2^96]. A step whose parameters spread further takes the exp path:
+// exponents shifted by the row's running max (log Z) or never positive (marginals).
 //
-// Table padding replaces masks: rho has 8 entries of -inf before distance 0 and -inf past
-// T - 1 (keys after their row get -inf), log Z has +inf past row T - 1 (terms past the end
-// of a column or distance line get exp2(-inf) = 0), alpha has 0 past T - 1 (only ever added
-// to a -inf); no sum of two infinities of opposite sign arises.
+// Both phases give each 16-lane group G consecutive rows (or outputs) and each lane 8
+// consecutive keys (or terms) at a time: the 8 G terms a lane forms per iteration come from
+// 2 16-byte LDS reads of one table and (G + 8) / 4 of the other, whose G + 7 entries cover
+// the sums of the two indices, and the reductions stay within 16-lane DPP rows. The
+// factored path, one FMA per term, takes G = 8 (1.5 bytes of LDS per term, which then bounds
+// it); the exp path G = 4 (2.5 bytes per term), its exps bounding it.
+//
+// Table padding replaces masks: factors are 0 outside their index range; on the exp path rho
+// has -inf before distance 0 and past T - 1, log Z +inf past row T - 1, alpha 0 past T - 1
+// (only ever added to a -inf), so no sum of two infinities of opposite sign arises.
 constexpr int HW = 16;            // waves per workgroup
-constexpr int RPAD = 8;           // -inf entries before rho(0)
-constexpr int TPAD = 16;          // entries past T - 1 in each table
+constexpr int RPAD = 8;           // entries before distance 0
+constexpr int TPAD = 32;          // entries past T - 1 in each table
+constexpr float kFactorSpread = 96.f;   // log2 units
 
 struct AdamHyper {
   float lr, beta1, beta2, eps;
 };
+
+// v[lane % 16] for the first N lanes of each 16-lane row: spreads the per-row results that
+// every lane of the row holds after a reduction over the row's lanes, one per lane.
+template <int N>
+__device__ __forceinline__ float pick(const float (&v)[N], int i) {
+  float r = v[0];
+#pragma unroll
+  for (int c = 1; c < N; ++c) r = i == c ? v[c] : r;
+  return r;
+}
 
 // Reductions over the 16 lanes of a DPP row (lanes 16 r .. 16 r + 15), every lane getting
 // the result: the quad permutations [1,0,3,2] and [2,3,0,1] combine lanes within quads, the
@@ -392,11 +414,15 @@ __device__ __forceinline__ float row16_max(float x) {
 
 template <int TMAX>
 struct HeadFit {
-  float a2[2][TMAX + TPAD];         // alpha * log2(e)
-  float r2[2][RPAD + TMAX + TPAD];  // rho * log2(e), rho(d) at RPAD + d
+  float a2[TMAX + TPAD];            // exp path: alpha * log2(e)
+  float r2[RPAD + TMAX + TPAD];     // exp path: rho * log2(e), rho(d) at RPAD + d
+  float fa[TMAX + TPAD];            // factored: A
+  float fr[RPAD + TMAX + TPAD];     // factored: R, R(d) at RPAD + d
   float z2[TMAX + TPAD];            // log2 Z
+  float zi[TMAX + TPAD];            // factored: Zi
   float par[2 * TMAX];              // alpha, then rho (natural units)
   float mom[2 * TMAX], vel[2 * TMAX], tgt[2 * TMAX];   // Adam moments; col, then dist
+  float rng[HW][4];                 // per wave: max alpha, -min alpha, max rho, -min rho
   double red[HW];
 };
 
@@ -414,33 +440,37 @@ __global__ __launch_bounds__(64 * HW) void fit_head_kernel(int T, int steps, Ada
   const size_t hb = (size_t)h * T;
   const float inv_t = 1.f / T;
 
+  // parameters, moments, targets; the padding of every table (entries [0, T) are written
+  // at the start of each step)
   for (int x = tid; x < TMAX + TPAD; x += 64 * HW) {
-    const float a = x < T ? alpha[hb + x] : 0.f;
-    const float r = x < T ? rho[hb + x] : kNegInf;
-    sm.a2[0][x] = x < T ? a * kLog2e : 0.f;
-    sm.a2[1][x] = 0.f;
-    sm.r2[0][RPAD + x] = x < T ? r * kLog2e : kNegInf;
-    sm.r2[1][RPAD + x] = kNegInf;
-    sm.z2[x] = __builtin_huge_valf();
     if (x < T) {
-      sm.par[x] = a;
-      sm.par[T + x] = r;
+      sm.par[x] = alpha[hb + x];
+      sm.par[T + x] = rho[hb + x];
       sm.tgt[x] = col[hb + x];
       sm.tgt[T + x] = dist[hb + x];
       sm.mom[x] = sm.mom[T + x] = 0.f;
       sm.vel[x] = sm.vel[T + x] = 0.f;
+    } else {
+      sm.a2[x] = 0.f;
+      sm.r2[RPAD + x] = kNegInf;
+      sm.fa[x] = 0.f;
+      sm.fr[RPAD + x] = 0.f;
+      sm.z2[x] = __builtin_huge_valf();
+      sm.zi[x] = 0.f;
     }
   }
-  if (tid < RPAD) sm.r2[0][tid] = sm.r2[1][tid] = kNegInf;
-  __syncthreads();
+  if (tid < RPAD) {
+    sm.r2[tid] = kNegInf;
+    sm.fr[tid] = 0.f;
+  }
 
   const int nb = (T + 15) / 16;   // 16-row (16-output) blocks
   // Block j of wave w: the waves take the blocks in rounds of HW, in reverse order every
   // other round, so that the lengths (which grow or shrink with the block index) even out.
   auto block_of = [&](int j) { return HW * j + ((j & 1) ? HW - 1 - w : w); };
 
-  // log2 Z(i) of every row from tables a, r
-  auto logz_phase = [&](const float* a, const float* r) {
+  // log2 Z(i) of every row, exp path
+  auto logz_exp = [&]() {
     for (int j = 0, u = block_of(0); u < nb; u = block_of(++j)) {
       const int i0 = 16 * u + 4 * qd;          // this lane group's rows i0 .. i0 + 3
       const int kend = min(16 * u + 15, T - 1);
@@ -448,10 +478,10 @@ __global__ __launch_bounds__(64 * HW) void fit_head_kernel(int T, int steps, Ada
       for (int k0 = 0; k0 <= kend; k0 += 128) {
         const int k = k0 + 8 * kl16;           // keys k .. k + 7
         if (k > i0 + 3 || i0 >= T) continue;   // none of them in this lane's rows
-        const float4 a0 = *reinterpret_cast<const float4*>(a + k);
-        const float4 a1 = *reinterpret_cast<const float4*>(a + k + 4);
+        const float4 a0 = *reinterpret_cast<const float4*>(sm.a2 + k);
+        const float4 a1 = *reinterpret_cast<const float4*>(sm.a2 + k + 4);
         // distances (i0 + q) - (k + e) = b + 8 + q - e with b = i0 - k - 8 >= -8, a multiple of 4
-        const float* rb = r + RPAD + (i0 - k - 8);
+        const float* rb = sm.r2 + RPAD + (i0 - k - 8);
         const float4 w0 = *reinterpret_cast<const float4*>(rb);
         const float4 w1 = *reinterpret_cast<const float4*>(rb + 4);
         const float4 w2 = *reinterpret_cast<const float4*>(rb + 8);
@@ -477,32 +507,75 @@ __global__ __launch_bounds__(64 * HW) void fit_head_kernel(int T, int steps, Ada
           mx[q] = m_new;
         }
       }
+      float zr[4];
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
         const float m = row16_max(mx[q]);
         const float t = row16_sum((mx[q] == kNegInf) ? 0.f : s[q] * __builtin_amdgcn_exp2f(mx[q] - m));
-        if (kl16 == 0 && i0 + q < T) sm.z2[i0 + q] = m + __log2f(t);
+        zr[q] = m + __log2f(t);
+      }
+      if (kl16 < 4 && i0 + kl16 < T) sm.z2[i0 + kl16] = pick(zr, kl16);   // lane q: row i0 + q
+    }
+  };
+
+  // log2 Z(i) and Zi(i) of every row, factored (32-row blocks, 8 rows per lane group);
+  // top = max alpha2 + max rho2
+  const int nb32 = (T + 31) / 32;
+  auto logz_fac = [&](float top) {
+    for (int j = 0, u = block_of(0); u < nb32; u = block_of(++j)) {
+      const int i0 = 32 * u + 8 * qd;          // rows i0 .. i0 + 7
+      const int kend = min(32 * u + 31, T - 1);
+      float s[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+      for (int k0 = 0; k0 <= kend; k0 += 128) {
+        const int k = k0 + 8 * kl16;
+        if (k > i0 + 7 || i0 >= T) continue;
+        const float4 a0 = *reinterpret_cast<const float4*>(sm.fa + k);
+        const float4 a1 = *reinterpret_cast<const float4*>(sm.fa + k + 4);
+        // distances (i0 + q) - (k + e) = b + 8 + q - e, b = i0 - k - 8 >= -8 (a multiple of 8)
+        const float* rb = sm.fr + RPAD + (i0 - k - 8);
+        float wv[16];
+#pragma unroll
+        for (int y = 0; y < 4; ++y) {
+          const float4 v = *reinterpret_cast<const float4*>(rb + 4 * y);
+          wv[4 * y] = v.x;
+          wv[4 * y + 1] = v.y;
+          wv[4 * y + 2] = v.z;
+          wv[4 * y + 3] = v.w;
+        }
+        const float av[8] = {a0.x, a0.y, a0.z, a0.w, a1.x, a1.y, a1.z, a1.w};
+#pragma unroll
+        for (int q = 0; q < 8; ++q)
+#pragma unroll
+          for (int e = 0; e < 8; ++e) s[q] = __builtin_fmaf(av[e], wv[8 + q - e], s[q]);
+      }
+#pragma unroll
+      for (int q = 0; q < 8; ++q) s[q] = row16_sum(s[q]);
+      if (kl16 < 8 && i0 + kl16 < T) {   // lane q: row i0 + q
+        const float t = pick(s, kl16);
+        sm.z2[i0 + kl16] = top + __log2f(t);
+        sm.zi[i0 + kl16] = 1.f / t;
       }
     }
   };
 
-  int cur = 0;
-  double p1 = 1.0, p2 = 1.0;
-  for (int step = 1; step <= steps; ++step) {
-    p1 *= hp.beta1;
-    p2 *= hp.beta2;
-    const float bc1 = (float)(1.0 - p1), bc2 = (float)(1.0 - p2);
-    const float* a = sm.a2[cur];
-    const float* r = sm.r2[cur];
-    logz_phase(a, r);
-    __syncthreads();
-    // marginals: output block u < nb: columns x = 16 u + 4 qd + c, sum over t of
-    // exp2(rho2(t) + alpha2(x) - z2(x + t)); block u >= nb: distances, alpha and rho swapped
+  // Adam on parameter k (alpha(x) at k = x, rho(d) at k = T + d) with marginal `sum`
+  auto adam = [&](int k, float sum, float bc1, float bc2) {
+    const float g = (sum - sm.tgt[k]) * inv_t;
+    const float mm = hp.beta1 * sm.mom[k] + (1.f - hp.beta1) * g;
+    const float vv = hp.beta2 * sm.vel[k] + (1.f - hp.beta2) * g * g;
+    sm.mom[k] = mm;
+    sm.vel[k] = vv;
+    sm.par[k] = sm.par[k] - hp.lr * (mm / bc1) / (sqrtf(vv / bc2) + hp.eps);
+  };
+
+  // Marginals and the Adam step, exp path: output block u < nb: columns x = 16 u + 4 qd + c,
+  // sum_t exp2(rho2(t) + alpha2(x) - z2(x + t)); u >= nb: distances (alpha and rho swapped).
+  auto marginals_exp = [&](float bc1, float bc2) {
     for (int j = 0, u = block_of(0); u < 2 * nb; u = block_of(++j)) {
       const bool is_col = u < nb;
       const int x0 = 16 * (is_col ? u : u - nb) + 4 * qd;
-      const float* own = is_col ? a : r + RPAD;
-      const float* oth = is_col ? r + RPAD : a;
+      const float* own = is_col ? sm.a2 : sm.r2 + RPAD;
+      const float* oth = is_col ? sm.r2 + RPAD : sm.a2;
       const int tend = T - 1 - 16 * (is_col ? u : u - nb);   // longest line of the block
       float ov[4], s[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -512,7 +585,7 @@ __global__ __launch_bounds__(64 * HW) void fit_head_kernel(int T, int steps, Ada
         if (t > T - 1 - x0) continue;          // past the longest of this lane group's lines
         const float4 o0 = *reinterpret_cast<const float4*>(oth + t);
         const float4 o1 = *reinterpret_cast<const float4*>(oth + t + 4);
-        const float* zb = sm.z2 + x0 + t;      // z2(x0 + c + t + e) = zb[c + e]
+        const float* zb = sm.z2 + x0 + t;      // entry x0 + c + t + e is zb[c + e]
         const float4 z0 = *reinterpret_cast<const float4*>(zb);
         const float4 z1 = *reinterpret_cast<const float4*>(zb + 4);
         const float4 z3 = *reinterpret_cast<const float4*>(zb + 8);
@@ -525,30 +598,96 @@ __global__ __launch_bounds__(64 * HW) void fit_head_kernel(int T, int steps, Ada
       }
 #pragma unroll
       for (int c = 0; c < 4; ++c) s[c] = row16_sum(s[c]);
-      if (kl16 == 0) {
+      const int x = x0 + kl16;   // lane c: output x0 + c
+      if (kl16 < 4 && x < T) adam(is_col ? x : T + x, pick(s, kl16), bc1, bc2);
+    }
+  };
+
+  // Marginals and the Adam step, factored: 32-output blocks, 8 outputs per lane group;
+  // columns sum_t R(t) Zi(x + t) times A(x), distances sum_t A(t) Zi(d + t) times R(d).
+  auto marginals_fac = [&](float bc1, float bc2) {
+    for (int j = 0, u = block_of(0); u < 2 * nb32; u = block_of(++j)) {
+      const bool is_col = u < nb32;
+      const int x0 = 32 * (is_col ? u : u - nb32) + 8 * qd;
+      const float* own = is_col ? sm.fa : sm.fr + RPAD;
+      const float* oth = is_col ? sm.fr + RPAD : sm.fa;
+      const int tend = T - 1 - 32 * (is_col ? u : u - nb32);
+      float s[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+      for (int t0 = 0; t0 <= tend; t0 += 128) {
+        const int t = t0 + 8 * kl16;
+        if (t > T - 1 - x0) continue;
+        const float4 o0 = *reinterpret_cast<const float4*>(oth + t);
+        const float4 o1 = *reinterpret_cast<const float4*>(oth + t + 4);
+        const float* zb = sm.zi + x0 + t;      // entry x0 + c + t + e is zb[c + e]
+        float zv[16];
 #pragma unroll
-        for (int c = 0; c < 4; ++c) {
-          const int x = x0 + c;
-          if (x >= T) continue;
-          const int k = is_col ? x : T + x;
-          const float g = (s[c] - sm.tgt[k]) * inv_t;
-          const float mm = hp.beta1 * sm.mom[k] + (1.f - hp.beta1) * g;
-          const float vv = hp.beta2 * sm.vel[k] + (1.f - hp.beta2) * g * g;
-          sm.mom[k] = mm;
-          sm.vel[k] = vv;
-          const float nv = sm.par[k] - hp.lr * (mm / bc1) / (sqrtf(vv / bc2) + hp.eps);
-          sm.par[k] = nv;
-          if (is_col) sm.a2[cur ^ 1][x] = nv * kLog2e;
-          else sm.r2[cur ^ 1][RPAD + x] = nv * kLog2e;
+        for (int y = 0; y < 4; ++y) {
+          const float4 v = *reinterpret_cast<const float4*>(zb + 4 * y);
+          zv[4 * y] = v.x;
+          zv[4 * y + 1] = v.y;
+          zv[4 * y + 2] = v.z;
+          zv[4 * y + 3] = v.w;
         }
+        const float tv[8] = {o0.x, o0.y, o0.z, o0.w, o1.x, o1.y, o1.z, o1.w};
+#pragma unroll
+        for (int c = 0; c < 8; ++c)
+#pragma unroll
+          for (int e = 0; e < 8; ++e) s[c] = __builtin_fmaf(tv[e], zv[c + e], s[c]);
+      }
+#pragma unroll
+      for (int c = 0; c < 8; ++c) s[c] = row16_sum(s[c]);
+      const int x = x0 + kl16;   // lane c: output x0 + c
+      if (kl16 < 8 && x < T) adam(is_col ? x : T + x, pick(s, kl16) * own[x], bc1, bc2);
+    }
+  };
+
+  double p1 = 1.0, p2 = 1.0;
+  for (int step = 1;; ++step) {
+    // spreads of the current parameters (all waves end up with the same values)
+    float st[4] = {kNegInf, kNegInf, kNegInf, kNegInf};
+    for (int x = tid; x < T; x += 64 * HW) {
+      const float a = sm.par[x], r = sm.par[T + x];
+      st[0] = fmaxf(st[0], a);
+      st[1] = fmaxf(st[1], -a);
+      st[2] = fmaxf(st[2], r);
+      st[3] = fmaxf(st[3], -r);
+    }
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      st[c] = wave_max(st[c]);
+      if (lane == 0) sm.rng[w][c] = st[c];
+    }
+    __syncthreads();
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      st[c] = sm.rng[0][c];
+      for (int v = 1; v < HW; ++v) st[c] = fmaxf(st[c], sm.rng[v][c]);
+    }
+    const float am2 = st[0] * kLog2e, rm2 = st[2] * kLog2e;
+    // false for a NaN or infinite spread
+    const bool fac = (st[0] + st[1] + st[2] + st[3]) * kLog2e <= kFactorSpread;
+    for (int x = tid; x < T; x += 64 * HW) {
+      const float a = sm.par[x] * kLog2e, r = sm.par[T + x] * kLog2e;
+      if (fac) {
+        sm.fa[x] = __builtin_amdgcn_exp2f(a - am2);
+        sm.fr[RPAD + x] = __builtin_amdgcn_exp2f(r - rm2);
+      } else {
+        sm.a2[x] = a;
+        sm.r2[RPAD + x] = r;
       }
     }
     __syncthreads();
-    cur ^= 1;
+    if (fac) logz_fac(am2 + rm2);
+    else logz_exp();
+    __syncthreads();
+    if (step > steps) break;
+    p1 *= hp.beta1;
+    p2 *= hp.beta2;
+    if (fac) marginals_fac((float)(1.0 - p1), (float)(1.0 - p2));
+    else marginals_exp((float)(1.0 - p1), (float)(1.0 - p2));
+    __syncthreads();
   }
 
-  logz_phase(sm.a2[cur], sm.r2[cur]);
-  __syncthreads();
   // the fitted tables, and the mean row KL (1/T) [sum log Z - alpha.col - rho.dist - sum ent]
   double acc = 0.0;
   for (int x = tid; x < T; x += 64 * HW) {

@@ -180,7 +180,7 @@ saf_status saf_compact_marginals(int32_t H, int32_t T, const float* alpha, const
  * SAF_FIT_PER_STEP launches two kernels per Adam step over all heads, each head spread over
  * many CUs, its state in the workspace; SAF_FIT_PER_HEAD runs the whole fit in one launch,
  * one workgroup per head with the head's state in LDS (T <= 2048; the workspace is not
- * used); SAF_FIT_AUTO takes SAF_FIT_PER_HEAD when T <= 2048 and there are 80 heads or more
+ * used); SAF_FIT_AUTO takes SAF_FIT_PER_HEAD when T <= 2048 and there are 16 heads or more
  * or T <= 256, SAF_FIT_PER_STEP otherwise. */
 typedef enum { SAF_FIT_AUTO = 0, SAF_FIT_PER_STEP = 1, SAF_FIT_PER_HEAD = 2 } saf_fit_schedule;
 

@@ -66,7 +66,7 @@ def to_dev(x):
 
 
 # Both schedules of saf_compact_fit: two launches per Adam step over all heads, and one
-# workgroup per head for the whole fit (taken automatically from 80 heads on, or for T <= 256).
+# workgroup per head for the whole fit (taken automatically from 16 heads on, or for T <= 256).
 SCHEDULES = [1, 2]
 
 
@@ -80,11 +80,14 @@ def gpu_fit(S, A, steps=cf.FIT_STEPS, alpha0=None, rho0=None, schedule=0):
     return alpha.cpu().numpy(), rho.cpu().numpy(), kl.cpu().numpy()
 
 
-def check_fit(A, alpha, rho, kl, steps=cf.FIT_STEPS, name=""):
-    """One head: the GPU's fitted pattern and KL against the oracle's fit of the same target."""
+def check_fit(A, alpha, rho, kl, steps=cf.FIT_STEPS, name="", alpha0=None, rho0=None):
+    """One head: the GPU's fitted pattern and KL against the oracle's fit of the same target
+    from the same starting point (zeros by default)."""
     T = A.shape[0]
     col, dist, _ = cf.pattern_stats(A)
-    a_ref, r_ref = cf.adam_fit(col, dist, np.zeros(T), np.zeros(T), steps=steps)
+    a0 = np.zeros(T) if alpha0 is None else np.asarray(alpha0, np.float64)
+    r0 = np.zeros(T) if rho0 is None else np.asarray(rho0, np.float64)
+    a_ref, r_ref = cf.adam_fit(col, dist, a0, r0, steps=steps)
     P_ref = saf_oracle.frozen_probs(a_ref, r_ref)[0]
     P_gpu = saf_oracle.frozen_probs(alpha, rho)[0]
     err = np.abs(P_gpu - P_ref).max()
@@ -201,6 +204,21 @@ def test_fit_per_head_long_lines(S, T, steps):
     alpha, rho, kl = gpu_fit(S, A, steps=steps, schedule=2)
     for h in range(2):
         check_fit(A[h], alpha[h], rho[h], kl[h], steps=steps, name=f"T={T} head {h}")
+
+
+@pytest.mark.parametrize("sched", SCHEDULES)
+@pytest.mark.parametrize("low", [-70.0, -200.0])
+def test_fit_wide_tables(S, sched, low):
+    """A start whose alpha spans more than 96 / log2(e) = 66.5: the per-head kernel computes
+    such steps with exps instead of factored products, throughout (low = -200, which 400
+    steps of at most lr each cannot lift) or until Adam has narrowed the spread (-70)."""
+    A = mean_attention_targets(3, 2, 130, seed=66)
+    a0 = np.zeros((2, 130), np.float32)
+    a0[:, 7] = low
+    a0[1, 100] = low / 2
+    alpha, rho, kl = gpu_fit(S, A, alpha0=a0, rho0=np.zeros_like(a0), schedule=sched)
+    for h in range(2):
+        check_fit(A[h], alpha[h], rho[h], kl[h], name=f"head {h}", alpha0=a0[h])
 
 
 def test_fit_many_heads_schedules_agree(S):
