@@ -412,14 +412,20 @@ __device__ __forceinline__ float row16_max(float x) {
   return fmaxf(x, dpp_mov<0x140>(x));
 }
 
+// The factored tables keep 4 floats of padding after every 64 entries (entry i at
+// i + 4 (i / 64)): the lane groups read at 8-float strides, which would otherwise put lanes
+// l and l + 8 of one hardware read group on the same LDS banks.
+__device__ __forceinline__ int padx(int i) { return i + ((i >> 6) << 2); }
+constexpr int padded(int n) { return n + (n + 63) / 64 * 4; }
+
 template <int TMAX>
 struct HeadFit {
   float a2[TMAX + TPAD];            // exp path: alpha * log2(e)
   float r2[RPAD + TMAX + TPAD];     // exp path: rho * log2(e), rho(d) at RPAD + d
-  float fa[TMAX + TPAD];            // factored: A
-  float fr[RPAD + TMAX + TPAD];     // factored: R, R(d) at RPAD + d
+  float fa[padded(TMAX + TPAD)];          // factored: A (padded layout)
+  float fr[padded(RPAD + TMAX + TPAD)];   // factored: R, R(d) at RPAD + d (padded layout)
   float z2[TMAX + TPAD];            // log2 Z
-  float zi[TMAX + TPAD];            // factored: Zi
+  float zi[padded(TMAX + TPAD)];          // factored: Zi (padded layout)
   float par[2 * TMAX];              // alpha, then rho (natural units)
   float mom[2 * TMAX], vel[2 * TMAX], tgt[2 * TMAX];   // Adam moments; col, then dist
   float rng[HW][4];                 // per wave: max alpha, -min alpha, max rho, -min rho
@@ -453,15 +459,15 @@ __global__ __launch_bounds__(64 * HW) void fit_head_kernel(int T, int steps, Ada
     } else {
       sm.a2[x] = 0.f;
       sm.r2[RPAD + x] = kNegInf;
-      sm.fa[x] = 0.f;
-      sm.fr[RPAD + x] = 0.f;
+      sm.fa[padx(x)] = 0.f;
+      sm.fr[padx(RPAD + x)] = 0.f;
       sm.z2[x] = __builtin_huge_valf();
-      sm.zi[x] = 0.f;
+      sm.zi[padx(x)] = 0.f;
     }
   }
   if (tid < RPAD) {
     sm.r2[tid] = kNegInf;
-    sm.fr[tid] = 0.f;
+    sm.fr[padx(tid)] = 0.f;
   }
 
   const int nb = (T + 15) / 16;   // 16-row (16-output) blocks
@@ -529,14 +535,14 @@ __global__ __launch_bounds__(64 * HW) void fit_head_kernel(int T, int steps, Ada
       for (int k0 = 0; k0 <= kend; k0 += 128) {
         const int k = k0 + 8 * kl16;
         if (k > i0 + 7 || i0 >= T) continue;
-        const float4 a0 = *reinterpret_cast<const float4*>(sm.fa + k);
-        const float4 a1 = *reinterpret_cast<const float4*>(sm.fa + k + 4);
+        const float4 a0 = *reinterpret_cast<const float4*>(sm.fa + padx(k));
+        const float4 a1 = *reinterpret_cast<const float4*>(sm.fa + padx(k + 4));
         // distances (i0 + q) - (k + e) = b + 8 + q - e, b = i0 - k - 8 >= -8 (a multiple of 8)
-        const float* rb = sm.fr + RPAD + (i0 - k - 8);
+        const int rb = RPAD + (i0 - k - 8);
         float wv[16];
 #pragma unroll
         for (int y = 0; y < 4; ++y) {
-          const float4 v = *reinterpret_cast<const float4*>(rb + 4 * y);
+          const float4 v = *reinterpret_cast<const float4*>(sm.fr + padx(rb + 4 * y));
           wv[4 * y] = v.x;
           wv[4 * y + 1] = v.y;
           wv[4 * y + 2] = v.z;
@@ -553,7 +559,7 @@ __global__ __launch_bounds__(64 * HW) void fit_head_kernel(int T, int steps, Ada
       if (kl16 < 8 && i0 + kl16 < T) {   // lane q: row i0 + q
         const float t = pick(s, kl16);
         sm.z2[i0 + kl16] = top + __log2f(t);
-        sm.zi[i0 + kl16] = 1.f / t;
+        sm.zi[padx(i0 + kl16)] = 1.f / t;
       }
     }
   };
@@ -609,20 +615,21 @@ __global__ __launch_bounds__(64 * HW) void fit_head_kernel(int T, int steps, Ada
     for (int j = 0, u = block_of(0); u < 2 * nb32; u = block_of(++j)) {
       const bool is_col = u < nb32;
       const int x0 = 32 * (is_col ? u : u - nb32) + 8 * qd;
-      const float* own = is_col ? sm.fa : sm.fr + RPAD;
-      const float* oth = is_col ? sm.fr + RPAD : sm.fa;
+      // own(x) at padx(own_b + x), oth(t) at padx(oth_b + t)
+      const float* own = is_col ? sm.fa : sm.fr;
+      const float* oth = is_col ? sm.fr : sm.fa;
+      const int own_b = is_col ? 0 : RPAD, oth_b = is_col ? RPAD : 0;
       const int tend = T - 1 - 32 * (is_col ? u : u - nb32);
       float s[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
       for (int t0 = 0; t0 <= tend; t0 += 128) {
         const int t = t0 + 8 * kl16;
         if (t > T - 1 - x0) continue;
-        const float4 o0 = *reinterpret_cast<const float4*>(oth + t);
-        const float4 o1 = *reinterpret_cast<const float4*>(oth + t + 4);
-        const float* zb = sm.zi + x0 + t;      // entry x0 + c + t + e is zb[c + e]
-        float zv[16];
+        const float4 o0 = *reinterpret_cast<const float4*>(oth + padx(oth_b + t));
+        const float4 o1 = *reinterpret_cast<const float4*>(oth + padx(oth_b + t + 4));
+        float zv[16];   // Zi(x0 + t + y), y = c + e
 #pragma unroll
         for (int y = 0; y < 4; ++y) {
-          const float4 v = *reinterpret_cast<const float4*>(zb + 4 * y);
+          const float4 v = *reinterpret_cast<const float4*>(sm.zi + padx(x0 + t + 4 * y));
           zv[4 * y] = v.x;
           zv[4 * y + 1] = v.y;
           zv[4 * y + 2] = v.z;
@@ -637,7 +644,7 @@ __global__ __launch_bounds__(64 * HW) void fit_head_kernel(int T, int steps, Ada
 #pragma unroll
       for (int c = 0; c < 8; ++c) s[c] = row16_sum(s[c]);
       const int x = x0 + kl16;   // lane c: output x0 + c
-      if (kl16 < 8 && x < T) adam(is_col ? x : T + x, pick(s, kl16) * own[x], bc1, bc2);
+      if (kl16 < 8 && x < T) adam(is_col ? x : T + x, pick(s, kl16) * own[padx(own_b + x)], bc1, bc2);
     }
   };
 
@@ -669,8 +676,8 @@ __global__ __launch_bounds__(64 * HW) void fit_head_kernel(int T, int steps, Ada
     for (int x = tid; x < T; x += 64 * HW) {
       const float a = sm.par[x] * kLog2e, r = sm.par[T + x] * kLog2e;
       if (fac) {
-        sm.fa[x] = __builtin_amdgcn_exp2f(a - am2);
-        sm.fr[RPAD + x] = __builtin_amdgcn_exp2f(r - rm2);
+        sm.fa[padx(x)] = __builtin_amdgcn_exp2f(a - am2);
+        sm.fr[padx(RPAD + x)] = __builtin_amdgcn_exp2f(r - rm2);
       } else {
         sm.a2[x] = a;
         sm.r2[RPAD + x] = r;

@@ -82,7 +82,7 @@ hipError_t launch_sharp_mean(const VarArgs& a, const void* q, const void* k, flo
 // keeps a whole head in one workgroup's LDS (T <= kFitHeadMaxT) and is chosen automatically
 // for kFitHeadMinHeads heads or more, or for lines of at most kFitHeadShortT. Measured at
 // T = 1024 (400 steps): the per-step launches take about 2.7 ms + 0.44 ms per head, the
-// per-head kernel 9.7 ms for up to 256 heads (one workgroup per CU), both scaling with T^2
+// per-head kernel 8.1 ms for up to 256 heads (one workgroup per CU), both scaling with T^2
 // above their launch costs.
 constexpr int kFitAuto = 0, kFitPerStep = 1, kFitPerHead = 2;
 constexpr int kFitHeadMaxT = 2048;
