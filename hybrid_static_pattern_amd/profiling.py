@@ -1,12 +1,12 @@
 """Turns rocprofv3 output into the summaries kept under profiles/.
 
     python -m hybrid_static_pattern_amd.profiling traffic \
-        --fetch gpurun_out/pmc_C/run_counter_collection.csv \
-        --write gpurun_out/pmc_D/run_counter_collection.csv \
+        --fetch <out>/pmc_fetch/run_counter_collection.csv \
+        --write <out>/pmc_write/run_counter_collection.csv \
         --copy-mib 256 --command "<the rocprofv3 command lines>" --out profiles/
 
     python -m hybrid_static_pattern_amd.profiling trace \
-        --stats gpurun_out/trace/run_kernel_stats.csv --title "..." --command "..." \
+        --stats <out>/trace/run_kernel_stats.csv --title "..." --command "..." \
         --out profiles/kernels_<workload>.md
 
 The trace summary is the kernel statistics table of `rocprofv3 --kernel-trace --stats`
