@@ -42,11 +42,6 @@ struct KTile {
   bf16 k[BN * D];   // key rows, swizzled (swz<D/8>)
 };
 
-template <int D>
-__device__ __forceinline__ void load_k(const bf16* K, int j0, int T, KTile<D>& tile) {
-  tile_load<D / 8, BN>(tile.k, [&](int row, int c) { return K + (size_t)min(j0 + row, T - 1) * D + c * 8; });
-}
-
 // One sequence's operands of a (128-query, 64-key) tile for the kernels that loop over the
 // sequences: its key rows, its query rows and (Welford) the rows' normalisers, all loaded
 // straight into LDS ahead of their use. Loading the query fragments into registers instead
@@ -67,15 +62,6 @@ struct SeqTile {
 constexpr int SEQ_STAGES = 2;
 template <int D> constexpr int SEQ_LOADS = (BN + BM) * (D / 8) / NTH + 1;
 
-template <int D>
-__device__ __forceinline__ void load_seq(const bf16* Q, const bf16* K, const float* l2, int i0, int j0, int T,
-                                         bool with_l2, SeqTile<D>& tile) {
-  load_k<D>(K, j0, T, *reinterpret_cast<KTile<D>*>(tile.k));
-  tile_load<D / 8, BM>(tile.q, [&](int row, int c) { return Q + (size_t)min(i0 + row, T - 1) * D + c * 8; });
-  const int w = wave_id();
-  if (with_l2) g2lds4(l2 + min(i0 + 64 * (w & 1) + lane_id(), T - 1), lds_addr(&tile.l2[64 * w]));
-}
-
 // Tile index of workgroup b of G: XCD x (the one b % 8 runs on) takes a contiguous range of
 // tiles, so the tiles of one head, which share query and key rows, share one L2 (measured:
 // 0.28 -> 0.23 ms for the Welford pass at N = 64, H = 12, T = 1024; the tiles in grid order,
@@ -83,6 +69,51 @@ __device__ __forceinline__ void load_seq(const bf16* Q, const bf16* K, const flo
 __device__ __forceinline__ int xcd_tile(int b, int G) {
   const int per = G / kNumXcd, rem = G % kNumXcd, x = b % kNumXcd;
   return x * per + min(x, rem) + b / kNumXcd;
+}
+
+// Per-lane byte offsets of a tile's loads within one sequence's [T, D] rows (and of its row
+// normalisers within the [T] row): they depend on the tile and T only, so the loop over the
+// sequences adds a wave-uniform base and spends no vector instructions on addresses.
+template <int D>
+struct SeqOffsets {
+  static constexpr int CPR = D / 8;
+  static constexpr int NK = BN * CPR / NTH, NQ = BM * CPR / NTH;   // loads per wave
+  uint32_t k[NK], q[NQ], l2;
+};
+
+template <int CPR, int NR, int PERW>
+__device__ __forceinline__ void tile_offsets(int r0, int T, uint32_t (&off)[PERW]) {
+  static_assert(NR * CPR == PERW * NTH, "tile must split evenly over the waves");
+  const int w = wave_id(), lane = lane_id();
+#pragma unroll
+  for (int x = 0; x < PERW; ++x) {
+    const int pch = (w * PERW + x) * 64 + lane, row = pch / CPR;
+    const int c = (pch % CPR) ^ swz<CPR>(row);
+    off[x] = 2u * (uint32_t)(min(r0 + row, T - 1) * (CPR * 8) + c * 8);
+  }
+}
+
+template <int D>
+__device__ __forceinline__ SeqOffsets<D> seq_offsets(int i0, int j0, int T) {
+  SeqOffsets<D> o;
+  tile_offsets<D / 8, BN>(j0, T, o.k);
+  tile_offsets<D / 8, BM>(i0, T, o.q);
+  o.l2 = 4u * (uint32_t)min(i0 + 64 * (wave_id() & 1) + lane_id(), T - 1);
+  return o;
+}
+
+// load_seq with precomputed offsets: Q, K point at the sequence's [T, D] rows, l2 at its
+// normalisers (all wave-uniform)
+template <int D>
+__device__ __forceinline__ void load_seq_off(const bf16* Q, const bf16* K, const float* l2, const SeqOffsets<D>& o,
+                                             bool with_l2, SeqTile<D>& tile) {
+  const int w = wave_id();
+  const uint32_t kb = lds_addr(tile.k), qb = lds_addr(tile.q);
+#pragma unroll
+  for (int x = 0; x < SeqOffsets<D>::NK; ++x) g2lds16_s(K, o.k[x], kb + (uint32_t)(w * SeqOffsets<D>::NK + x) * 1024u);
+#pragma unroll
+  for (int x = 0; x < SeqOffsets<D>::NQ; ++x) g2lds16_s(Q, o.q[x], qb + (uint32_t)(w * SeqOffsets<D>::NQ + x) * 1024u);
+  if (with_l2) g2lds4_s(l2, o.l2, lds_addr(&tile.l2[64 * w]));
 }
 
 // this lane's query fragments (row 32 w + m of the tile, k-halves hh) from LDS
@@ -135,11 +166,11 @@ __global__ __launch_bounds__(NTH, 2) void var_lse_kernel(const VarParams p) {
   const bf16* K = p.k + head * D;
   float mx_run = kNegInf, l = 0.f;
   const int n_kt = min(2 * qt + 2, (T + BN - 1) / BN);
-  load_k<D>(K, 0, T, stg[0]);
+  tile_load_rows<D / 8, BN, NTH / 64>(stg[0].k, K, 0, T);
   wait_vm0();
   __syncthreads();
   for (int J = 0; J < n_kt; ++J) {
-    if (J + 1 < n_kt) load_k<D>(K, (J + 1) * BN, T, stg[(J + 1) & 1]);
+    if (J + 1 < n_kt) tile_load_rows<D / 8, BN, NTH / 64>(stg[(J + 1) & 1].k, K, (J + 1) * BN, T);
     const int j0 = J * BN;
     if (j0 <= i0w) {
       f32x16 s[2];
@@ -220,9 +251,10 @@ __global__ __launch_bounds__(NTH, 2) void var_welford_kernel(const VarParams p) 
   const size_t nh_stride = (size_t)p.H * T;
   uint32_t koff[D / 16];
   key_offsets<D>(m, hh, koff);
+  const SeqOffsets<D> goff = seq_offsets<D>(i0, j0, T);
   auto load = [&](int n, int u) {  // sequences past N re-read the last one (never used)
     const size_t head = (size_t)min(n, p.N - 1) * nh_stride + (size_t)h * T;
-    load_seq<D>(p.q + head * D, p.k + head * D, p.lse2 + head, i0, j0, T, true, stg[u]);
+    load_seq_off<D>(p.q + head * D, p.k + head * D, p.lse2 + head, goff, true, stg[u]);
   };
   run_pipeline<NS, NS - 1, SEQ_LOADS<D>, 0>(p.N, load, [&](int n, int u, bool) {
     if (active) {
@@ -232,7 +264,9 @@ __global__ __launch_bounds__(NTH, 2) void var_welford_kernel(const VarParams p) 
       const float l2 = (i < T) ? cur.l2[32 * w + m] : __builtin_huge_valf();
       f32x16 s[2];
       scores<D>(cur.k, qf, koff, s);
-      const float rn = 1.f / (float)(n + 1);
+      // 1 / (n + 1) by the hardware reciprocal (within 1 ulp; exact for n = 0, so N equal
+      // sequences still leave M2 = 0 exactly)
+      const float rn = __builtin_amdgcn_rcpf((float)(n + 1));
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
@@ -332,9 +366,10 @@ __global__ __launch_bounds__(NTH, 2) void sharp_logits_kernel(const VarParams p,
   const size_t nh_stride = (size_t)p.H * T;
   uint32_t koff[D / 16];
   key_offsets<D>(m, hh, koff);
+  const SeqOffsets<D> goff = seq_offsets<D>(i0, j0, T);
   auto load = [&](int n, int u) {  // sequences past N re-read the last one (never used)
     const size_t head = (size_t)min(n, p.N - 1) * nh_stride + (size_t)h * T;
-    load_seq<D>(p.q + head * D, p.k + head * D, nullptr, i0, j0, T, false, stg[u]);
+    load_seq_off<D>(p.q + head * D, p.k + head * D, nullptr, goff, false, stg[u]);
   };
   f32x16 acc[2] = {f32x16{}, f32x16{}};
   run_pipeline<NS, NS - 1, SEQ_LOADS<D> - 1, 0>(p.N, load, [&](int n, int u, bool) {

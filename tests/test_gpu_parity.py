@@ -298,6 +298,13 @@ def test_var_score_small(S):
     assert list(rank) == list(saf_oracle.rank_heads([ref[h] for h in range(4)]))
 
 
+def test_var_score_d64_ragged_several_tiles(S):
+    """Ragged T over several Welford tiles: zero tiles above the diagonal, diagonal tiles
+    that some waves skip, and keys past T in the last tile."""
+    C = inputs.make_calibration(3, 2, 333, 64, seed=24)
+    _check_var(S, C)
+
+
 def test_var_score_d128_ragged(S):
     C = inputs.make_calibration(3, 2, 67, 128, seed=22)
     _check_var(S, C)
