@@ -104,10 +104,6 @@ __device__ __forceinline__ void g2lds16_s(const void* sbase, uint32_t voff, uint
 __device__ __forceinline__ void g2lds4(const void* gsrc, uint32_t lds_base) {
   asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dword %1, off" ::"s"(lds_base), "v"(gsrc) : "m0");
 }
-// The same with a wave-uniform base in SGPRs and a 32-bit per-lane byte offset.
-__device__ __forceinline__ void g2lds4_s(const void* sbase, uint32_t voff, uint32_t lds_base) {
-  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dword %1, %2" ::"s"(lds_base), "v"(voff), "s"(sbase) : "m0");
-}
 #pragma clang diagnostic pop
 
 // Waits until at most N vector-memory loads of this wave are outstanding (they complete in

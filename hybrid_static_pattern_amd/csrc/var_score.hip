@@ -71,6 +71,15 @@ __device__ __forceinline__ int xcd_tile(int b, int G) {
   return x * per + min(x, rem) + b / kNumXcd;
 }
 
+// 4 bytes per lane from a wave-uniform base in SGPRs and a 32-bit per-lane byte offset:
+// lane l's dword lands at lds_base + 4 l (as g2lds16_s, for the row normalisers).
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+__device__ __forceinline__ void g2lds4_s(const void* sbase, uint32_t voff, uint32_t lds_base) {
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dword %1, %2" ::"s"(lds_base), "v"(voff), "s"(sbase) : "m0");
+}
+#pragma clang diagnostic pop
+
 // Per-lane byte offsets of a tile's loads within one sequence's [T, D] rows (and of its row
 // normalisers within the [T] row): they depend on the tile and T only, so the loop over the
 // sequences adds a wave-uniform base and spends no vector instructions on addresses.
