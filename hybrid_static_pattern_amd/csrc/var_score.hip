@@ -111,7 +111,7 @@ __device__ __forceinline__ SeqOffsets<D> seq_offsets(int i0, int j0, int T) {
   return o;
 }
 
-// load_seq with precomputed offsets: Q, K point at the sequence's [T, D] rows, l2 at its
+// One sequence's tile loads with precomputed offsets: Q, K point at its [T, D] rows, l2 at its
 // normalisers (all wave-uniform)
 template <int D>
 __device__ __forceinline__ void load_seq_off(const bf16* Q, const bf16* K, const float* l2, const SeqOffsets<D>& o,
