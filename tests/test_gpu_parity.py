@@ -91,6 +91,8 @@ BF16_CASES = [
     (3, 2, 150, 64, [1]),         # folded columns 192 (two 128-column forward items at T <= 512)
     (3, 2, 600, 64, [1]),         # folded columns 192 in a 256-column item (T > 512)
     (5, 2, 520, 128, [0]),        # folded columns 640: three 256-column items, the last partial
+    (3, 4, 300, 128, [2]),        # a quarter frozen, folded columns 384: three 128-column items
+    (8, 4, 600, 64, [1]),         # a quarter frozen, folded columns 512: four 128-column items
 ]
 
 
