@@ -10,17 +10,17 @@
 //
 // Kernels, in launch order:
 //   bwd_delta   delta for ordinary heads (one 8-lane group per row);
-//   dkdv        one launch of 8-wave workgroups on 16x16x32 MFMAs, two kinds of items:
-//       ordinary (b, h, 128-key tile): each wave keeps 16 keys (K, V fragments and the
-//           fp32 dK, dV tiles) in registers and walks the 64-query steps from the
-//           diagonal down; S and dP are computed with the key as the lane index so P
-//           and dS feed the dV and dK products straight from registers;
+//   dkdv        one launch of 4-wave workgroups on 16x16x32 MFMAs, two kinds of items:
+//       ordinary (b, h, 128-key tile): each wave keeps 32 keys (K fragments and the fp32
+//           dK, dV tiles) in registers and walks the 32-query steps from the diagonal
+//           down; S and dP are computed with the key as the lane index so P and dS feed
+//           the dV and dK products straight from registers;
 //       frozen (h, 128-key tile, column chunk): the batch is folded into up to 256
 //           columns of [dO_0 | dO_1 | ...]; P^T is regenerated per lane and split into a
 //           bf16 high and low part (two MFMAs) so the fp32 dV keeps ~16 bits of P;
 //   dq          ordinary (b, h, 128-query tile), keys from 0 to the diagonal, the query
 //           as the lane index (as in the forward): dQ = scale * sum_J dS K_J.
-// Q/dO (dK/dV kernel) and K/V (dQ kernel) tiles go from HBM straight into double-buffered
+// Q/dO (dK/dV kernel) and K/V (dQ kernel) tiles go from HBM straight into multi-stage
 // LDS, one barrier per step; the transposed operands (dO^T, Q^T, K^T) are read from the
 // same row-major tiles with ds_read_b64_tr_b16. The split into a key-stationary and a query-stationary kernel recomputes S and dP once
 // more instead of accumulating dQ with atomics; every output is written exactly once.
@@ -31,7 +31,7 @@ namespace saf {
 
 namespace {
 
-constexpr int BNK = 256;   // keys per dK/dV workgroup
+constexpr int BNK = 128;   // keys per dK/dV workgroup
 constexpr int BMQ = 32;    // queries per dK/dV step
 constexpr int NWD = 4;     // waves per dQ workgroup (two workgroups per CU)
 constexpr int BMD = 32 * NWD;   // queries per dQ workgroup
@@ -120,24 +120,28 @@ __global__ __launch_bounds__(256) void bwd_delta_kernel(const DeltaParams p) {
 // A[l % 16][8 (l / 16) + e]; B (32 x 16): lane l holds B[8 (l / 16) + e][l % 16]; C (16 x 16):
 // lane l, register r holds C[4 (l / 16) + r][l % 16]. Below n = l % 16 and g = l / 16.
 //
-// One workgroup of 8 waves per 256-key tile; wave w owns keys 32 w .. 32 w + 31 (two 16-key
+// One workgroup of 4 waves per 128-key tile; wave w owns keys 32 w .. 32 w + 31 (two 16-key
 // groups kg) and keeps their K fragments and fp32 dK and dV tiles in registers, while the
 // tile's V rows sit in LDS for the whole item. Every Q and dO byte a wave reads from LDS
 // feeds two MFMAs. Steps are 32-query blocks whose Q / dO rows (and per-wave tables) go from
-// HBM straight into one of NSK LDS stages, NSK - 1 steps ahead of their use.
+// HBM straight into one of NSK<D> LDS stages, NSK<D> - 1 steps ahead of their use. Small
+// workgroups let two (D = 128) or three (D = 64) of them share a CU, their barriers
+// independent (measured against one 8-wave workgroup per 256-key tile with four stages:
+// 124M shape dK/dV 0.485 -> 0.396 ms, B = 64 prefill shape 0.889 -> 0.841 ms, 1B shape 1%).
 //
 // S = Q K^T is computed in two 16-query halves h whose A rows are the block's Q rows
 // 8 (rho / 4) + 4 h + rho % 4 (rho = MFMA row): register r of half h in lane group g then
 // holds query 8 g + 4 h + r, and the 8 values of lane group g are exactly the 8 consecutive
 // queries 8 g .. 8 g + 7 that the P^T operand of the dV product needs (k index e = 4 h + r).
 
-constexpr int NWK = 8;                   // waves per dK/dV workgroup
+constexpr int NWK = 4;                   // waves per dK/dV workgroup
 constexpr int NTK = 64 * NWK;
 constexpr int KPW = BNK / NWK;           // keys per wave
 constexpr int NKG = KPW / 16;            // 16-key groups per wave
-constexpr int NSK = 4;                   // LDS stages
+// LDS stages: four for D = 64 (three workgroups per CU), two for D = 128 (two per CU)
+template <int D> constexpr int NSK = D == 64 ? 4 : 2;
 constexpr int DIAG_STEPS = BNK / BMQ;    // steps over the tile's own queries
-static_assert(KPW == 32 && DIAG_STEPS % NSK == 0, "tile layout");
+static_assert(KPW == 32 && DIAG_STEPS % NSK<64> == 0 && DIAG_STEPS % NSK<128> == 0, "tile layout");
 
 // Values read in place of rows past the data: +inf (a log-normaliser that zeroes its row's
 // weights) and -inf (a distance table entry of a key after its query).
@@ -207,21 +211,23 @@ struct DynStage {
 };
 template <int D>
 struct DynSmem {
-  DynStage<D> st[NSK];
+  DynStage<D> st[NSK<D>];
   bf16 vs[BNK * D];           // V rows of the key tile, swizzled (swzv)
 };
+template <int FC>
 struct FrzStage {
-  bf16 gs[BMQ * FCOLS];       // folded dO [q][column], swizzled (swz16); read transposed
+  bf16 gs[BMQ * FC];          // folded dO [q][column], swizzled (swz16); read transposed
   float tab[NWK][128];        // per wave: log Z (+inf past T), then rho over the wave's
                               // 63-distance window (-inf for negative distances)
 };
 
-template <int D>
+template <int D, int FC>
 constexpr int dkdv_smem_bytes() {
-  return sizeof(DynSmem<D>) > NSK * sizeof(FrzStage) ? (int)sizeof(DynSmem<D>) : (int)(NSK * sizeof(FrzStage));
+  return sizeof(DynSmem<D>) > NSK<D> * sizeof(FrzStage<FC>) ? (int)sizeof(DynSmem<D>)
+                                                            : (int)(NSK<D> * sizeof(FrzStage<FC>));
 }
 
-// Frozen item (h, 256-key tile, column chunk): dV_b[j] = sum_{i>=j} P(i,j) dO_b[i] for the
+// Frozen item (h, 128-key tile, column chunk): dV_b[j] = sum_{i>=j} P(i,j) dO_b[i] for the
 // batch folded into FC (64, 128 or 256) columns. Each wave keeps its 32 keys x FC columns of
 // fp32 dV; P^T is regenerated per lane from alpha, rho and log Z (entries for j > i come out
 // as 0 from the -inf distances of the window) and split into bf16 high and low parts.
@@ -229,12 +235,11 @@ template <int D, int FC>
 __device__ void dv_frz(const BwdParams& p, int h, int chunk, int kt, unsigned char* smem_raw) {
   constexpr int CPR = FC / 8;
   constexpr int NCB = FC / 16;
-  // 16-byte chunks per lane per step. At FC = 64 the 32 x 64 tile is 4 KiB, half a chunk per
-  // lane: every wave still loads one (the same number of loads on every wave keeps the
-  // pipeline's counter waits uniform), and waves 4-7 fill blocks 4-7 of the stage, past the
-  // tile, with the next 32 rows, which no one reads.
-  constexpr int PERW = BMQ * CPR >= NTK ? BMQ * CPR / NTK : 1;
-  FrzStage* stg = reinterpret_cast<FrzStage*>(smem_raw);
+  // 16-byte chunks per lane per step: the 32 x FC tile splits evenly over the workgroup's
+  // lanes (the same number of loads on every wave keeps the pipeline's counter waits uniform)
+  static_assert(BMQ * CPR % NTK == 0, "frozen dO tile must split evenly over the lanes");
+  constexpr int PERW = BMQ * CPR / NTK;
+  FrzStage<FC>* stg = reinterpret_cast<FrzStage<FC>*>(smem_raw);
   const int lane = lane_id(), w = wave_id();
   const int n = lane & 15, g = lane >> 4;
   const int T = p.T, H = p.H, B = p.B;
@@ -270,7 +275,7 @@ __device__ void dv_frz(const BwdParams& p, int h, int chunk, int kt, unsigned ch
     srow[x] = row;
   }
   auto load = [&](int st, int u) {
-    FrzStage& sm = stg[u];
+    FrzStage<FC>& sm = stg[u];
     const int i0 = kbase + st * BMQ;
 #pragma unroll
     for (int x = 0; x < PERW; ++x)
@@ -293,7 +298,7 @@ __device__ void dv_frz(const BwdParams& p, int h, int chunk, int kt, unsigned ch
   };
 
   auto compute = [&](int st, int u, bool on_diag) {
-    const FrzStage& sm = stg[u];
+    const FrzStage<FC>& sm = stg[u];
     if (on_diag && st < w) return;   // the block ends before this wave's keys
     const float* tb = sm.tab[w];
     // queries i0 + 8 g + e; window index of distance i - j is (8 g + e) - (16 kg + n) + 31
@@ -323,7 +328,7 @@ __device__ void dv_frz(const BwdParams& p, int h, int chunk, int kt, unsigned ch
   };
 
   const int n_steps = (T - kbase + BMQ - 1) / BMQ;
-  run_pipeline<NSK, NSK - 1, PERW + 2, DIAG_STEPS>(n_steps, load, compute);
+  run_pipeline<NSK<D>, NSK<D> - 1, PERW + 2, DIAG_STEPS>(n_steps, load, compute);
 
 #pragma unroll
   for (int kg = 0; kg < NKG; ++kg)
@@ -340,14 +345,14 @@ __device__ void dv_frz(const BwdParams& p, int h, int chunk, int kt, unsigned ch
     }
 }
 
-// Ordinary item (b, h, 256-key tile): dV and dK for the wave's 32 keys over all queries
+// Ordinary item (b, h, 128-key tile): dV and dK for the wave's 32 keys over all queries
 // from the tile's first one to T, one 32-query block per step.
 template <int D>
 __device__ void dkdv_dyn(const BwdParams& p, int b, int h, int kt, unsigned char* smem_raw) {
   constexpr int CPR = D / 8;
   constexpr int NKS = D / 32;   // 32-wide k-steps over d
   constexpr int NDB = D / 16;   // 16-wide d blocks of dK, dV
-  // waves 0..3 load the step's Q rows, waves 4..7 its dO rows
+  // waves 0..1 load the step's Q rows, waves 2..3 its dO rows
   constexpr int PERW = BMQ * CPR / (NTK / 2);
   constexpr int PERV = BNK * CPR / NTK;   // V tile chunks per lane
   static_assert(PERW >= 1 && PERV >= 1, "tile split");
@@ -495,7 +500,7 @@ __device__ void dkdv_dyn(const BwdParams& p, int b, int h, int kt, unsigned char
   };
 
   const int n_steps = (T - kbase + BMQ - 1) / BMQ;
-  run_pipeline<NSK, NSK - 1, PERW + 1, DIAG_STEPS>(n_steps, load, compute);
+  run_pipeline<NSK<D>, NSK<D> - 1, PERW + 1, DIAG_STEPS>(n_steps, load, compute);
 
 #pragma unroll
   for (int kg = 0; kg < NKG; ++kg)
@@ -516,7 +521,7 @@ __device__ void dkdv_dyn(const BwdParams& p, int b, int h, int kt, unsigned char
 // (b, h) items, then the frozen (h, column chunk) items.
 template <int D, int FC>
 __global__ __launch_bounds__(NTK, 2) void dkdv_kernel(const BwdParams p) {
-  __shared__ __attribute__((aligned(16))) unsigned char smem[dkdv_smem_bytes<D>()];
+  __shared__ __attribute__((aligned(16))) unsigned char smem[dkdv_smem_bytes<D, FC>()];
   const int nd = p.B * p.n_dyn;
   int kt, rem;   // heaviest key tile (kt = 0) first
   if (!xcd_item(blockIdx.x, nd, p.n_frz * p.n_chunks, kt, rem)) return;
