@@ -70,15 +70,18 @@ struct DynStage {
   bf16 v[BN * D];   // value tile, row-major, swizzled; read transposed
 };
 
+template <int FC>
 struct FrzStage {
-  bf16 v[BN * FCOLS];     // folded value tile [key][column], swizzled; read transposed
+  bf16 v[BN * FC];        // folded value tile [key][column], swizzled; read transposed
   float tab[NW][FTAB];    // per wave: alpha of the tile's 64 keys, then rho over the wave's
                           // 95-distance window (-inf past the data)
 };
 
-template <int D>
+// the frozen stage is sized by the launch's column count, so that narrow launches (D = 64 with
+// at most 128 columns: 38 KiB instead of 70) fit three workgroups per CU
+template <int D, int FC>
 constexpr int smem_bytes() {
-  return NS * (sizeof(DynStage<D>) > sizeof(FrzStage) ? (int)sizeof(DynStage<D>) : (int)sizeof(FrzStage));
+  return NS * (sizeof(DynStage<D>) > sizeof(FrzStage<FC>) ? (int)sizeof(DynStage<D>) : (int)sizeof(FrzStage<FC>));
 }
 
 // Online-softmax bookkeeping of one lane (one query row). `mx` is this lane's max over its
@@ -225,7 +228,7 @@ __device__ void dyn_item(const FwdParams& p, int b, int h, int qt, unsigned char
 template <int D, int FC>
 __device__ void frz_item(const FwdParams& p, int h, int chunk, int qt, unsigned char* smem_raw) {
   constexpr int CPR = FC / 8;
-  FrzStage* st = reinterpret_cast<FrzStage*>(smem_raw);
+  FrzStage<FC>* st = reinterpret_cast<FrzStage<FC>*>(smem_raw);
   const int lane = lane_id(), w = wave_id();
   const int m = lane & 31, hh = lane >> 5;
   const int T = p.T, H = p.H, B = p.B;
@@ -257,7 +260,7 @@ __device__ void frz_item(const FwdParams& p, int h, int chunk, int qt, unsigned 
     srow[x] = row;
   }
   auto load = [&](int J, int u) {
-    FrzStage& sm = st[u];
+    FrzStage<FC>& sm = st[u];
     const int j0 = J * BN;
 #pragma unroll
     for (int x = 0; x < PERW; ++x)
@@ -286,7 +289,7 @@ __device__ void frz_item(const FwdParams& p, int h, int chunk, int qt, unsigned 
   }
 
   auto tile = [&](int J, int u, bool) {
-    const FrzStage& sm = st[u];
+    const FrzStage<FC>& sm = st[u];
     const int j0 = J * BN;
     if (j0 <= i0w) {
       // logits alpha(j) + rho(i - j); the window index of (i, j0 + kofs + e) is
@@ -352,7 +355,7 @@ __device__ void frz_item(const FwdParams& p, int h, int chunk, int qt, unsigned 
 
 template <int D, int FC>
 __global__ __launch_bounds__(NTH, 2) void hybrid_fwd_kernel(const FwdParams p) {
-  __shared__ __attribute__((aligned(16))) unsigned char smem[smem_bytes<D>()];
+  __shared__ __attribute__((aligned(16))) unsigned char smem[smem_bytes<D, FC>()];
   const int nd = p.B * p.n_dyn;
   int row, rem;
   if (!xcd_item(blockIdx.x, nd, p.n_frz * p.n_chunks, row, rem)) return;
