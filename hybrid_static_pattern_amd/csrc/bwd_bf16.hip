@@ -9,7 +9,10 @@
 //       P rebuilt from alpha, rho and log Z exactly as in the forward (Eq. (3)).
 //
 // Kernels, in launch order:
-//   bwd_delta   delta for ordinary heads (one 8-lane group per row);
+//   dq          ordinary (b, h, 128-query tile), keys from 0 to the diagonal, the query
+//           as the lane index (as in the forward): dQ = scale * sum_J dS K_J. It runs
+//           first because it also forms delta for its rows and writes it, with
+//           lse * log2(e), for the dK/dV items;
 //   dkdv        one launch of 4-wave workgroups on 16x16x32 MFMAs, two kinds of items:
 //       ordinary (b, h, 128-key tile): each wave keeps 32 keys (K fragments and the fp32
 //           dK, dV tiles) in registers and walks the 32-query steps from the diagonal
@@ -17,9 +20,8 @@
 //           the dV and dK products straight from registers;
 //       frozen (h, 128-key tile, column chunk): the batch is folded into up to 256
 //           columns of [dO_0 | dO_1 | ...]; P^T is regenerated per lane and split into a
-//           bf16 high and low part (two MFMAs) so the fp32 dV keeps ~16 bits of P;
-//   dq          ordinary (b, h, 128-query tile), keys from 0 to the diagonal, the query
-//           as the lane index (as in the forward): dQ = scale * sum_J dS K_J.
+//           bf16 high and low part (two MFMAs) so the fp32 dV keeps ~16 bits of P.
+// bwd_delta forms delta on its own for the float32 path.
 // Q/dO (dK/dV kernel) and K/V (dQ kernel) tiles go from HBM straight into multi-stage
 // LDS, one barrier per step; the transposed operands (dO^T, Q^T, K^T) are read from the
 // same row-major tiles with ds_read_b64_tr_b16. The split into a key-stationary and a query-stationary kernel recomputes S and dP once
@@ -40,13 +42,14 @@ constexpr int NSD = 2;     // dQ LDS stages
 constexpr int FCOLS = 256;   // batch-folded columns per frozen item (at most)
 
 struct BwdParams {
+  const bf16* o;        // forward output (the dQ kernel forms delta from it)
   const bf16* q;
   const bf16* k;
   const bf16* v;
   const bf16* dO;
   const float* lse;
-  const float* delta;
-  const float* ls2;     // lse * log2(e) of ordinary heads
+  float* delta;         // delta_i of ordinary heads (written by the dQ kernel)
+  float* ls2;           // lse * log2(e) of ordinary heads (written by the dQ kernel)
   const float* alpha;
   const float* rho;
   float* dq;
@@ -568,7 +571,24 @@ __global__ __launch_bounds__(64 * NWD, 2) void dq_kernel(const BwdParams p) {
     gf[kk] = *reinterpret_cast<const bf16x8*>(p.dO + off);
   }
   const float lse2 = (i < T) ? p.lse[head + i] * kLog2e : __builtin_huge_valf();
-  const float dlt = (i < T) ? p.delta[head + i] : 0.f;
+  // delta_i = sum_c dO_ic O_ic from this lane's half of the row (the dO fragments above) and
+  // the other half-wave's; written with lse * log2(e) for the dK/dV kernel, which runs next
+  float dlt = 0.f;
+  {
+    const bf16* orow = p.o + (head + min(i, T - 1)) * D;
+#pragma unroll
+    for (int kk = 0; kk < D / 16; ++kk) {
+      const bf16x8 of = *reinterpret_cast<const bf16x8*>(orow + kk * 16 + hh * 8);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) dlt = __builtin_fmaf((float)of[e], (float)gf[kk][e], dlt);
+    }
+    dlt = xhalf_sum(dlt);
+    if (i >= T) dlt = 0.f;
+    if (i < T && hh == 0) {
+      p.delta[head + i] = dlt;
+      p.ls2[head + i] = lse2;
+    }
+  }
   f32x16 acc[NDB];
 #pragma unroll
   for (int db = 0; db < NDB; ++db) acc[db] = f32x16{};
@@ -648,9 +668,10 @@ __global__ __launch_bounds__(64 * NWD, 2) void dq_kernel(const BwdParams p) {
 }
 
 BwdParams make_params(const AttnArgs& a, const void* q, const void* k, const void* v,
-                      const void* dO, const float* lse, const float* delta, const float* alpha,
+                      const void* dO, const float* lse, float* delta, const float* alpha,
                       const float* rho, float* dq, float* dk, float* dv) {
   BwdParams p;
+  p.o = nullptr;
   p.q = static_cast<const bf16*>(q);
   p.k = static_cast<const bf16*>(k);
   p.v = static_cast<const bf16*>(v);
@@ -708,10 +729,23 @@ hipError_t launch_bwd_bf16(const AttnArgs& a, const void* q, const void* k, cons
                            const float* alpha, const float* rho, float* dq, float* dk,
                            float* dv, float* delta, hipStream_t s) {
   float* ls2 = delta + attn_ws_floats(a);
-  hipError_t e = launch_delta(a, o, dO, delta, lse, ls2, s);
-  if (e != hipSuccess) return e;
   BwdParams p = make_params(a, q, k, v, dO, lse, delta, alpha, rho, dq, dk, dv);
+  p.o = static_cast<const bf16*>(o);
   p.ls2 = ls2;
+  hipError_t e = hipSuccess;
+  // dQ first: its items also write delta and lse * log2(e) of the ordinary rows, which the
+  // dK/dV items read
+  if (p.n_dyn > 0) {
+    p.n_tiles = (a.T + BMD - 1) / BMD;
+    const int n_dq = p.n_tiles * xcd_row_slots(a.B * p.n_dyn, 0);
+    prof_begin("dq", s);
+    if (a.D == 64)
+      hipLaunchKernelGGL(dq_kernel<64>, dim3(n_dq), dim3(64 * NWD), 0, s, p);
+    else
+      hipLaunchKernelGGL(dq_kernel<128>, dim3(n_dq), dim3(64 * NWD), 0, s, p);
+    prof_end(s);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+  }
   p.n_tiles = (a.T + BNK - 1) / BNK;
   // folded columns per frozen item: B * D rounded up to 64, 128 or 256, except that with at
   // most a quarter of the heads frozen and B * D <= 512 the items take 128 columns: more,
@@ -738,16 +772,7 @@ hipError_t launch_bwd_bf16(const AttnArgs& a, const void* q, const void* k, cons
     prof_end(s);
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
-  if (p.n_dyn == 0) return hipSuccess;
-  p.n_tiles = (a.T + BMD - 1) / BMD;
-  const int n_dq = p.n_tiles * xcd_row_slots(a.B * p.n_dyn, 0);
-  prof_begin("dq", s);
-  if (a.D == 64)
-    hipLaunchKernelGGL(dq_kernel<64>, dim3(n_dq), dim3(64 * NWD), 0, s, p);
-  else
-    hipLaunchKernelGGL(dq_kernel<128>, dim3(n_dq), dim3(64 * NWD), 0, s, p);
-  prof_end(s);
-  return hipGetLastError();
+  return hipSuccess;
 }
 
 }  // namespace saf
