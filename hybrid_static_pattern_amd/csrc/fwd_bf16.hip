@@ -155,6 +155,10 @@ __device__ void dyn_item(const FwdParams& p, int b, int h, int qt, unsigned char
 
   // one key tile; `diag` (the tile holding this wave's diagonal) masks keys after the query
   auto body = [&](const DynStage<D>& sm, int j0, bool diag) {
+    // the compiler's MFMA / LDS-read interleaving strategy 0 for this region (alternating
+    // runs on one box, 1B shape: forward 0.514 -> 0.507 ms; 124M and prefill shapes
+    // unchanged; in the dQ kernel it was slower and is not used)
+    __builtin_amdgcn_iglp_opt(0);
     {
       // S^T for keys j0 .. j0+63: two independent 32-key chains, interleaved
       f32x16 s[2] = {f32x16{}, f32x16{}};
