@@ -24,9 +24,9 @@
 //       [V_0 | V_1 | ...] and the exp work is shared by every batch entry.
 // Key tiles (and a frozen item's per-wave alpha / rho tables) go from HBM straight into one of
 // NS LDS stages, NS - 1 tiles ahead of their use (no staging registers), one barrier per
-// tile; V is stored row-major and read transposed (ds_read_b64_tr_b16). Two workgroups share
-// a CU: their waves are not tied by a common barrier, so one runs its softmax arithmetic
-// while the other keeps the matrix cores busy. Items are issued heaviest q-tile first; key
+// tile; V is stored row-major and read transposed (ds_read_b64_tr_b16). Two workgroups (three
+// at D = 64 with at most 128 folded columns) share a CU: their waves are not tied by a common
+// barrier, so one runs its softmax arithmetic while another keeps the matrix cores busy. Items are issued heaviest q-tile first; key
 // tiles above a wave's causal diagonal are skipped by that wave.
 #include "saf_device.h"
 #include "saf_internal.h"
