@@ -396,14 +396,17 @@ hipError_t launch_fwd_bf16(const AttnArgs& a, const void* q, const void* k, cons
   p.n_frz = a.heads.n_frz;
   p.n_qt = (a.T + BM - 1) / BM;
   // folded columns per frozen item: B * D rounded up to 64, 128 or 256, except
-  //  * at most a quarter of the heads frozen and B * D <= 512: 128 columns (more, narrower
-  //    items between the ordinary ones, the logits kept in registers: 124M shape at
-  //    r = 25% 0.272 -> 0.258 ms in alternating runs, 1B shape 0.510 -> 0.501 ms; with
-  //    more frozen heads the regenerated pattern tiles dominate and 256 columns stay faster);
+  //  * D = 64: at most 128, so that the launch's LDS (the frozen stage is sized by the
+  //    column count) fits three workgroups per CU, ordinary items included (alternating
+  //    runs: 124M shape at r = 50% forward 0.258 -> 0.226 ms, B = 64 prefill shape at
+  //    T = 2048 0.555 -> 0.526 ms);
+  //  * D = 128 with at most a quarter of the heads frozen and B * D <= 512: 128 columns
+  //    (more, narrower items between the ordinary ones, the logits kept in registers: 1B
+  //    shape 0.510 -> 0.501 ms; with more frozen heads the regenerated pattern tiles
+  //    dominate and 256 columns stay faster);
   //  * T <= 512: at most 128, where a few query tiles make a short grid whose critical path
-  //    the longer 256-column items set (B = 64, H = 12, D = 64, T = 512: 5% less time with 3
-  //    or 6 frozen heads; no difference from T = 1024 on).
-  const bool narrow = (a.B * a.D <= 512 && 4 * a.heads.n_frz <= a.H) || a.T <= 512;
+  //    the longer 256-column items set.
+  const bool narrow = a.D == 64 || (a.B * a.D <= 512 && 4 * a.heads.n_frz <= a.H) || a.T <= 512;
   const int fc = a.B * a.D <= 64 ? 64 : (a.B * a.D <= 128 || narrow ? 128 : FCOLS);
   p.n_chunks = (a.B * a.D + fc - 1) / fc;
   p.per_qt = a.B * p.n_dyn + p.n_frz * p.n_chunks;
