@@ -766,10 +766,9 @@ hipError_t launch_bwd_bf16(const AttnArgs& a, const void* q, const void* k, cons
   if (p.per_tile > 0) {
     prof_begin("dkdv", s);
     const dim3 grid(n_items), block(NTK);
-    if (a.D == 64) {
+    if (a.D == 64) {   // narrow: at most 128 columns
       if (fc == 64) hipLaunchKernelGGL((dkdv_kernel<64, 64>), grid, block, 0, s, p);
-      else if (fc == 128) hipLaunchKernelGGL((dkdv_kernel<64, 128>), grid, block, 0, s, p);
-      else hipLaunchKernelGGL((dkdv_kernel<64, FCOLS>), grid, block, 0, s, p);
+      else hipLaunchKernelGGL((dkdv_kernel<64, 128>), grid, block, 0, s, p);
     } else {
       if (fc == 128) hipLaunchKernelGGL((dkdv_kernel<128, 128>), grid, block, 0, s, p);
       else hipLaunchKernelGGL((dkdv_kernel<128, FCOLS>), grid, block, 0, s, p);

@@ -418,10 +418,9 @@ hipError_t launch_fwd_bf16(const AttnArgs& a, const void* q, const void* k, cons
   if (p.per_qt == 0) return hipSuccess;
   prof_begin("hybrid_fwd", s);
   const dim3 grid(n_items), block(NTH);
-  if (a.D == 64) {
+  if (a.D == 64) {   // narrow: at most 128 columns
     if (fc == 64) hipLaunchKernelGGL((hybrid_fwd_kernel<64, 64>), grid, block, 0, s, p);
-    else if (fc == 128) hipLaunchKernelGGL((hybrid_fwd_kernel<64, 128>), grid, block, 0, s, p);
-    else hipLaunchKernelGGL((hybrid_fwd_kernel<64, FCOLS>), grid, block, 0, s, p);
+    else hipLaunchKernelGGL((hybrid_fwd_kernel<64, 128>), grid, block, 0, s, p);
   } else {
     if (fc == 128) hipLaunchKernelGGL((hybrid_fwd_kernel<128, 128>), grid, block, 0, s, p);
     else hipLaunchKernelGGL((hybrid_fwd_kernel<128, FCOLS>), grid, block, 0, s, p);

@@ -4,9 +4,9 @@ sampled heads. The bars are the ones the hot path is held to:
                    (max|o| replaced by 1 for a tensor that is identically zero);
   bf16 storage:    max |g - o| <= 2e-2 and mean |g - o| <= 2e-3 on values (outputs and
                    float32 gradients), against the float64 oracle on the same inputs.
-A key/value head shared by several query heads gets the sum of their gradients; each
-summand is held to the bar above, so the sum of n of them is held to n times it (the
-triangle inequality), n being the number of query heads that contribute.
+A key/value head shared by several query heads gets the sum of their gradients: the GPU
+tests hold each summand to the bar above (the same layer with K, V repeated per query head)
+and the shared gradient to their float32 sum.
 """
 from __future__ import annotations
 
@@ -36,7 +36,7 @@ def down(t: torch.Tensor) -> np.ndarray:
     return t.detach().float().cpu().numpy().astype(np.float64)
 
 
-def check(gpu: np.ndarray, ref: np.ndarray, dtype: str, name: str, lse: bool = False, terms: int = 1):
+def check(gpu: np.ndarray, ref: np.ndarray, dtype: str, name: str, lse: bool = False):
     assert gpu.shape == ref.shape, (name, gpu.shape, ref.shape)
     assert np.all(np.isfinite(gpu)), f"{name}: non-finite values"
     err = np.abs(gpu - ref)
@@ -50,8 +50,8 @@ def check(gpu: np.ndarray, ref: np.ndarray, dtype: str, name: str, lse: bool = F
         rel = err.max() / (scale if scale > 0 else 1.0)
         assert rel <= FP32_REL, f"{name}: normwise rel err {rel:.3e}"
         return rel
-    assert err.max() <= BF16_MAX * terms, f"{name}: max abs err {err.max():.3e}"
-    assert err.mean() <= BF16_MEAN * terms, f"{name}: mean abs err {err.mean():.3e}"
+    assert err.max() <= BF16_MAX, f"{name}: max abs err {err.max():.3e}"
+    assert err.mean() <= BF16_MEAN, f"{name}: mean abs err {err.mean():.3e}"
     return err.max()
 
 

@@ -333,6 +333,48 @@ def pin_kl_score_closed_forms(orc):
     assert abs(s_kl - ref) < 1e-14 and s_kl > 0
 
 
+def pin_kl_score_through_qk(orc):
+    """The wrapper kl_score(q, k, scale) (part 二.1, the s^KL selector): at T = 5 with three
+    sequences and two heads, every attention row is formed in pure Python (math.exp over
+    scale * q_i . k_j for j <= i), averaged into A-hat, and the score summed as
+    (1/(N T)) sum_n sum_i sum_j A log(A / A-hat) with math.log. The scale is not 1 and q, k
+    differ, so a dropped scale or swapped operands change the result; the heads' temperatures
+    differ so the ranking is not the head order; the T = 1 case (one key per row) scores 0."""
+    r = _rng(33)
+    N, H, T, D, scale = 3, 3, 5, 4, 0.7
+    q = r.standard_normal((N, H, T, D)) * np.array([2.5, 0.3, 1.2])[None, :, None, None]
+    k = r.standard_normal((N, H, T, D))
+    A_hat, s_kl, rank = orc.kl_score(q, k, scale)
+    want = []
+    for h in range(H):
+        rows = []
+        for n in range(N):
+            A = [[0.0] * T for _ in range(T)]
+            for i in range(T):
+                logits = [scale * sum(q[n, h, i, c] * k[n, h, j, c] for c in range(D)) for j in range(i + 1)]
+                mx = max(logits)
+                w = [math.exp(x - mx) for x in logits]
+                for j in range(i + 1):
+                    A[i][j] = w[j] / sum(w)
+            rows.append(A)
+        mean = [[sum(rows[n][i][j] for n in range(N)) / N for j in range(T)] for i in range(T)]
+        tot = 0.0
+        for n in range(N):
+            for i in range(T):
+                for j in range(i + 1):
+                    tot += rows[n][i][j] * math.log(rows[n][i][j] / mean[i][j])
+        want.append(tot / (N * T))
+        for i in range(T):
+            for j in range(T):
+                assert abs(A_hat[h, i, j] - mean[i][j]) < 1e-14
+    for h in range(H):
+        assert abs(s_kl[h] - want[h]) <= 1e-13 * want[h] + 1e-16, (h, s_kl[h], want[h])
+    order = sorted(range(H), key=lambda h: (want[h], h))
+    assert list(rank) == order and order != list(range(H))
+    _, s1, _ = orc.kl_score(q[:, :, :1], k[:, :, :1], scale)
+    assert np.all(s1 == 0.0)
+
+
 def pin_sharp_mean(orc):
     """Sharp mean (part 二.2): one sequence gives that sequence's attention; the logits are
     averaged before the softmax (pure-Python evaluation at T = 4 with two sequences); it

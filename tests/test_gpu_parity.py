@@ -9,6 +9,7 @@ import torch
 
 from hybrid_static_pattern_amd import inputs
 from oracle import saf_oracle
+from tests import golden_calibration
 from tests.gpu_util import check, dev, down, layer_on_device, oracle_head, up
 
 pytestmark = pytest.mark.gpu
@@ -39,6 +40,8 @@ def run(S, L, bwd=True, sentinel=float("nan")):
 
 
 def compare_layer(L, out, bwd=True):
+    """Every output of a layer without shared key/value heads against the oracle."""
+    assert L["v"].shape[1] == L["H"], "shared key/value heads: use compare_shared"
     scale = 1.0 / math.sqrt(L["D"])
     dt = L["dtype"]
     O, lse = saf_oracle.attn_fwd(L["q"], L["k"], L["v"], L["frozen"], L["alpha"], L["rho"], scale)
@@ -48,18 +51,79 @@ def compare_layer(L, out, bwd=True):
         return
     dq, dk, dv = saf_oracle.attn_bwd(L["q"], L["k"], L["v"], L["do"], L["frozen"], L["alpha"], L["rho"], scale)
     dyn = L["frozen"] == 0
-    # a key/value head gets dK from the ordinary query heads of its group (with H_kv = H,
-    # the group is the head itself)
-    G = len(dyn) // L["v"].shape[1]
-    kv_dyn = dyn.reshape(-1, G).any(axis=1)
-    n_dyn = int(dyn.reshape(-1, G).sum(axis=1).max())   # most ordinary heads sharing one K
     if dyn.any():
         check(out["dq"][:, dyn], dq[:, dyn], dt, "dQ")
-        check(out["dk"][:, kv_dyn], dk[:, kv_dyn], dt, "dK", terms=n_dyn)
-    check(out["dv"], dv, dt, "dV", terms=G)
-    # dQ of frozen heads and dK of key/value heads without an ordinary query head are never
-    # written (NaN sentinels survive)
-    assert np.all(np.isnan(out["dq"][:, ~dyn])) and np.all(np.isnan(out["dk"][:, ~kv_dyn]))
+        check(out["dk"][:, dyn], dk[:, dyn], dt, "dK")
+    check(out["dv"], dv, dt, "dV")
+    # dQ and dK of frozen heads are never written (NaN sentinels survive)
+    assert np.all(np.isnan(out["dq"][:, ~dyn])) and np.all(np.isnan(out["dk"][:, ~dyn]))
+
+
+def repeat_kv(L):
+    """The same layer with every shared key/value head repeated once per query head that reads
+    it (H_kv = H): ordinary multi-head attention whose per-head dK, dV are the summands of the
+    shared heads' gradients."""
+    G = L["H"] // L["v"].shape[1]
+    R = dict(L)
+    R["k"] = np.repeat(L["k"], G, axis=1)
+    R["v"] = np.repeat(L["v"], G, axis=1)
+    R["H_kv"] = L["H"]
+    return R
+
+
+def sum_close(got, want, name):
+    """Float32 sums of the same per-head gradients in another order: normwise 1e-5."""
+    assert np.all(np.isfinite(got)), f"{name}: non-finite values"
+    scale = max(np.abs(want).max(), 1e-30)
+    rel = np.abs(got - want).max() / scale
+    assert rel <= 1e-5, f"{name}: normwise rel err {rel:.3e} against the sum of the per-head gradients"
+
+
+def compare_shared(S, L, out, groups=None, oracle_heads=None):
+    """A layer with shared key/value heads (G = H / H_kv query heads per key/value head).
+
+    O, lse and dQ are per query head and held to the bar against the oracle directly. The
+    gradient of a shared K or V is a sum over its group; each summand is held to the bar:
+    the same inputs run with K, V repeated per query head (repeat_kv) give the per-head
+    gradients, which must meet the bar against the oracle, and the shared gradient must equal
+    their float32 sum (dK over the group's ordinary heads, dV over all of them). `groups`
+    limits the checks to some key/value heads (full-size shapes, where the oracle runs on a
+    sample)."""
+    scale = 1.0 / math.sqrt(L["D"])
+    dt = L["dtype"]
+    H, H_kv = L["H"], L["v"].shape[1]
+    G = H // H_kv
+    fz = L["frozen"]
+    groups = range(H_kv) if groups is None else groups
+    R = repeat_kv(L)
+    rep = run(S, R)
+    for g in groups:
+        hs = slice(g * G, (g + 1) * G)
+        O, lse = saf_oracle.attn_fwd(L["q"][:, hs], L["k"][:, g:g + 1], L["v"][:, g:g + 1], fz[hs],
+                                     L["alpha"][hs], L["rho"][hs], scale)
+        check(out["o"][:, hs], O, dt, f"O group {g}")
+        check(out["lse"][:, hs], lse, dt, f"lse group {g}", lse=True)
+        dq, dk_h, dv_h = saf_oracle.attn_bwd(R["q"][:, hs], R["k"][:, hs], R["v"][:, hs], R["do"][:, hs],
+                                             fz[hs], R["alpha"][hs], R["rho"][hs], scale)
+        dyn = fz[hs] == 0
+        # the summands: per-query-head gradients of the repeated layer, each at the bar
+        check(rep["dv"][:, hs], dv_h, dt, f"dV summands of group {g}")
+        if dyn.any():
+            check(out["dq"][:, hs][:, dyn], dq[:, dyn], dt, f"dQ group {g}")
+            check(rep["dk"][:, hs][:, dyn], dk_h[:, dyn], dt, f"dK summands of group {g}")
+            sum_close(out["dk"][:, g], rep["dk"][:, hs][:, dyn].sum(axis=1), f"dK group {g}")
+        else:
+            # no ordinary head reads this K: its gradient is never written
+            assert np.all(np.isnan(out["dk"][:, g])), f"dK group {g} written"
+        sum_close(out["dv"][:, g], rep["dv"][:, hs].sum(axis=1), f"dV group {g}")
+        assert np.all(np.isnan(out["dq"][:, hs][:, ~dyn]))
+
+
+def compare(S, L, out):
+    if L["v"].shape[1] == L["H"]:
+        compare_layer(L, out)
+    else:
+        compare_shared(S, L, out)
 
 
 # ---------------------------------------------------------------- small layers
@@ -82,14 +146,14 @@ BF16_CASES = [
     (2, 4, 300, 64, [1, 3]),      # several tiles, ragged tail
     (1, 3, 257, 128, [0]),        # ragged; folded columns 128 < 256
     (3, 2, 130, 128, [1]),        # folded columns 384: three forward items of 128, two dV items of 256
-    (8, 2, 129, 64, [0]),         # folded columns 512: two full chunks
+    (8, 2, 129, 64, [0]),         # folded columns 512: four 128-column items (D = 64 takes at most 128)
     (1, 2, 1, 64, [1]),           # T = 1
     (2, 3, 64, 64, []),           # all ordinary (r = 0)
     (2, 2, 200, 128, [0, 1]),     # all frozen: q, k are NULL
     (1, 2, 513, 128, [1]),        # crosses the 512-key boundary of the dK/dV tiles
     (1, 2, 700, 64, [0]),         # folded columns 64 (the narrowest frozen item), ragged
     (3, 2, 150, 64, [1]),         # folded columns 192 (two 128-column forward items at T <= 512)
-    (3, 2, 600, 64, [1]),         # folded columns 192 in a 256-column item (T > 512)
+    (3, 2, 600, 64, [1]),         # folded columns 192 at T > 512: a full and a partial 128-column item
     (5, 2, 520, 128, [0]),        # folded columns 640: three 256-column items, the last partial
     (3, 4, 300, 128, [2]),        # a quarter frozen, folded columns 384: three 128-column items
     (8, 4, 600, 64, [1]),         # a quarter frozen, folded columns 512: four 128-column items
@@ -117,7 +181,7 @@ GQA_CASES = [
 @pytest.mark.parametrize("B,H,H_kv,T,D,frozen,dt", GQA_CASES)
 def test_gqa_forward_backward(S, B, H, H_kv, T, D, frozen, dt):
     L = inputs.make_layer(B, H, T, D, dtype=dt, seed=17, frozen_heads=frozen, kv_heads=H_kv)
-    compare_layer(L, run(S, L))
+    compare(S, L, run(S, L))
 
 
 def _random_cases(n, seed=123):
@@ -141,7 +205,7 @@ def _random_cases(n, seed=123):
 @pytest.mark.parametrize("B,H,H_kv,T,D,frozen,dt,seed", _random_cases(16))
 def test_random_layers(S, B, H, H_kv, T, D, frozen, dt, seed):
     L = inputs.make_layer(B, H, T, D, dtype=dt, seed=seed, frozen_heads=frozen, kv_heads=H_kv)
-    compare_layer(L, run(S, L))
+    compare(S, L, run(S, L))
 
 
 def test_max_head_count(S):
@@ -151,7 +215,7 @@ def test_max_head_count(S):
     L = inputs.make_layer(1, 256, 65, 64, dtype="bf16", seed=19, frozen_heads=fz)
     compare_layer(L, run(S, L))
     L = inputs.make_layer(1, 256, 40, 64, dtype="bf16", seed=20, frozen_heads=fz, kv_heads=32)
-    compare_layer(L, run(S, L))
+    compare_shared(S, L, run(S, L))
 
 
 def test_gqa_frozen_query_never_read(S):
@@ -468,26 +532,14 @@ def test_full_prefill_single_sequence(S):
 
 def test_full_gqa_4b_sampled(S):
     """The shared-key/value shape (B=1, H=32 over 8 key/value heads, T=4096, D=128, r=25%):
-    two whole groups (four query heads each) against the oracle."""
+    two whole groups (four query heads each) against the oracle, the shared dK, dV through
+    their per-head summands."""
     L = inputs.make_layer(**dict(inputs.WORKLOADS["gqa_4b"]))
     out = run(S, L)
-    scale = 1.0 / math.sqrt(L["D"])
     G = L["H"] // L["H_kv"]
     fz = L["frozen"]
     groups = sorted({int(np.flatnonzero(fz)[0]) // G, int(np.flatnonzero(fz == 0)[-1]) // G})
-    for g in groups:
-        hs = slice(g * G, (g + 1) * G)
-        O, lse = saf_oracle.attn_fwd(L["q"][:, hs], L["k"][:, g:g + 1], L["v"][:, g:g + 1], fz[hs],
-                                     L["alpha"][hs], L["rho"][hs], scale)
-        dq, dk, dv = saf_oracle.attn_bwd(L["q"][:, hs], L["k"][:, g:g + 1], L["v"][:, g:g + 1], L["do"][:, hs],
-                                         fz[hs], L["alpha"][hs], L["rho"][hs], scale)
-        check(out["o"][:, hs], O, "bf16", f"O group {g}")
-        check(out["lse"][:, hs], lse, "bf16", f"lse group {g}", lse=True)
-        check(out["dv"][:, g:g + 1], dv, "bf16", f"dV group {g}", terms=G)
-        dyn = fz[hs] == 0
-        if dyn.any():
-            check(out["dq"][:, hs][:, dyn], dq[:, dyn], "bf16", f"dQ group {g}")
-            check(out["dk"][:, g:g + 1], dk, "bf16", f"dK group {g}", terms=int(dyn.sum()))
+    compare_shared(S, L, out, groups=groups)
 
 
 def test_full_prefill_t2048_half_frozen(S):
@@ -495,16 +547,33 @@ def test_full_prefill_t2048_half_frozen(S):
 
 
 def test_full_calibration_sampled(S):
+    """The calibration workload: A-hat of three sampled heads entry by entry against the oracle,
+    and every head's s_var (1e-3 relative), the sum of its A-hat squared and the full ranking
+    against the oracle's stored values (tests/golden/calibration_N64_H12_T1024.txt)."""
     C = inputs.make_calibration(**inputs.CALIBRATION)
     tau = C["tau"]
     heads = [int(np.argmin(tau)), int(np.argmax(tau)), 5]
-    ref, s_var, rank = _check_var(S, C, heads=heads)
-    # sharper heads (small temperature) score higher: the sampled order must agree
-    order = sorted(heads, key=lambda h: ref[h])
-    assert [h for h in rank if h in heads] == order
+    _, s_var, rank = _check_var(S, C, heads=heads)
+    g = golden_calibration.load()
+    for h in range(C["H"]):
+        assert abs(s_var[h] - g["s_var"][h]) <= 1e-3 * g["s_var"][h], (h, s_var[h], g["s_var"][h])
+    assert list(rank) == g["rank_var"]
+    a_hat, _, _ = S.var_score(up(C["q"], "bf16"), up(C["k"], "bf16"))
+    torch.cuda.synchronize()
+    sq = (a_hat.cpu().numpy().astype(np.float64) ** 2).sum(axis=(1, 2))
+    # each entry within 1e-5 of the oracle's and the rows summing to 1 bound the change of the
+    # sum of squares by 2e-5 T (+ T^2 1e-10)
+    T = C["T"]
+    assert np.all(np.abs(sq - g["a_hat_sq"]) <= 2e-5 * T + 1e-10 * T * T), (sq, g["a_hat_sq"])
 
 
 def test_full_calibration_kl_sampled(S):
+    """s^KL on the calibration workload: A-hat of two sampled heads against the oracle, every
+    head's score and the full ranking against the oracle's stored values."""
     C = inputs.make_calibration(**inputs.CALIBRATION)
     tau = C["tau"]
-    _check_kl(S, C, heads=[int(np.argmin(tau)), int(np.argmax(tau))])
+    _, s_kl, rank = _check_kl(S, C, heads=[int(np.argmin(tau)), int(np.argmax(tau))])
+    g = golden_calibration.load()
+    for h in range(C["H"]):
+        assert abs(s_kl[h] - g["s_kl"][h]) <= 1e-3 * g["s_kl"][h] + 2e-5, (h, s_kl[h], g["s_kl"][h])
+    assert list(rank) == g["rank_kl"]

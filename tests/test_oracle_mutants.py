@@ -163,6 +163,24 @@ def _kl_by_t2(A_stack):
     return val / np.shape(A_stack)[1], A_hat
 
 
+def _kl_wrapper_factory(kind):
+    """Mistakes in the q, k -> s^KL wrapper itself (kl_score_of left intact)."""
+    def kl_score(q, k, scale):
+        N, H, T, _ = np.shape(q)
+        A_hat = np.empty((H, T, T))
+        s = np.empty(H)
+        for h in range(H):
+            if kind == "no_scale":
+                stack = [so.dynamic_probs(q[n, h], k[n, h], 1.0)[0] for n in range(N)]
+            elif kind == "swapped":
+                stack = [so.dynamic_probs(k[n, h], q[n, h], scale)[0] for n in range(N)]
+            else:   # "first_head": every head scored on head 0's inputs
+                stack = [so.dynamic_probs(q[n, 0], k[n, 0], scale)[0] for n in range(N)]
+            s[h], A_hat[h] = so.kl_score_of(np.stack(stack))
+        return A_hat, s, so.rank_heads(s)
+    return kl_score
+
+
 def _sharp_prob_mean(q, k, scale):
     return so.var_score(q, k, scale)[0]
 
@@ -192,6 +210,9 @@ MUTANTS = {
     "rank: descending": ("rank_heads", _rank_desc),
     "kl: reverse direction KL(A-hat || A)": ("kl_score_of", _kl_reverse),
     "kl: divides by N T^2": ("kl_score_of", _kl_by_t2),
+    "kl wrapper: 1/sqrt(d) scale dropped": ("kl_score", _kl_wrapper_factory("no_scale")),
+    "kl wrapper: q and k swapped": ("kl_score", _kl_wrapper_factory("swapped")),
+    "kl wrapper: every head scored on head 0": ("kl_score", _kl_wrapper_factory("first_head")),
     "sharp mean: probabilities averaged instead of logits": ("sharp_mean", _sharp_prob_mean),
 }
 
