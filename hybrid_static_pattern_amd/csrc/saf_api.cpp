@@ -19,14 +19,19 @@ namespace {
 
 thread_local std::string g_err;
 
+saf_status vfail(saf_status st, const char* fmt, va_list ap) {
+  char buf[512];
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  g_err = buf;
+  return st;
+}
+
 saf_status fail(saf_status st, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
 saf_status fail(saf_status st, const char* fmt, ...) {
-  char buf[512];
   va_list ap;
   va_start(ap, fmt);
-  vsnprintf(buf, sizeof(buf), fmt, ap);
+  vfail(st, fmt, ap);
   va_end(ap);
-  g_err = buf;
   return st;
 }
 
@@ -128,6 +133,14 @@ saf_status check_ptr(const void* p, bool required, const char* name) {
 }  // namespace
 
 namespace saf {
+
+saf_status set_error(saf_status st, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vfail(st, fmt, ap);
+  va_end(ap);
+  return st;
+}
 
 void prof_begin(const char* name, hipStream_t s) {
   if (!g_prof.on || g_prof.recs.size() >= ProfState::kCap) return;

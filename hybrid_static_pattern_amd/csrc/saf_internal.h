@@ -3,6 +3,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "saf.h"
+
 namespace saf {
 
 constexpr int kMaxHeads = 256;
@@ -23,6 +25,9 @@ struct AttnArgs {
   int tab_stride;
   HeadLists heads;
 };
+
+// Records a thread-local error message (printf format) for saf_last_error and returns st.
+saf_status set_error(saf_status st, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
 
 // Kernel timing hooks (saf_prof_*); no-ops unless enabled on this thread.
 void prof_begin(const char* name, hipStream_t s);

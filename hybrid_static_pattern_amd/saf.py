@@ -25,7 +25,11 @@ EXPORTS = (
     "saf_var_score", "saf_select_heads", "saf_status_string", "saf_last_error",
     "saf_prof_enable", "saf_prof_read", "saf_pattern_stats", "saf_compact_marginals",
     "saf_fit_workspace_size", "saf_compact_fit", "saf_select_fitted", "saf_kl_score", "saf_sharp_mean",
+    "saf_attn_bwd_noalloc",
 )
+
+# Bytes of the library's own device array behind saf_attn_bwd_noalloc (SAF_NOALLOC_SCRATCH_BYTES).
+NOALLOC_SCRATCH_BYTES = 32 << 20
 
 
 class SafError(RuntimeError):
@@ -81,6 +85,7 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.saf_attn_workspace_size.argtypes = [pd]
     lib.saf_attn_workspace_size.restype = sz
     lib.saf_attn_bwd.argtypes = [pd, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+    lib.saf_attn_bwd_noalloc.argtypes = [pd, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp]
     lib.saf_var_workspace_size.argtypes = [pv]
     lib.saf_var_workspace_size.restype = sz
     lib.saf_var_score.argtypes = [pv, vp, vp, vp, vp, vp, vp, sz, vp]
@@ -103,7 +108,7 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.saf_select_fitted.argtypes = [ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_float), i32,
                                       ctypes.c_double, ctypes.c_float, ctypes.POINTER(i32)]
     lib.saf_select_fitted.restype = i32
-    for fn in ("saf_attn_fwd", "saf_attn_bwd", "saf_var_score", "saf_kl_score", "saf_sharp_mean",
+    for fn in ("saf_attn_fwd", "saf_attn_bwd", "saf_attn_bwd_noalloc", "saf_var_score", "saf_kl_score", "saf_sharp_mean",
                "saf_prof_enable", "saf_pattern_stats",
                "saf_compact_marginals", "saf_compact_fit"):
         getattr(lib, fn).restype = ctypes.c_int
@@ -240,6 +245,26 @@ def attn_bwd(q, k, v, o, do, lse, frozen, alpha=None, rho=None, scale=None,
     _check(lib.saf_attn_bwd(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(do), _ptr(lse),
                             _ptr(alpha), _ptr(rho), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(workspace),
                             workspace.numel() * workspace.element_size(), _stream(v)))
+    return dq, dk, dv
+
+
+def attn_bwd_noalloc(q, k, v, o, do, lse, frozen, dq, dk, dv, alpha=None, rho=None, scale=None):
+    """Hybrid backward without a workspace (saf_attn_bwd_noalloc): the library's own device
+    array stands in for it, so nothing is allocated here either; the caller passes dq, dk, dv.
+    Results as attn_bwd. Calls that overlap in time on one GPU share that array and race."""
+    lib = load()
+    B, H, H_kv, T, D = _heads(v, frozen)
+    for name, t, hh in (("q", q, H), ("k", k, H_kv), ("v", v, H_kv), ("o", o, H), ("do", do, H)):
+        _need(t, name, shape=(B, hh, T, D), dtype=v.dtype, device=v.device)
+    _need(lse, "lse", shape=(B, H, T), dtype=torch.float32, device=v.device)
+    for name, t, hh in (("dq", dq, H), ("dk", dk, H_kv), ("dv", dv, H_kv)):
+        if t is None:
+            raise ValueError(f"{name} is required (this entry point allocates nothing)")
+        _need(t, name, shape=(B, hh, T, D), dtype=torch.float32, device=v.device)
+    _tables(alpha, rho, H, T, v.device)
+    desc, mask = _attn_desc(v, frozen, alpha, scale)
+    _check(lib.saf_attn_bwd_noalloc(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(do),
+                                    _ptr(lse), _ptr(alpha), _ptr(rho), _ptr(dq), _ptr(dk), _ptr(dv), _stream(v)))
     return dq, dk, dv
 
 

@@ -106,6 +106,24 @@ saf_status saf_attn_bwd(const saf_attn_desc* desc, const void* q, const void* k,
                         const float* alpha, const float* rho, void* dq, void* dk,
                         void* dv, void* workspace, size_t ws_bytes, void* stream);
 
+/* Bytes of the device array that saf_attn_bwd_noalloc takes its workspace from. */
+#define SAF_NOALLOC_SCRATCH_BYTES ((size_t)32 << 20)
+
+/* saf_attn_bwd without a workspace argument, for callers that cannot allocate device memory
+ * (code under HIP graph capture, tight serving loops, harnesses that forbid allocation): the
+ * workspace comes from a device array of SAF_NOALLOC_SCRATCH_BYTES that the library holds on
+ * every GPU it runs on until the process ends. Arguments, results, layouts and errors are
+ * those of saf_attn_bwd, whose kernels it runs; it calls no allocation routine. A layer whose
+ * saf_attn_workspace_size exceeds SAF_NOALLOC_SCRATCH_BYTES is rejected with SAF_EWORKSPACE
+ * before anything is enqueued (without shared key/value heads that is B * H * T above 4M).
+ * The first call on a device looks up the array's address there (SAF_EHIP if that fails).
+ * All calls on one GPU share the array: calls that overlap in time on one GPU (other streams,
+ * other threads) race and must be ordered by the caller. */
+saf_status saf_attn_bwd_noalloc(const saf_attn_desc* desc, const void* q, const void* k,
+                                const void* v, const void* o, const void* dO, const float* lse,
+                                const float* alpha, const float* rho, void* dq, void* dk, void* dv,
+                                void* stream);
+
 /* Calibration batch of one layer: N sequences (N >= 2), H heads, length T, width D. */
 typedef struct {
   int32_t N, H, T, D;

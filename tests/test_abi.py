@@ -85,6 +85,23 @@ def test_bwd_workspace_contract(lib):
     assert lib.saf_attn_workspace_size(None) == 0
 
 
+def test_noalloc_bounds(lib):
+    """saf_attn_bwd_noalloc: a layer whose workspace exceeds the library's array is rejected
+    with SAF_EWORKSPACE before anything is touched (B * H * T = 8M here); a bad descriptor
+    gets saf_attn_bwd's own error; the array's size is the header's."""
+    d, mask = _desc(B=64, H=2, T=65536, stride=65536)
+    assert lib.saf_attn_workspace_size(ctypes.byref(d)) > saf.NOALLOC_SCRATCH_BYTES
+    st = lib.saf_attn_bwd_noalloc(ctypes.byref(d), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, None,
+                                  FAKE, FAKE, FAKE, None)
+    assert st == saf.SAF_EWORKSPACE and b"scratch" in lib.saf_last_error()
+    d, mask = _desc(B=0)
+    assert lib.saf_attn_bwd_noalloc(ctypes.byref(d), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, None,
+                                    FAKE, FAKE, FAKE, None) == saf.SAF_EINVAL
+    with open(os.path.join(ROOT, "include", "saf.h")) as f:
+        m = re.search(r"#define SAF_NOALLOC_SCRATCH_BYTES \(\(size_t\)(\d+) << (\d+)\)", f.read())
+    assert m and int(m.group(1)) << int(m.group(2)) == saf.NOALLOC_SCRATCH_BYTES
+
+
 def test_gqa_workspace_contract(lib):
     """Shared key/value heads need two more [B, H, T, D] float32 arrays (per-query-head dK, dV)."""
     d1, m1 = _desc(B=2, H=8, T=100, kv=8)
