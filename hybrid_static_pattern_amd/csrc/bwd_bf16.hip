@@ -331,7 +331,10 @@ __device__ void dv_frz(const BwdParams& p, int h, int chunk, int kt, unsigned ch
   };
 
   const int n_steps = (T - kbase + BMQ - 1) / BMQ;
-  run_pipeline<NSK<D>, NSK<D> - 1, PERW + 2, DIAG_STEPS>(n_steps, load, compute);
+  run_pipeline<NSK<D>, NSK<D> - 1, PERW + 2, DIAG_STEPS>(n_steps, load, compute, [&] {
+#pragma unroll
+    for (int kg = 0; kg < NKG; ++kg) settle(a2[kg]);
+  });
 
 #pragma unroll
   for (int kg = 0; kg < NKG; ++kg)
@@ -506,7 +509,12 @@ __device__ void dkdv_dyn(const BwdParams& p, int b, int h, int kt, unsigned char
   };
 
   const int n_steps = (T - kbase + BMQ - 1) / BMQ;
-  run_pipeline<NSK<D>, NSK<D> - 1, PERW + 1, DIAG_STEPS>(n_steps, load, compute);
+  run_pipeline<NSK<D>, NSK<D> - 1, PERW + 1, DIAG_STEPS>(n_steps, load, compute, [&] {
+#pragma unroll
+    for (int kg = 0; kg < NKG; ++kg)
+#pragma unroll
+      for (int ks = 0; ks < NKS; ++ks) settle(kf[kg][ks]);
+  });
 
 #pragma unroll
   for (int kg = 0; kg < NKG; ++kg)
@@ -651,7 +659,13 @@ __global__ __launch_bounds__(64 * NWD, 2) void dq_kernel(const BwdParams p) {
   };
   constexpr int PERW = BND * CPR / (64 * NWD);   // loads per wave and tile, for each of K, V
   static_assert(BMD == 2 * BND && NSD == 2, "the diagonal lies in the first two tiles visited");
-  run_pipeline<NSD, NSD - 1, 2 * PERW, 2>(n_kt, load, tile);
+  run_pipeline<NSD, NSD - 1, 2 * PERW, 2>(n_kt, load, tile, [&] {
+#pragma unroll
+    for (int kk = 0; kk < D / 16; ++kk) {
+      settle(qf[kk]);
+      settle(gf[kk]);
+    }
+  });
 
   if (i < T) {
     float* out = p.dq + (head + i) * D;

@@ -206,7 +206,10 @@ __device__ void dyn_item(const FwdParams& p, int b, int h, int qt, unsigned char
   };
   constexpr int PERW = BN * CPR / (64 * NW);   // loads per wave and tile, for each of K, V
   static_assert(BM == 2 * BN && NS == 2, "the diagonal lies in the first two tiles visited");
-  run_pipeline<NS, NS - 1, 2 * PERW, 2>(n_kt, load, tile);
+  run_pipeline<NS, NS - 1, 2 * PERW, 2>(n_kt, load, tile, [&] {
+#pragma unroll
+    for (int kk = 0; kk < D / 16; ++kk) settle(qf[kk]);
+  });
 
   const float lt = xhalf_sum(l);
   if (i < T) {

@@ -199,6 +199,19 @@ __device__ __forceinline__ void pipelined(Read read, Mma mma) {
   }
 }
 
+// Marks a register value loaded from global memory before a pipelined loop as settled. The
+// compiler's count of outstanding vector-memory loads does not include the loads issued from
+// inline assembly (g2lds16 and friends), so at each step's first use of such a value it
+// would insert "s_waitcnt vmcnt(N)" for the value's own load, which in hardware waits for the
+// youngest N loads in flight: the next steps' tile loads. An empty asm that rewrites the
+// value moves that wait to where it stands (the compiler retires the load before the rewrite)
+// and leaves the loop free of it. Call it only after a hardware wait that has retired the
+// load (run_pipeline's prologue wait does, for loads issued before the pipeline starts).
+template <class T>
+__device__ __forceinline__ void settle(T& x) {
+  asm volatile("" : "+v"(x));
+}
+
 // Multi-stage LDS pipeline over the steps 0 .. n_steps - 1 of a work item. Step st
 // computes on stage st % NS; the loads of step st + PD (L vector-memory loads per wave and
 // step, direct to LDS) are issued at step st and waited for PD - 1 steps later, one barrier
@@ -207,13 +220,15 @@ __device__ __forceinline__ void pipelined(Read read, Mma mma) {
 // (callers clamp their rows or read sentinels), so every step issues the same L loads. The
 // first NPEEL steps (a multiple of NS) run with `peeled` set, in a loop of their own.
 // load(step, stage) and compute(step, stage, peeled) are called with compile-time stage
-// indices. Leaves no load outstanding.
-template <int NS, int PD, int L, int NPEEL, class Load, class Compute>
-__device__ __forceinline__ void run_pipeline(int n_steps, Load load, Compute compute) {
+// indices; settle() runs once after the prologue's wait (see settle above) for the values the
+// caller loaded into registers before the pipeline. Leaves no load outstanding.
+template <int NS, int PD, int L, int NPEEL, class Load, class Compute, class Settle>
+__device__ __forceinline__ void run_pipeline(int n_steps, Load load, Compute compute, Settle settle_regs) {
   static_assert(NS >= 2 && PD >= 1 && PD <= NS - 1 && NPEEL % NS == 0, "pipeline shape");
 #pragma unroll
   for (int s = 0; s < PD; ++s) load(s, s);
   wait_vm<L * (PD - 1)>();
+  settle_regs();
   __syncthreads();
   auto step = [&](int st, int u, bool peeled) {
     load(st + PD, (u + PD) % NS);
@@ -240,6 +255,11 @@ __device__ __forceinline__ void run_pipeline(int n_steps, Load load, Compute com
       if (st + u < n_steps) step(st + u, u, false);
   }
   wait_vm0();
+}
+
+template <int NS, int PD, int L, int NPEEL, class Load, class Compute>
+__device__ __forceinline__ void run_pipeline(int n_steps, Load load, Compute compute) {
+  run_pipeline<NS, PD, L, NPEEL>(n_steps, load, compute, [] {});
 }
 
 // Loads rows j0 .. j0 + NR - 1 (rows past T - 1 re-read row T - 1) of a row-major
