@@ -307,6 +307,31 @@ __device__ __forceinline__ bool xcd_item(int b, int nd, int nf, int& row, int& i
   return t < nf;
 }
 
+// Maximum and sum of the 32 values of two accumulator tiles as balanced trees: the row
+// statistics of a tile then take a handful of dependent steps instead of a 32-long chain.
+__device__ __forceinline__ float tree_max32(const f32x16 (&s)[2]) {
+  float v[16];
+#pragma unroll
+  for (int r = 0; r < 16; ++r) v[r] = fmaxf(s[0][r], s[1][r]);
+#pragma unroll
+  for (int w = 8; w >= 1; w >>= 1)
+#pragma unroll
+    for (int r = 0; r < w; ++r) v[r] = fmaxf(v[r], v[r + w]);
+  return v[0];
+}
+template <int N>
+__device__ __forceinline__ float tree_sum(const float* x) {
+  static_assert(N >= 1 && (N & (N - 1)) == 0, "power of two");
+  float v[N];
+#pragma unroll
+  for (int r = 0; r < N; ++r) v[r] = x[r];
+#pragma unroll
+  for (int w = N / 2; w >= 1; w >>= 1)
+#pragma unroll
+    for (int r = 0; r < w; ++r) v[r] += v[r + w];
+  return v[0];
+}
+
 // Combine a value across the two half-waves (lanes l and l ^ 32) with v_permlane32_swap (no
 // LDS round trip). Swapping two copies of x leaves the lower half's values in the first and
 // the upper half's in the second, on every lane. Inline assembly keeps the two copies in

@@ -156,9 +156,16 @@ __device__ __forceinline__ void load_q(const bf16* Q, int i, int T, int hh, bf16
     qf[kk] = *reinterpret_cast<const bf16x8*>(Q + (size_t)min(i, T - 1) * D + kk * 16 + hh * 8);
 }
 
+// Row normalisers: key tiles go through LSE_STAGES LDS stages, three tiles ahead of their
+// use, so a short item (a few tiles; the items are many) does not wait for each tile's load
+// in turn. The running max is raised lazily (only when a tile's max exceeds it by more than
+// 2^8 in log2 units), and the sum rescaled then, per lane and without a branch.
+constexpr int LSE_STAGES = 4;
+constexpr float kLseSlack = 8.0f;
+
 template <int D>
 __global__ __launch_bounds__(NTH, 2) void var_lse_kernel(const VarParams p) {
-  __shared__ __attribute__((aligned(16))) KTile<D> stg[2];
+  __shared__ __attribute__((aligned(16))) KTile<D> stg[LSE_STAGES];
   const int n_qt = p.n_it;
   // heaviest query tiles first over the whole grid (an XCD-contiguous order, which shares
   // key rows through one L2 but ends on a tail of heavy tiles, measured 0.13 -> 0.17 ms)
@@ -173,42 +180,42 @@ __global__ __launch_bounds__(NTH, 2) void var_lse_kernel(const VarParams p) {
   uint32_t koff[D / 16];
   key_offsets<D>(m, hh, koff);
   const bf16* K = p.k + head * D;
-  float mx_run = kNegInf, l = 0.f;
+  float m_run = kNegInf, l = 0.f;
   const int n_kt = min(2 * qt + 2, (T + BN - 1) / BN);
-  tile_load_rows<D / 8, BN, NTH / 64>(stg[0].k, K, 0, T);
-  wait_vm0();
-  __syncthreads();
-  for (int J = 0; J < n_kt; ++J) {
-    if (J + 1 < n_kt) tile_load_rows<D / 8, BN, NTH / 64>(stg[(J + 1) & 1].k, K, (J + 1) * BN, T);
+  auto load = [&](int J, int u) {   // steps past the end reload the last tile (never used)
+    tile_load_rows<D / 8, BN, NTH / 64>(stg[u].k, K, min(J, n_kt - 1) * BN, T);
+  };
+  constexpr int PERW = BN * (D / 8) / NTH;
+  auto tile = [&](int J, int u, bool) {
     const int j0 = J * BN;
-    if (j0 <= i0w) {
-      f32x16 s[2];
-      scores<D>(stg[J & 1].k, qf, koff, s);
-      const bool diag = j0 + BN - 1 > i0w;
-      float mx = kNegInf;
+    if (j0 > i0w) return;
+    f32x16 s[2];
+    scores<D>(stg[u].k, qf, koff, s);
+    const bool diag = j0 + BN - 1 > i0w;
+    if (diag) {
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          float x = s[kb][r] * p.c;
-          if (diag && j0 + kb * 32 + acc_pos(r, hh) > i) x = kNegInf;
-          s[kb][r] = x;
-          mx = fmaxf(mx, x);
-        }
-      mx = xhalf_max(mx);
-      const float m_new = fmaxf(mx_run, mx);
-      l *= (mx_run == kNegInf) ? 0.f : __builtin_amdgcn_exp2f(mx_run - m_new);
-      mx_run = m_new;
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) l += __builtin_amdgcn_exp2f(s[kb][r] - mx_run);
+        for (int r = 0; r < 16; ++r)
+          if (j0 + kb * 32 + acc_pos(r, hh) > i) s[kb][r] = kNegInf;
     }
-    wait_vm0();
-    __syncthreads();
-  }
+    const float mx = xhalf_max(tree_max32(s)) * p.c;
+    const bool up = mx > m_run + kLseSlack;
+    const float m_new = up ? mx : m_run;
+    // m_run = -inf on the first tile: the factor is exp2(-inf) = 0 and l starts from 0
+    l *= up ? __builtin_amdgcn_exp2f(m_run - m_new) : 1.f;
+    m_run = m_new;
+    float e[32];
+#pragma unroll
+    for (int x = 0; x < 32; ++x) e[x] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[x >> 4][x & 15], p.c, -m_run));
+    l += tree_sum<32>(e);
+  };
+  run_pipeline<LSE_STAGES, LSE_STAGES - 1, PERW, 0>(n_kt, load, tile, [&] {
+#pragma unroll
+    for (int kk = 0; kk < D / 16; ++kk) settle(qf[kk]);
+  });
   const float lt = xhalf_sum(l);
-  if (i < T && hh == 0) p.lse2[head + i] = mx_run + __log2f(lt);
+  if (i < T && hh == 0) p.lse2[head + i] = m_run + __log2f(lt);
 }
 
 // KL = false: Welford's mean and M2, the tile's partial is sum M2 (Eq. (1)).
@@ -282,18 +289,28 @@ __global__ __launch_bounds__(NTH, 2) void var_welford_kernel(const VarParams p) 
         for (int r = 0; r < 16; ++r) {
           const float z = __builtin_fmaf(s[kb][r], p.c, -l2);
           float a = __builtin_amdgcn_exp2f(z);
-          if (diag && j0 + kb * 32 + acc_pos(r, hh) > i) a = 0.f;
           const int x = kb * 16 + r;
+          if constexpr (KL) {
+            if (diag && j0 + kb * 32 + acc_pos(r, hh) > i) a = 0.f;
+            if (a > 0.f) alog = __builtin_fmaf(a, z, alog);
+          }
+          // Welford: entries after the query (diagonal tiles) accumulate whatever their
+          // logits give and are set to 0 once after the loop, which is the same as feeding
+          // them zeros, since every entry's mean and M2 are its own
           const float dlt = a - mean[x];
           mean[x] = __builtin_fmaf(dlt, rn, mean[x]);
-          if constexpr (KL) {
-            if (a > 0.f) alog = __builtin_fmaf(a, z, alog);
-          } else {
-            m2[x] = __builtin_fmaf(dlt, a - mean[x], m2[x]);
-          }
+          if constexpr (!KL) m2[x] = __builtin_fmaf(dlt, a - mean[x], m2[x]);
         }
     }
   });
+  if (diag) {   // entries after the query: A_hat = 0 and no deviation
+#pragma unroll
+    for (int x = 0; x < 32; ++x)
+      if (j0 + (x >> 4) * 32 + acc_pos(x & 15, hh) > i) {
+        mean[x] = 0.f;
+        if constexpr (!KL) m2[x] = 0.f;
+      }
+  }
 
   float sum = 0.f;
   if (i < T) {
