@@ -267,22 +267,26 @@ __device__ void dv_frz(const BwdParams& p, int h, int chunk, int kt, unsigned ch
   // this lane's chunks of each step's tile: folded column col0 + 8 chunk is column d of batch
   // element bb (columns past B * D, in a partial last chunk, read element B - 1 and are not
   // stored); 1 KiB block (w PERW + x) of the tile
-  const bf16* src[PERW];
+  // grow[x]: this lane's chunk in row kbase + srow[x] (step 0) of the folded dO
+  const bf16* grow[PERW];
   int srow[PERW];
 #pragma unroll
   for (int x = 0; x < PERW; ++x) {
     const int pch = (w * PERW + x) * 64 + lane, row = pch / CPR;
     const int col = col0 + ((pch % CPR) ^ swz16<CPR>(row)) * 8;
     const int bb = min(col / D, B - 1), d = col % D;
-    src[x] = p.dO + (((size_t)bb * H + h) * T) * D + d;
+    grow[x] = p.dO + (((size_t)bb * H + h) * T + kbase + row) * D + d;
     srow[x] = row;
   }
   auto load = [&](int st, int u) {
     FrzStage<FC>& sm = stg[u];
     const int i0 = kbase + st * BMQ;
+    const bool full = i0 + BMQ <= T;
 #pragma unroll
     for (int x = 0; x < PERW; ++x)
-      g2lds16(src[x] + (size_t)min(i0 + srow[x], T - 1) * D, lds_addr(sm.gs) + (uint32_t)(w * PERW + x) * 1024u);
+      // steps with all 32 queries before T add their rows; the last ones clamp rows to T - 1
+      g2lds16(grow[x] + (ptrdiff_t)(full ? st * BMQ : min(i0 + srow[x], T - 1) - kbase - srow[x]) * D,
+              lds_addr(sm.gs) + (uint32_t)(w * PERW + x) * 1024u);
     // table entry e = 64 y + lane: log Z of query i0 + e (e < 32), then rho at distance
     // i0 - (k0w + 31) + e - 32 (32 <= e < 95)
 #pragma unroll
@@ -404,10 +408,27 @@ __device__ void dkdv_dyn(const BwdParams& p, int b, int h, int kt, unsigned char
 
   const bf16* tsrc = (w < NWK / 2) ? Q : G;
   const int wl = w & (NWK / 2 - 1);
+  // per-lane offsets of a step's rows from its first row, and the lane's table entry (lanes
+  // 0..31 lse * log2(e) of query lane, 32..63 delta) at step 0: for steps whose 32 queries all
+  // lie before T the loads then cost no address arithmetic
+  uint32_t roff[PERW];
+#pragma unroll
+  for (int x = 0; x < PERW; ++x) {
+    const int pch = (wl * PERW + x) * 64 + lane, row = pch / CPR;
+    roff[x] = 2u * (uint32_t)(row * D + ((pch % CPR) ^ swz16<CPR>(row)) * 8);
+  }
+  const float* tab0 = ((lane < 32) ? p.ls2 : p.delta) + head + kbase + (lane & 31);
   auto load = [&](int st, int u) {
     DynStage<D>& sm = smem->st[u];
     const int i0 = kbase + st * BMQ;
     bf16* tile = (w < NWK / 2) ? sm.qs : sm.gs;
+    if (i0 + BMQ <= T) {
+      const bf16* base = tsrc + (size_t)i0 * D;
+#pragma unroll
+      for (int x = 0; x < PERW; ++x) g2lds16_s(base, roff[x], lds_addr(tile) + (uint32_t)(wl * PERW + x) * 1024u);
+      g2lds4(tab0 + st * BMQ, lds_addr(sm.tab[w]));
+      return;
+    }
     // rows past T (the last step, and the steps past the end) re-read row T - 1; the base row
     // ib <= every row read keeps the unsigned per-lane offsets non-negative
     const int ib = min(i0, T - 1);
@@ -418,7 +439,7 @@ __device__ void dkdv_dyn(const BwdParams& p, int b, int h, int kt, unsigned char
       const uint32_t o = 2u * (uint32_t)((min(i0 + row, T - 1) - ib) * D + c * 8);
       g2lds16_s(tsrc + (size_t)ib * D, o, lds_addr(tile) + (uint32_t)(wl * PERW + x) * 1024u);
     }
-    // table: lanes 0..31 lse * log2(e) of query i0 + lane, lanes 32..63 delta
+    // table: lanes 0..31 lse * log2(e) of query i0 + lane (+inf past T), lanes 32..63 delta
     const int i = i0 + (lane & 31);
     const float* a = (lane < 32) ? ((i < T) ? p.ls2 + head + i : &kSentinel[0]) : p.delta + head + min(i, T - 1);
     g2lds4(a, lds_addr(sm.tab[w]));
@@ -608,10 +629,19 @@ __global__ __launch_bounds__(64 * NWD, 2) void dq_kernel(const BwdParams p) {
   // diagonal (BMD = 2 BND) come first: they run in a peeled region with the causal mask, and
   // every later tile is a full one with no mask arithmetic.
   const int n_kt = min((qt + 1) * (BMD / BND), (T + BND - 1) / BND);
+  // K and V tiles share their per-lane offsets, kept in registers at D = 128 only: at D = 64
+  // the two registers raise the kernel past 128 per lane, which costs a workgroup per CU
+  // (alternating runs, 124M shape: dQ 0.239 -> 0.250 ms with them)
+  const RowTileLoader<CPR, BND, NWD> rows;
   auto load = [&](int s, int u) {
     const int J = max(n_kt - 1 - s, 0);   // steps past the end reload tile 0
-    tile_load_rows<CPR, BND, NWD>(stg[u].k, K, J * BND, T);
-    tile_load_rows<CPR, BND, NWD>(stg[u].v, V, J * BND, T);
+    if constexpr (D == 128) {
+      rows.load(stg[u].k, K, J * BND, T);
+      rows.load(stg[u].v, V, J * BND, T);
+    } else {
+      tile_load_rows<CPR, BND, NWD>(stg[u].k, K, J * BND, T);
+      tile_load_rows<CPR, BND, NWD>(stg[u].v, V, J * BND, T);
+    }
   };
 
   uint32_t koff[D / 16], toff[NDB][2];

@@ -137,10 +137,11 @@ __device__ void dyn_item(const FwdParams& p, int b, int h, int qt, unsigned char
   // diagonal (BM = 2 BN) come first: they run in a peeled region with the causal mask, and
   // every later tile is a full one with no mask arithmetic.
   const int n_kt = min((qt + 1) * (BM / BN), (T + BN - 1) / BN);
+  const RowTileLoader<CPR, BN, NW> rows;   // K and V tiles share their per-lane offsets
   auto load = [&](int s, int u) {
     const int J = max(n_kt - 1 - s, 0);   // steps past the end reload tile 0
-    tile_load_rows<CPR, BN, NW>(st[u].k, K, J * BN, T);
-    tile_load_rows<CPR, BN, NW>(st[u].v, V, J * BN, T);
+    rows.load(st[u].k, K, J * BN, T);
+    rows.load(st[u].v, V, J * BN, T);
   };
   // per-lane LDS offsets: K rows in pi order (one per k-step), V^T reads (per d-block)
   constexpr int NDB = D / 32;
@@ -256,22 +257,26 @@ __device__ void frz_item(const FwdParams& p, int h, int chunk, int qt, unsigned 
   // element bb (columns past B * D, in a partial last chunk, read element B - 1 and are not
   // stored); 1 KiB block (w PERW + x) of the tile
   constexpr int PERW = BN * CPR / (64 * NW);
-  const bf16* src[PERW];
+  // vrow[x]: this lane's chunk in row srow[x] of key tile 0 (V of h's key/value head)
+  const bf16* vrow[PERW];
   int srow[PERW];
 #pragma unroll
   for (int x = 0; x < PERW; ++x) {
     const int pch = (w * PERW + x) * 64 + lane, row = pch / CPR;
     const int col = col0 + ((pch % CPR) ^ swz<CPR>(row)) * 8;
     const int bb = min(col / D, B - 1), d = col % D;
-    src[x] = p.v + (((size_t)bb * p.Hkv + h / p.G) * T) * D + d;   // V of h's key/value head
+    vrow[x] = p.v + (((size_t)bb * p.Hkv + h / p.G) * T + row) * D + d;
     srow[x] = row;
   }
   auto load = [&](int J, int u) {
     FrzStage<FC>& sm = st[u];
     const int j0 = J * BN;
+    const bool full = j0 + BN <= T;
 #pragma unroll
     for (int x = 0; x < PERW; ++x)
-      g2lds16(src[x] + (size_t)min(j0 + srow[x], T - 1) * D, lds_addr(sm.v) + (uint32_t)(w * PERW + x) * 1024u);
+      // tiles with all 64 keys before T add j0 rows; the last one clamps rows to T - 1
+      g2lds16(vrow[x] + (ptrdiff_t)(full ? j0 : min(j0 + srow[x], T - 1) - srow[x]) * D,
+              lds_addr(sm.v) + (uint32_t)(w * PERW + x) * 1024u);
     // table entry e = 64 y + lane: alpha of key j0 + e (e < 64), then rho at distance
     // i0w - (j0 + 63) + (e - 64) (64 <= e < 159); -inf past the data
 #pragma unroll
@@ -279,7 +284,7 @@ __device__ void frz_item(const FwdParams& p, int h, int chunk, int qt, unsigned 
       const int e = 64 * y + lane;
       const float* a = &kNegSentinel[0];
       if (e < BN) {
-        if (j0 + e < T) a = alpha + j0 + e;
+        if (full || j0 + e < T) a = alpha + j0 + e;
       } else if (e < 2 * BN + 31) {
         const int dd = i0w - (j0 + BN - 1) + (e - BN);
         if (dd >= 0) a = rho + min(dd, T - 1);

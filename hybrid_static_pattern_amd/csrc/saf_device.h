@@ -282,6 +282,37 @@ __device__ __forceinline__ void tile_load_rows(bf16* tile, const bf16* src, int 
   }
 }
 
+// tile_load_rows with the per-lane offsets computed once: for a tile whose rows all lie before
+// T (every tile of a loop but possibly the one holding the last row), lane l's offset from the
+// tile's first row depends on the lane and the wave only, so each load is a scalar base plus
+// that offset and costs no vector instruction. Tiles that reach past T take tile_load_rows.
+template <int CPR, int NR, int NW>
+struct RowTileLoader {
+  static constexpr int PERW = NR * CPR / (64 * NW);
+  static_assert(PERW >= 1 && NR * CPR == PERW * 64 * NW, "tile must split evenly over the waves");
+  uint32_t off[PERW];
+  __device__ __forceinline__ RowTileLoader() {
+    const int w = wave_id(), lane = lane_id();
+#pragma unroll
+    for (int x = 0; x < PERW; ++x) {
+      const int pch = (w * PERW + x) * 64 + lane, row = pch / CPR;
+      const int c = (pch % CPR) ^ swz<CPR>(row);
+      off[x] = 2u * (uint32_t)(row * (CPR * 8) + c * 8);
+    }
+  }
+  // rows j0 .. j0 + NR - 1 of the row-major [T, 8 CPR] matrix src
+  __device__ __forceinline__ void load(bf16* tile, const bf16* src, int j0, int T) const {
+    if (j0 + NR <= T) {
+      const bf16* base = src + (size_t)j0 * (CPR * 8);
+      const uint32_t lb = lds_addr(tile) + (uint32_t)(wave_id() * PERW) * 1024u;
+#pragma unroll
+      for (int x = 0; x < PERW; ++x) g2lds16_s(base, off[x], lb + (uint32_t)x * 1024u);
+    } else {
+      tile_load_rows<CPR, NR, NW>(tile, src, j0, T);
+    }
+  }
+};
+
 // XCD-aware work-item map. MI355X has 8 XCDs, each with its own L2, and workgroup b runs on
 // XCD b % 8. Items come in rows (one row per tile position, heaviest row first) of nd
 // "stream" items (one per ordinary (b, h): the items of one stream read the same K/V or Q/dO

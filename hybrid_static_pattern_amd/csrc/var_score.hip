@@ -182,8 +182,9 @@ __global__ __launch_bounds__(NTH, 2) void var_lse_kernel(const VarParams p) {
   const bf16* K = p.k + head * D;
   float m_run = kNegInf, l = 0.f;
   const int n_kt = min(2 * qt + 2, (T + BN - 1) / BN);
+  const RowTileLoader<D / 8, BN, NTH / 64> rows;
   auto load = [&](int J, int u) {   // steps past the end reload the last tile (never used)
-    tile_load_rows<D / 8, BN, NTH / 64>(stg[u].k, K, min(J, n_kt - 1) * BN, T);
+    rows.load(stg[u].k, K, min(J, n_kt - 1) * BN, T);
   };
   constexpr int PERW = BN * (D / 8) / NTH;
   auto tile = [&](int J, int u, bool) {
