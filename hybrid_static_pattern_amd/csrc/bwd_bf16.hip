@@ -26,6 +26,7 @@
 // LDS, one barrier per step; the transposed operands (dO^T, Q^T, K^T) are read from the
 // same row-major tiles with ds_read_b64_tr_b16. The split into a key-stationary and a query-stationary kernel recomputes S and dP once
 // more instead of accumulating dQ with atomics; every output is written exactly once.
+#include "frz_amax.h"
 #include "saf_device.h"
 #include "saf_internal.h"
 
@@ -55,6 +56,10 @@ struct BwdParams {
   float* dq;
   float* dk;
   float* dv;
+  FrzAmaxArgs famax;    // the frozen dO's block maxima, extra dQ items n_dq .. n_dq + n_famax - 1
+  int n_dq, n_famax;
+  const uint16_t* dh;   // frozen heads' dO in fp16, scaled per (b, frozen head): [B, n_frz, T, D]
+  const int32_t* dexp;  // the scales' exponents [B * n_frz]: dV of batch b is 2^e times the product
   int tab_stride, B, H, T;
   int Hkv, G;   // key/value heads; query heads per key/value head
   float c;      // scale * log2(e)
@@ -233,9 +238,11 @@ constexpr int dkdv_smem_bytes() {
 // Frozen item (h, 128-key tile, column chunk): dV_b[j] = sum_{i>=j} P(i,j) dO_b[i] for the
 // batch folded into FC (64, 128 or 256) columns. Each wave keeps its 32 keys x FC columns of
 // fp32 dV; P^T is regenerated per lane from alpha, rho and log Z (entries for j > i come out
-// as 0 from the -inf distances of the window) and split into bf16 high and low parts.
+// as 0 from the -inf distances of the window) and rounded to fp16, and the product takes the
+// fp16 copy of dO scaled by 2^-e_bf (frz_half.hip): one fp16 MFMA per tile, P with 11
+// significant bits, and dV_b scaled back by 2^e_bf when stored. f is h's frozen-head index.
 template <int D, int FC>
-__device__ void dv_frz(const BwdParams& p, int h, int chunk, int kt, unsigned char* smem_raw) {
+__device__ void dv_frz(const BwdParams& p, int h, int f, int chunk, int kt, unsigned char* smem_raw) {
   constexpr int CPR = FC / 8;
   constexpr int NCB = FC / 16;
   // 16-byte chunks per lane per step: the 32 x FC tile splits evenly over the workgroup's
@@ -275,7 +282,7 @@ __device__ void dv_frz(const BwdParams& p, int h, int chunk, int kt, unsigned ch
     const int pch = (w * PERW + x) * 64 + lane, row = pch / CPR;
     const int col = col0 + ((pch % CPR) ^ swz16<CPR>(row)) * 8;
     const int bb = min(col / D, B - 1), d = col % D;
-    grow[x] = p.dO + (((size_t)bb * H + h) * T + kbase + row) * D + d;
+    grow[x] = reinterpret_cast<const bf16*>(p.dh) + (((size_t)bb * p.n_frz + f) * T + kbase + row) * D + d;
     srow[x] = row;
   }
   auto load = [&](int st, int u) {
@@ -310,27 +317,20 @@ __device__ void dv_frz(const BwdParams& p, int h, int chunk, int kt, unsigned ch
     const float* tb = sm.tab[w];
     // queries i0 + 8 g + e; window index of distance i - j is (8 g + e) - (16 kg + n) + 31
     const int qofs = 8 * g;
-    bf16x8 ahi[NKG], alo[NKG];
+    f16x8 ap[NKG];
 #pragma unroll
     for (int kg = 0; kg < NKG; ++kg) {
       const int rbase = BMQ + qofs - (16 * kg + n) + KPW - 1;
-      float ph[8], pl[8];
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const float pv = __builtin_amdgcn_exp2f(__builtin_fmaf(tb[rbase + e] - tb[qofs + e], kLog2e, a2[kg]));
-        const bf16 hi = (bf16)pv;
-        ph[e] = (float)hi;
-        pl[e] = pv - ph[e];
-      }
-      ahi[kg] = pack8(ph);
-      alo[kg] = pack8(pl);
+      for (int e = 0; e < 8; ++e)
+        ap[kg][e] = (_Float16)__builtin_amdgcn_exp2f(__builtin_fmaf(tb[rbase + e] - tb[qofs + e], kLog2e, a2[kg]));
     }
     pipelined<NCB>([&](int cb) { return lds_b16<CPR>(sm.gs, goff ^ (32u * cb)); },
                    [&](int cb, const bf16x8& bg) {
+                     const f16x8 bh = __builtin_bit_cast(f16x8, bg);
 #pragma unroll
-                     for (int kg = 0; kg < NKG; ++kg) dv[kg][cb] = mfma16(ahi[kg], bg, dv[kg][cb]);
-#pragma unroll
-                     for (int kg = 0; kg < NKG; ++kg) dv[kg][cb] = mfma16(alo[kg], bg, dv[kg][cb]);
+                     for (int kg = 0; kg < NKG; ++kg)
+                       dv[kg][cb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ap[kg], bh, dv[kg][cb], 0, 0, 0);
                    });
   };
 
@@ -347,10 +347,11 @@ __device__ void dv_frz(const BwdParams& p, int h, int chunk, int kt, unsigned ch
       const int col = col0 + 16 * cb + n;
       if (16 * cb >= ncols) continue;
       const int bb = col / D, d = col % D;
+      const int e2 = p.dexp[bb * p.n_frz + f];
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int key = k0w + 16 * kg + 4 * g + r;
-        if (key < T) p.dv[(((size_t)bb * H + h) * T + key) * D + d] = dv[kg][cb][r];
+        if (key < T) p.dv[(((size_t)bb * H + h) * T + key) * D + d] = ldexpf(dv[kg][cb][r], e2);
       }
     }
 }
@@ -564,7 +565,7 @@ __global__ __launch_bounds__(NTK, 2) void dkdv_kernel(const BwdParams p) {
     dkdv_dyn<D>(p, rem / p.n_dyn, p.dyn[rem % p.n_dyn], kt, smem);
   } else {
     rem -= nd;
-    dv_frz<D, FC>(p, p.frz[rem / p.n_chunks], rem % p.n_chunks, kt, smem);
+    dv_frz<D, FC>(p, p.frz[rem / p.n_chunks], rem / p.n_chunks, rem % p.n_chunks, kt, smem);
   }
 }
 
@@ -582,6 +583,10 @@ __global__ __launch_bounds__(64 * NWD, 2) void dq_kernel(const BwdParams p) {
   constexpr int NDB = D / 32;
   __shared__ __attribute__((aligned(16))) unsigned char smem_raw[NSD * sizeof(DqSmem<D>)];
   DqSmem<D>* stg = reinterpret_cast<DqSmem<D>*>(smem_raw);
+  if ((int)blockIdx.x >= p.n_dq) {   // a block of the frozen dO's maxima (frz_amax.h)
+    frz_amax_item(p.famax, p.frz, blockIdx.x - p.n_dq, reinterpret_cast<float*>(smem_raw));
+    return;
+  }
   int row, bh;
   if (!xcd_item(blockIdx.x, p.B * p.n_dyn, 0, row, bh)) return;
   const int qt = p.n_tiles - 1 - row;   // heaviest q-tile first
@@ -730,6 +735,8 @@ BwdParams make_params(const AttnArgs& a, const void* q, const void* k, const voi
   p.dq = dq;
   p.dk = dk;
   p.dv = dv;
+  p.dh = nullptr;
+  p.dexp = nullptr;
   p.tab_stride = a.tab_stride;
   p.B = a.B;
   p.H = a.H;
@@ -774,25 +781,31 @@ hipError_t launch_delta(const AttnArgs& a, const void* o, const void* dO, float*
 hipError_t launch_bwd_bf16(const AttnArgs& a, const void* q, const void* k, const void* v,
                            const void* o, const void* dO, const float* lse,
                            const float* alpha, const float* rho, float* dq, float* dk,
-                           float* dv, float* delta, hipStream_t s) {
+                           float* dv, float* delta, const FrzHalfWs& fh, hipStream_t s) {
   float* ls2 = delta + attn_ws_floats(a);
   BwdParams p = make_params(a, q, k, v, dO, lse, delta, alpha, rho, dq, dk, dv);
+  p.dh = fh.dh;
+  p.dexp = fh.dexp;
   p.o = static_cast<const bf16*>(o);
   p.ls2 = ls2;
   hipError_t e = hipSuccess;
   // dQ first: its items also write delta and lse * log2(e) of the ordinary rows, which the
-  // dK/dV items read
+  // dK/dV items read, and, as extra items after its own, the block maxima of the frozen heads'
+  // dO; then the frozen dO in fp16 (frz_half.hip) for the frozen dK/dV items
+  if (p.n_frz > 0) p.famax = frz_amax_args(a, dO, fh);
+  p.n_famax = p.n_frz > 0 ? frz_half_blocks(a) * a.B * p.n_frz : 0;
   if (p.n_dyn > 0) {
     p.n_tiles = (a.T + BMD - 1) / BMD;
-    const int n_dq = p.n_tiles * xcd_row_slots(a.B * p.n_dyn, 0);
+    p.n_dq = p.n_tiles * xcd_row_slots(a.B * p.n_dyn, 0);
     prof_begin("dq", s);
     if (a.D == 64)
-      hipLaunchKernelGGL(dq_kernel<64>, dim3(n_dq), dim3(64 * NWD), 0, s, p);
+      hipLaunchKernelGGL(dq_kernel<64>, dim3(p.n_dq + p.n_famax), dim3(64 * NWD), 0, s, p);
     else
-      hipLaunchKernelGGL(dq_kernel<128>, dim3(n_dq), dim3(64 * NWD), 0, s, p);
+      hipLaunchKernelGGL(dq_kernel<128>, dim3(p.n_dq + p.n_famax), dim3(64 * NWD), 0, s, p);
     prof_end(s);
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
+  if ((e = launch_frz_half(a, dO, fh, p.n_dyn > 0, s)) != hipSuccess) return e;
   p.n_tiles = (a.T + BNK - 1) / BNK;
   // folded columns per frozen item: B * D rounded up to 64, 128 or 256, except
   //  * D = 64: at most 128, so that the launch's LDS (the frozen stages are sized by the

@@ -182,7 +182,8 @@ saf_status saf_attn_fwd(const saf_attn_desc* desc, const void* q, const void* k,
 size_t saf_attn_workspace_size(const saf_attn_desc* desc) {
   saf::AttnArgs a;
   if (validate_attn(desc, &a) != SAF_OK) return 0;
-  return (2 * saf::attn_ws_floats(a) + 2 * saf::gqa_ws_floats(a)) * sizeof(float);
+  return (2 * saf::attn_ws_floats(a) + 2 * saf::gqa_ws_floats(a)) * sizeof(float) +
+         (a.bf16 ? saf::frz_half_ws_bytes(a) : 0);
 }
 
 saf_status saf_attn_bwd(const saf_attn_desc* desc, const void* q, const void* k, const void* v,
@@ -216,8 +217,11 @@ saf_status saf_attn_bwd(const saf_attn_desc* desc, const void* q, const void* k,
     dk_out = delta + 2 * saf::attn_ws_floats(a);
     dv_out = dk_out + saf::gqa_ws_floats(a);
   }
+  // bf16: the frozen heads' dO in fp16 after the float32 arrays (see frz_half.hip)
+  saf::FrzHalfWs fh{};
+  if (a.bf16) fh = saf::frz_half_ws(a, delta + 2 * saf::attn_ws_floats(a) + 2 * saf::gqa_ws_floats(a));
   hipError_t e = a.bf16 ? saf::launch_bwd_bf16(a, q, k, v, o, dO, lse, alpha, rho, static_cast<float*>(dq),
-                                               dk_out, dv_out, delta, s)
+                                               dk_out, dv_out, delta, fh, s)
                         : saf::launch_bwd_fp32(a, q, k, v, o, dO, lse, alpha, rho, static_cast<float*>(dq),
                                                dk_out, dv_out, delta, s);
   if (e == hipSuccess && a.G > 1)

@@ -55,14 +55,51 @@ inline size_t attn_ws_floats(const AttnArgs& a) { return ((size_t)a.B * a.H * a.
 inline size_t gqa_ws_floats(const AttnArgs& a) {
   return a.G > 1 ? ((size_t)a.B * a.H * a.T * a.D + 63) / 64 * 64 : 0;
 }
+// Frozen heads' dO in float16 for the frozen-head dV product (frz_half.hip): per batch entry b
+// and frozen head f, dO[b, frz[f]] scaled by 2^-e_bf and rounded to fp16, [B, n_frz, T, D]; the
+// block maxima of the first pass; e_bf [B * n_frz]. Blocks of kFrzBlock values.
+constexpr int kFrzBlock = 8192;
+struct FrzHalfWs {
+  uint16_t* dh;
+  float* amax;
+  int32_t* dexp;
+};
+inline int frz_half_blocks(const AttnArgs& a) {
+  return (int)(((size_t)a.T * a.D + kFrzBlock - 1) / kFrzBlock);
+}
+// bytes of the three arrays, each padded to 256 bytes (0 without frozen heads)
+inline size_t frz_half_ws_bytes(const AttnArgs& a) {
+  if (a.heads.n_frz == 0) return 0;
+  const size_t ns = (size_t)a.B * a.heads.n_frz;
+  auto pad = [](size_t x) { return (x + 255) / 256 * 256; };
+  return pad(ns * a.T * a.D * 2) + pad(ns * frz_half_blocks(a) * 4) + pad(ns * 4);
+}
+inline FrzHalfWs frz_half_ws(const AttnArgs& a, void* base) {
+  const size_t ns = (size_t)a.B * a.heads.n_frz;
+  auto pad = [](size_t x) { return (x + 255) / 256 * 256; };
+  char* c = static_cast<char*>(base);
+  FrzHalfWs w;
+  w.dh = reinterpret_cast<uint16_t*>(c);
+  c += pad(ns * a.T * a.D * 2);
+  w.amax = reinterpret_cast<float*>(c);
+  c += pad(ns * frz_half_blocks(a) * 4);
+  w.dexp = reinterpret_cast<int32_t*>(c);
+  return w;
+}
+// The block-maxima pass (unless amax_done: the dQ kernel ran it), then the conversion.
+hipError_t launch_frz_half(const AttnArgs& a, const void* dO, const FrzHalfWs& ws, bool amax_done,
+                           hipStream_t s);
+struct FrzAmaxArgs;
+FrzAmaxArgs frz_amax_args(const AttnArgs& a, const void* dO, const FrzHalfWs& ws);
+
 hipError_t launch_gqa_reduce(const AttnArgs& a, const float* dk_heads, const float* dv_heads, float* dk,
                              float* dv, hipStream_t s);
 
-// Backward. `delta` is the workspace.
+// Backward. `delta` is the workspace; `fh` the frozen heads' fp16 dO (launch_frz_half first).
 hipError_t launch_bwd_bf16(const AttnArgs& a, const void* q, const void* k, const void* v,
                            const void* o, const void* dO, const float* lse,
                            const float* alpha, const float* rho, float* dq, float* dk,
-                           float* dv, float* delta, hipStream_t s);
+                           float* dv, float* delta, const FrzHalfWs& fh, hipStream_t s);
 hipError_t launch_bwd_fp32(const AttnArgs& a, const void* q, const void* k, const void* v,
                            const void* o, const void* dO, const float* lse,
                            const float* alpha, const float* rho, float* dq, float* dk,

@@ -29,7 +29,7 @@ EXPORTS = (
 )
 
 # Bytes of the library's own device array behind saf_attn_bwd_noalloc (SAF_NOALLOC_SCRATCH_BYTES).
-NOALLOC_SCRATCH_BYTES = 32 << 20
+NOALLOC_SCRATCH_BYTES = 64 << 20
 
 
 class SafError(RuntimeError):

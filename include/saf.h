@@ -107,7 +107,7 @@ saf_status saf_attn_bwd(const saf_attn_desc* desc, const void* q, const void* k,
                         void* dv, void* workspace, size_t ws_bytes, void* stream);
 
 /* Bytes of the device array that saf_attn_bwd_noalloc takes its workspace from. */
-#define SAF_NOALLOC_SCRATCH_BYTES ((size_t)32 << 20)
+#define SAF_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
 
 /* saf_attn_bwd without a workspace argument, for callers that cannot allocate device memory
  * (code under HIP graph capture, tight serving loops, harnesses that forbid allocation): the
@@ -115,7 +115,9 @@ saf_status saf_attn_bwd(const saf_attn_desc* desc, const void* q, const void* k,
  * every GPU it runs on until the process ends. Arguments, results, layouts and errors are
  * those of saf_attn_bwd, whose kernels it runs; it calls no allocation routine. A layer whose
  * saf_attn_workspace_size exceeds SAF_NOALLOC_SCRATCH_BYTES is rejected with SAF_EWORKSPACE
- * before anything is enqueued (without shared key/value heads that is B * H * T above 4M).
+ * before anything is enqueued: the bf16 workspace is 8 B H T bytes plus 2 B T D bytes per
+ * frozen head (plus 8 B H T D bytes with shared key/value heads), so a layer of B = 2, H = 16,
+ * T = 8192, D = 128 fits with up to 15 of its 16 heads frozen.
  * The first call on a device looks up the array's address there (SAF_EHIP if that fails).
  * All calls on one GPU share the array: calls that overlap in time on one GPU (other streams,
  * other threads) race and must be ordered by the caller. */

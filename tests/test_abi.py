@@ -87,9 +87,9 @@ def test_bwd_workspace_contract(lib):
 
 def test_noalloc_bounds(lib):
     """saf_attn_bwd_noalloc: a layer whose workspace exceeds the library's array is rejected
-    with SAF_EWORKSPACE before anything is touched (B * H * T = 8M here); a bad descriptor
+    with SAF_EWORKSPACE before anything is touched (B * H * T = 16M here); a bad descriptor
     gets saf_attn_bwd's own error; the array's size is the header's."""
-    d, mask = _desc(B=64, H=2, T=65536, stride=65536)
+    d, mask = _desc(B=64, H=4, T=65536, stride=65536)
     assert lib.saf_attn_workspace_size(ctypes.byref(d)) > saf.NOALLOC_SCRATCH_BYTES
     st = lib.saf_attn_bwd_noalloc(ctypes.byref(d), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, None,
                                   FAKE, FAKE, FAKE, None)

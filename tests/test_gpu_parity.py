@@ -278,6 +278,38 @@ def test_alpha_rho_shift_invariance(S):
     compare_layer(L2, shifted)
 
 
+@pytest.mark.parametrize("k", [20, -20, 60, -60])
+def test_frozen_dv_power_of_two_scaling(S, k):
+    """The frozen-head dV product takes dO in fp16 after scaling each (batch, frozen head) slice
+    by a power of two chosen from its largest magnitude, and scales dV back: dO times 2^k
+    (exact in bf16) must give the frozen heads' dV times 2^k exactly, far outside fp16's range
+    too; ordinary heads' gradients scale the same way within their float32 rounding."""
+    L = inputs.make_layer(2, 3, 300, 128, dtype="bf16", seed=31, frozen_heads=[0, 2])
+    base = run(S, L)
+    L2 = dict(L)
+    L2["do"] = (L["do"] * 2.0 ** k).astype(np.float32)
+    out = run(S, L2)
+    assert np.array_equal(out["dv"][:, [0, 2]], base["dv"][:, [0, 2]] * 2.0 ** k)
+    compare_layer(L, base)
+
+
+def test_frozen_dv_wide_dynamic_range(S):
+    """dO rows spread over 2^-20 .. 2^10 (beyond fp16's range at both ends): the frozen heads'
+    dV against the oracle within 2e-3 of sum_i P(i, j) |dO_i| per entry (fp16 keeps 11
+    significant bits of P; dO converts exactly within 2^28 of the slice's largest value)."""
+    L = inputs.make_layer(2, 2, 257, 64, dtype="bf16", seed=32, frozen_heads=[1])
+    r = np.random.default_rng(33)
+    row_scale = 2.0 ** r.integers(-20, 11, size=(2, 2, 257, 1))
+    L["do"] = inputs.round_to_bf16((L["do"] * row_scale).astype(np.float32))
+    out = run(S, L)
+    P, _ = saf_oracle.frozen_probs(L["alpha"][1], L["rho"][1])
+    for b in range(2):
+        ref = P.T @ L["do"][b, 1].astype(np.float64)
+        bound = P.T @ np.abs(L["do"][b, 1].astype(np.float64))
+        err = np.abs(out["dv"][b, 1] - ref)
+        assert np.all(err <= 2e-3 * bound + 1e-30), (b, float((err / (bound + 1e-30)).max()))
+
+
 def test_frozen_equals_dynamic_rank1(S):
     """Affine rho(d) = -lam d: the frozen head equals an ordinary head with q_i = e0/scale,
     k_j = (alpha(j) + lam j) e0 (float32 path)."""
