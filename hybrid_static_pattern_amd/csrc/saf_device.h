@@ -339,18 +339,7 @@ __device__ __forceinline__ bool xcd_item(int b, int nd, int nf, int& row, int& i
   return t < nf;
 }
 
-// Maximum and sum of the 32 values of two accumulator tiles as balanced trees: the row
-// statistics of a tile then take a handful of dependent steps instead of a 32-long chain.
-__device__ __forceinline__ float tree_max32(const f32x16 (&s)[2]) {
-  float v[16];
-#pragma unroll
-  for (int r = 0; r < 16; ++r) v[r] = fmaxf(s[0][r], s[1][r]);
-#pragma unroll
-  for (int w = 8; w >= 1; w >>= 1)
-#pragma unroll
-    for (int r = 0; r < w; ++r) v[r] = fmaxf(v[r], v[r + w]);
-  return v[0];
-}
+// Sum of N values as a balanced tree: a handful of dependent steps instead of an N-long chain.
 template <int N>
 __device__ __forceinline__ float tree_sum(const float* x) {
   static_assert(N >= 1 && (N & (N - 1)) == 0, "power of two");

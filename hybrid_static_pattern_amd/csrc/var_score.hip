@@ -12,6 +12,8 @@
 //                A_hat tile and the tile's sum of squared deviations;
 //   var_final    sums the per-tile partials in float64, divides by (N - 1) T^2 and ranks
 //                the heads (stable: equal scores keep the lower head index first).
+#include <type_traits>
+
 #include "saf_device.h"
 #include "saf_internal.h"
 
@@ -187,20 +189,21 @@ __global__ __launch_bounds__(NTH, 2) void var_lse_kernel(const VarParams p) {
     rows.load(stg[u].k, K, min(J, n_kt - 1) * BN, T);
   };
   constexpr int PERW = BN * (D / 8) / NTH;
-  auto tile = [&](int J, int u, bool) {
-    const int j0 = J * BN;
-    if (j0 > i0w) return;
+  auto body = [&](int j0, int u, auto diag_t) {
     f32x16 s[2];
     scores<D>(stg[u].k, qf, koff, s);
-    const bool diag = j0 + BN - 1 > i0w;
-    if (diag) {
+    if constexpr (decltype(diag_t)::value) {
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
         for (int r = 0; r < 16; ++r)
           if (j0 + kb * 32 + acc_pos(r, hh) > i) s[kb][r] = kNegInf;
     }
-    const float mx = xhalf_max(tree_max32(s)) * p.c;
+    // a chain of max3 (a balanced tree of fmaxf canonicalises every MFMA result first)
+    float mx = kNegInf;
+#pragma unroll
+    for (int x = 0; x < 32; ++x) mx = fmaxf(mx, s[x >> 4][x & 15]);
+    mx = xhalf_max(mx) * p.c;
     const bool up = mx > m_run + kLseSlack;
     const float m_new = up ? mx : m_run;
     // m_run = -inf on the first tile: the factor is exp2(-inf) = 0 and l starts from 0
@@ -210,6 +213,13 @@ __global__ __launch_bounds__(NTH, 2) void var_lse_kernel(const VarParams p) {
 #pragma unroll
     for (int x = 0; x < 32; ++x) e[x] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[x >> 4][x & 15], p.c, -m_run));
     l += tree_sum<32>(e);
+  };
+  // the causal mask only on the tiles that hold a wave's diagonal (a branch, not selects)
+  auto tile = [&](int J, int u, bool) {
+    const int j0 = J * BN;
+    if (j0 > i0w) return;
+    if (j0 + BN - 1 > i0w) body(j0, u, std::true_type{});
+    else body(j0, u, std::false_type{});
   };
   run_pipeline<LSE_STAGES, LSE_STAGES - 1, PERW, 0>(n_kt, load, tile, [&] {
 #pragma unroll
@@ -229,32 +239,54 @@ __global__ __launch_bounds__(NTH, 2) void var_welford_kernel(const VarParams p) 
   constexpr int NS = SEQ_STAGES;
   __shared__ __attribute__((aligned(16))) SeqTile<D> stg[NS];
   __shared__ float red[NTH / 64];
-  const int tile = xcd_tile(blockIdx.x, gridDim.x);
-  const int jt = tile % p.n_jt;
-  const int it = (tile / p.n_jt) % p.n_it;
-  const int h = tile / (p.n_jt * p.n_it);
+  // Work order: the tiles every wave works on (jt <= 2 it: it^2 per head) first, in contiguous
+  // ranges per XCD so that one head's query and key rows share an L2; then the tiles right
+  // of the diagonal block (jt = 2 it + 1, where two of the four waves have no causal entry:
+  // half the work), so that the last round of workgroups is a light one; then one workgroup per
+  // row band for the zeros above the diagonal.
+  const int n_full = p.H * p.n_it * p.n_it;
+  const int n_half = (p.n_jt >= 2 * p.n_it) ? p.n_it : p.n_it - 1;
+  int h, it, jt;
+  if ((int)blockIdx.x < n_full) {
+    const int tile = xcd_tile(blockIdx.x, n_full), e = tile % (p.n_it * p.n_it);
+    h = tile / (p.n_it * p.n_it);
+    it = (int)sqrtf((float)e);
+    while (it * it > e) --it;
+    while ((it + 1) * (it + 1) <= e) ++it;
+    jt = e - it * it;
+  } else if ((int)blockIdx.x < n_full + p.H * n_half) {
+    const int x = blockIdx.x - n_full;
+    h = x / n_half;
+    it = x % n_half;
+    jt = 2 * it + 1;
+  } else {
+    const int x = blockIdx.x - n_full - p.H * n_half;
+    h = x / p.n_it;
+    it = x % p.n_it;
+    jt = -1;
+  }
   const int t = threadIdx.x, lane = lane_id(), w = wave_id(), m = lane & 31, hh = lane >> 5;
   const int T = p.T;
   const int i0 = it * BM, i0w = i0 + 32 * w, i = i0w + m, j0 = jt * BN;
   float* A = p.a_hat + (size_t)h * T * T;
-  float* part = p.partial + ((size_t)h * p.n_it + it) * p.n_jt + jt;
 
-  if (j0 > i0 + BM - 1) {  // tile above the diagonal: A_hat is 0 there
-    for (int x = t; x < BM * (BN / 4); x += NTH) {
-      const int r = x / (BN / 4), c4 = x % (BN / 4);
-      const int ii = i0 + r, jj = j0 + 4 * c4;
-      if (ii < T) {
-        if ((T & 3) == 0 && jj + 3 < T) {
-          *reinterpret_cast<f32x4*>(A + (size_t)ii * T + jj) = f32x4{0.f, 0.f, 0.f, 0.f};
-        } else {
-          for (int e = 0; e < 4; ++e)
-            if (jj + e < T) A[(size_t)ii * T + jj + e] = 0.f;
-        }
+  if (jt < 0) {   // row band it above the diagonal block: A_hat is 0 there, partials are 0
+    const int c0 = (2 * it + 2) * BN;   // first column to the right of the diagonal block
+    const int w4 = (T - c0 + 3) / 4;    // 4-column groups per row (the last may be partial)
+    for (int x = t; x < BM * max(w4, 0); x += NTH) {
+      const int r = x / w4, ii = i0 + r, jj = c0 + 4 * (x % w4);
+      if (ii >= T) continue;
+      if ((T & 3) == 0) {
+        *reinterpret_cast<f32x4*>(A + (size_t)ii * T + jj) = f32x4{0.f, 0.f, 0.f, 0.f};
+      } else {
+        for (int e = 0; e < 4; ++e)
+          if (jj + e < T) A[(size_t)ii * T + jj + e] = 0.f;
       }
     }
-    if (t == 0) *part = 0.f;
+    for (int x = 2 * it + 2 + t; x < p.n_jt; x += NTH) p.partial[((size_t)h * p.n_it + it) * p.n_jt + x] = 0.f;
     return;
   }
+  float* part = p.partial + ((size_t)h * p.n_it + it) * p.n_jt + jt;
 
   float mean[32], m2[KL ? 1 : 32];
   float alog = 0.f;   // KL: sum over n and this lane's entries of a log2 a
@@ -355,13 +387,20 @@ __global__ __launch_bounds__(256) void var_final_kernel(const VarParams p) {
   __shared__ double sv[kMaxHeads];
   const int h = threadIdx.x;
   const int per = p.n_it * p.n_jt;
-  if (h < p.H) {
+  // each wave sums the partials of heads w, w + 4, ...: its lanes take every 64th partial,
+  // then a butterfly over the wave (the loads of one head are independent, not a chain)
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  for (int hh = wv; hh < p.H; hh += 4) {
+    const float* part = p.partial + (size_t)hh * per;
     double acc = 0.0;
-    const float* part = p.partial + (size_t)h * per;
-    for (int x = 0; x < per; ++x) acc += (double)part[x];
-    const double v = KL ? acc / (double)p.T : acc / ((double)(p.N - 1) * (double)p.T * (double)p.T);
-    sv[h] = v;
-    p.s_var[h] = v;
+    for (int x = lane; x < per; x += 64) acc += (double)part[x];
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) acc += __shfl_xor(acc, o, 64);
+    if (lane == 0) {
+      const double v = KL ? acc / (double)p.T : acc / ((double)(p.N - 1) * (double)p.T * (double)p.T);
+      sv[hh] = v;
+      p.s_var[hh] = v;
+    }
   }
   __syncthreads();
   if (h < p.H) {
@@ -496,7 +535,9 @@ hipError_t launch_var_score(const VarArgs& a, const void* q, const void* k, floa
   prof_end(s);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  const dim3 grid(p.n_jt * p.n_it * a.H), block(NTH);
+  // full tiles, half tiles right of each diagonal block, one zero-writer per row band
+  const int n_half = (p.n_jt >= 2 * p.n_it) ? p.n_it : p.n_it - 1;
+  const dim3 grid(a.H * (p.n_it * p.n_it + n_half + p.n_it)), block(NTH);
   prof_begin(kl ? "kl_welford" : "var_welford", s);
   if (a.D == 64) {
     if (kl) hipLaunchKernelGGL((var_welford_kernel<64, true>), grid, block, 0, s, p);
