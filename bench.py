@@ -23,15 +23,17 @@ sys.path.insert(0, ROOT)
 METRIC = "hybrid attn fwd+bwd tokens/s per layer + MFMA util (1B-shape, T=8192, r=25%)"
 PEAK_BF16_TFLOPS = 2516.6  # MI355X dense bf16 MFMA (published)
 # fp32 vector rate, the published 157.3 TFLOP/s: 256 CUs x 4 SIMDs x 32 lanes x 2 FLOP (FMA)
-# x 2.4 GHz. A probe of plain (non-packed) v_fma_f32 reaches 127 TFLOP/s on this chip, so the
-# kernels, built without the packed forms, are held to the full figure.
+# x 2.4 GHz, which counts the packed two-wide FMA. The kernels are built without the packed
+# forms; a probe of plain v_fma_f32 issues one wave64 instruction per 4 cycles per SIMD
+# (16 lanes per clock: half the published rate, 67.5 TFLOP/s at the clock it ran at), so the
+# reported fraction of the published peak can reach at most about one half.
 PEAK_FP32_VALU_TFLOPS = 256 * 4 * 32 * 2 * 2.4e9 / 1e12
 # fp32 operations per (causal pair, sequence) in the Welford pass of the calibration score:
 # logit-to-log2 FMA (2), exp2 (1), delta (1), mean FMA (2), M2 subtract + FMA (3)
 WELFORD_FLOP_PER_SAMPLE = 9
-# exp2 rate: transcendental VALU instructions issue at a quarter of the fp32 rate, so
+# exp2 rate: a wave64 v_exp_f32 occupies the SIMD's vector ALU for 8 cycles (twice an FMA), so
 # 256 CUs x 4 SIMDs x 8 lanes per clock x 2.4 GHz = 19.7 Texp/s (a probe of v_exp_f32 measures
-# 19.2 Texp/s)
+# 17.6 Texp/s at the clock it ran at)
 PEAK_EXP_PER_S = 256 * 4 * 8 * 2.4e9
 
 
@@ -156,7 +158,10 @@ def main():
     o = torch.empty_like(v)
     lse = torch.empty((B, H, T), dtype=torch.float32, device=dev)
     dq, dk, dv = (torch.zeros((B, H, T, D), dtype=torch.float32, device=dev) for _ in range(3))
-    ws = torch.empty(max(saf.attn_workspace_size(v, L["frozen"], alpha), 1), dtype=torch.uint8, device=dev)
+    # one workspace for every head split this run times (its size grows with the frozen count)
+    ws_need = max(saf.attn_workspace_size(v, m, alpha)
+                  for m in (L["frozen"], np.zeros(H, np.uint8), np.ones(H, np.uint8)))
+    ws = torch.empty(max(ws_need, 1), dtype=torch.uint8, device=dev)
 
     def step(mask):
         saf.attn_fwd(q, k, v, mask, alpha, rho, o=o, lse=lse)

@@ -32,9 +32,11 @@ CSRC = os.path.join(PKG, "csrc")
 # kernel (short name) -> source files whose text determines it
 KERNEL_SOURCES = {
     "hybrid_fwd_kernel": ["fwd_bf16.hip", "saf_device.h"],
-    "dkdv_kernel": ["bwd_bf16.hip", "saf_device.h"],
-    "dq_kernel": ["bwd_bf16.hip", "saf_device.h"],
-    "bwd_delta_kernel": ["bwd_bf16.hip", "saf_device.h"],
+    "dkdv_kernel": ["bwd_bf16.hip", "saf_device.h", "frz_amax.h"],
+    "dq_kernel": ["bwd_bf16.hip", "saf_device.h", "frz_amax.h"],
+    "bwd_delta_kernel": ["bwd_bf16.hip", "saf_device.h", "frz_amax.h"],
+    "frz_half_kernel": ["frz_half.hip", "saf_device.h", "frz_amax.h"],
+    "frz_amax_kernel": ["frz_half.hip", "saf_device.h", "frz_amax.h"],
     "var_lse_kernel": ["var_score.hip", "saf_device.h"],
     "var_welford_kernel": ["var_score.hip", "saf_device.h"],
 }
@@ -43,7 +45,8 @@ KERNEL_WORKLOAD = {"var_lse_kernel": "calibration_N64_H12_T1024", "var_welford_k
 DEFAULT_WORKLOAD = "1b_T8192_r25"
 # bench/prof names -> kernel short names
 PROF_TO_KERNEL = {"hybrid_fwd": "hybrid_fwd_kernel", "dkdv": "dkdv_kernel", "dq": "dq_kernel",
-                  "bwd_delta": "bwd_delta_kernel", "var_lse": "var_lse_kernel",
+                  "bwd_delta": "bwd_delta_kernel", "frz_half": "frz_half_kernel",
+                  "frz_amax": "frz_amax_kernel", "var_lse": "var_lse_kernel",
                   "var_welford": "var_welford_kernel"}
 
 
@@ -182,14 +185,15 @@ def trace_summary(stats_csv: str, title: str, command: str, bench_log: str | Non
     return "\n".join(lines) + "\n"
 
 
-def mfma_summary(runs, command: str, n_simd: int = 1024, peak_clock_ghz: float = 2.4) -> str:
+def mfma_summary(runs, command: str, n_simd: int = 1024, peak_clock_ghz: float = 2.4,
+                 title: str = "1B-shape layer, B=2, H=16, T=8192, d_h=128, bf16") -> str:
     """MFMA utilisation per kernel from one `rocprofv3 --pmc SQ_VALU_MFMA_BUSY_CYCLES
     SQ_INSTS_VALU_MFMA_MOPS_BF16 SQ_BUSY_CU_CYCLES GRBM_GUI_ACTIVE` run per label.
     GRBM_GUI_ACTIVE is summed over the 8 XCDs, so /8 is the shader cycles of the dispatch; the
     MFMA-busy fraction is SQ_VALU_MFMA_BUSY_CYCLES over those cycles times the SIMD count,
     and against the published clock the same busy cycles over duration x 2.4 GHz x SIMDs.
     Executed bf16 FLOPs are SQ_INSTS_VALU_MFMA_MOPS_BF16 x 512."""
-    lines = ["# MFMA utilisation from counters (1B-shape layer, B=2, H=16, T=8192, d_h=128, bf16)", "",
+    lines = [f"# MFMA utilisation from counters ({title})", "",
              "Command (repository root R on the MI355X box):", "", "```", command, "```", "",
              "Counters are collected per dispatch (the kernels run slower under collection than in",
              "`bench.py`). Clock = GRBM_GUI_ACTIVE / 8 XCDs / duration.", "",
@@ -226,6 +230,7 @@ def main():
     mf.add_argument("--run", action="append", required=True, help="LABEL=path/to/run_counter_collection.csv")
     mf.add_argument("--command", default="")
     mf.add_argument("--out", required=True)
+    mf.add_argument("--title", default="1B-shape layer, B=2, H=16, T=8192, d_h=128, bf16")
     tr = sub.add_parser("trace")
     tr.add_argument("--stats", required=True)
     tr.add_argument("--title", required=True)
@@ -244,7 +249,7 @@ def main():
     if a.cmd == "mfma":
         runs = [tuple(x.rsplit("=", 1)) for x in a.run]
         with open(a.out, "w") as f:
-            f.write(mfma_summary(runs, a.command))
+            f.write(mfma_summary(runs, a.command, title=a.title))
         print(f"wrote {a.out}")
         return
     if a.cmd == "trace":
