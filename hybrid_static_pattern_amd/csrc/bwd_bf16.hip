@@ -807,15 +807,14 @@ hipError_t launch_bwd_bf16(const AttnArgs& a, const void* q, const void* k, cons
   }
   if ((e = launch_frz_half(a, dO, fh, p.n_dyn > 0, s)) != hipSuccess) return e;
   p.n_tiles = (a.T + BNK - 1) / BNK;
-  // folded columns per frozen item: B * D rounded up to 64, 128 or 256, except
-  //  * D = 64: at most 128, so that the launch's LDS (the frozen stages are sized by the
-  //    column count) fits three workgroups per CU (alternating runs: 124M shape at r = 50%
-  //    0.380 -> 0.341 ms, B = 64 prefill shape at T = 2048 0.828 -> 0.774 ms);
-  //  * D = 128 with at most a quarter of the heads frozen and B * D <= 512: 128 columns,
-  //    more and narrower frozen items between the ordinary ones (1B shape within 1%). With
-  //    more frozen heads the regenerated pattern tiles dominate and 256 columns stay faster
-  //    (every head frozen: 0.45 vs 0.60 ms).
-  const bool narrow = a.D == 64 || (a.B * a.D <= 512 && 4 * p.n_frz <= a.H);
+  // folded columns per frozen item: B * D rounded up to 64, 128 or 256, except at D = 64:
+  // at most 128, so that the launch's LDS (the frozen stages are sized by the column count)
+  // fits three workgroups per CU (alternating runs: 124M shape at r = 50% 0.380 -> 0.341 ms,
+  // B = 64 prefill shape at T = 2048 0.828 -> 0.774 ms). Each item regenerates its pattern
+  // tile, so wider items make fewer exps: with the single fp16 product per tile, 256 columns
+  // beat 128 on the 1B shape at r = 25% too (dK/dV 0.819 -> 0.812 ms in alternating runs;
+  // every head frozen: 0.45 vs 0.60 ms with the earlier two-product tile).
+  const bool narrow = a.D == 64;
   const int fc = a.B * a.D <= 64 ? 64 : (a.B * a.D <= 128 || narrow ? 128 : FCOLS);
   p.n_chunks = (a.B * a.D + fc - 1) / fc;
   p.per_tile = a.B * p.n_dyn + p.n_frz * p.n_chunks;
