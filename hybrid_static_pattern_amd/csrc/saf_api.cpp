@@ -113,6 +113,18 @@ saf_status validate_attn(const saf_attn_desc* d, saf::AttnArgs* a) {
     if (d->frozen_mask[h]) a->heads.frz[a->heads.n_frz++] = (uint8_t)h;
     else a->heads.dyn[a->heads.n_dyn++] = (uint8_t)h;
   }
+  // With shared key/value heads, the ordinary heads of one group should run on one XCD, so
+  // that their reads of the group's K and V share that XCD's L2. The attention kernels put
+  // ordinary (b, h) stream s = b n_dyn + x on XCD s mod 8; when n_dyn is a multiple of 8
+  // that is x mod 8, and dealing the ascending list out in contiguous runs of n_dyn / 8
+  // (run c to positions c, c + 8, ...) keeps consecutive heads, hence groups, together.
+  const int nd = a->heads.n_dyn;
+  if (a->G > 1 && nd % 8 == 0 && nd > 8) {
+    uint8_t sorted[saf::kMaxHeads];
+    std::memcpy(sorted, a->heads.dyn, sizeof(sorted));
+    const int per = nd / 8;
+    for (int k = 0; k < nd; ++k) a->heads.dyn[(k % per) * 8 + k / per] = sorted[k];
+  }
   if (a->heads.n_frz > 0 && d->tab_stride < d->T)
     return fail(SAF_EINVAL, "tab_stride (%d) must be >= T (%d)", d->tab_stride, d->T);
   return SAF_OK;

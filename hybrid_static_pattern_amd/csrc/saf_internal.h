@@ -9,8 +9,9 @@ namespace saf {
 
 constexpr int kMaxHeads = 256;
 
-// Head lists of one layer: the dynamic (ordinary) heads and the frozen heads, in
-// ascending head order.
+// Head lists of one layer: the dynamic (ordinary) heads and the frozen heads (frozen in
+// ascending head order; ordinary ones too, except that with shared key/value heads they may
+// be dealt out so that each group's heads share an XCD, see validate_attn).
 struct HeadLists {
   int n_dyn, n_frz;
   uint8_t dyn[kMaxHeads];
