@@ -19,13 +19,18 @@
 //           down; S and dP are computed with the key as the lane index so P and dS feed
 //           the dV and dK products straight from registers;
 //       frozen (h, 128-key tile, column chunk): the batch is folded into up to 256
-//           columns of [dO_0 | dO_1 | ...]; P^T is regenerated per lane and split into a
-//           bf16 high and low part (two MFMAs) so the fp32 dV keeps ~16 bits of P.
+//           columns of [dO_0 | dO_1 | ...]; P^T is regenerated per lane, rounded to fp16
+//           (11 significant bits) and multiplied in one fp16 MFMA per tile by a copy of the
+//           frozen heads' dO scaled by a power of two per (b, head) into fp16's range
+//           (frz_half.hip, launched between dq and dkdv; dq's extra items take the block
+//           maxima it needs), so the fp32 dV keeps P to 11 bits and dO exactly.
 // bwd_delta forms delta on its own for the float32 path.
 // Q/dO (dK/dV kernel) and K/V (dQ kernel) tiles go from HBM straight into multi-stage
 // LDS, one barrier per step; the transposed operands (dO^T, Q^T, K^T) are read from the
-// same row-major tiles with ds_read_b64_tr_b16. The split into a key-stationary and a query-stationary kernel recomputes S and dP once
-// more instead of accumulating dQ with atomics; every output is written exactly once.
+// same row-major tiles with ds_read_b64_tr_b16. The split into a key-stationary and a
+// query-stationary kernel recomputes S and dP once more instead of accumulating dQ with
+// atomics (fp32 atomic adds run at about 1.3 TB/s on this GPU, and a fused kernel would issue
+// gigabytes of them per layer); every output is written exactly once.
 #include "frz_amax.h"
 #include "saf_device.h"
 #include "saf_internal.h"
