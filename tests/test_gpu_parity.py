@@ -175,6 +175,10 @@ GQA_CASES = [
     (2, 4, 2, 70, 64, [1, 2], "fp32"),
     (1, 4, 1, 33, 128, [0], "fp32"),
     (2, 6, 3, 40, 64, [2, 3], "fp32"),         # group 1 all frozen
+    # 16 ordinary heads (a multiple of 8): the ordinary head list is dealt out so that each
+    # group's heads share an XCD, which must not change any result
+    (1, 16, 4, 200, 64, [], "bf16"),
+    (2, 24, 6, 130, 128, [0, 3, 7, 8, 12, 13, 17, 23], "bf16"),
 ]
 
 
