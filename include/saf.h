@@ -95,7 +95,11 @@ size_t saf_attn_workspace_size(const saf_attn_desc* desc);
  * Frozen heads:   dV = P^T dO only (part 二.4: alpha, rho are fixed buffers without
  *                 gradient and there is no query or key); lse must hold log Z(i).
  * o and lse are the forward's outputs for the same inputs. dQ/dK slices of frozen heads
- * are never written; dV is written for every head. Gradients are float32.
+ * are never written; dV is written for every head. Gradients are float32. With bf16 inputs
+ * the frozen heads' P^T dO is formed with P rounded to fp16 (11 significant bits) and dO
+ * scaled per (b, frozen head) by a power of two into fp16's range, which keeps every dO value
+ * within 2^28 of its slice's largest exact (the workspace holds that copy); the result is
+ * scaled back when stored.
  * With shared key/value heads (kv_heads < H) the gradient of a shared K or V is the sum over
  * the query heads of its group: dK[b, g] sums the group's ordinary heads (and is not written
  * when every head of the group is frozen); dV[b, g] sums all of them.
