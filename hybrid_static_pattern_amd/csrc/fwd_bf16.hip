@@ -306,36 +306,40 @@ __device__ void frz_item(const FwdParams& p, int h, int chunk, int qt, unsigned 
     if (j0 <= i0w) {
       // logits alpha(j) + rho(i - j); the window index of (i, j0 + kofs + e) is
       // m - (kofs + e) + 63, and entries for j > i hold -inf, so the causal mask comes for
-      // free. Up to 128 columns the 32 logits stay in registers between the max and the
-      // exps; next to the 128 accumulators of 256 columns they are read twice from LDS.
+      // free. The logits stay in registers between the max and the exps: all 32 of a tile
+      // up to 128 columns, and next to the 128 accumulators of 256 columns the tile is taken
+      // in two 32-key halves of 16 logits, each with its own max (an online softmax over any
+      // split of the keys is exact).
       const float* tb = sm.tab[w];
       const int rb0 = BN + m + BN - 1 - hh * 8;
       auto logit = [&](int ks, int e) { return tb[ks * 16 + hh * 8 + e] + tb[rb0 - ks * 16 - e]; };
-      float lg[FC <= 128 ? 4 : 1][8];
-      float mx = kNegInf;
+      constexpr int NHT = FC <= 128 ? 1 : 2;   // key halves of the tile
+      constexpr int KSH = 4 / NHT;             // 16-key steps per half
 #pragma unroll
-      for (int ks = 0; ks < 4; ++ks)
+      for (int ht = 0; ht < NHT; ++ht) {
+        float lg[KSH][8];
+        float mx = kNegInf;
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const float x = logit(ks, e);
-          if constexpr (FC <= 128) lg[ks][e] = x;
-          mx = fmaxf(mx, x);
+        for (int k2 = 0; k2 < KSH; ++k2)
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            lg[k2][e] = logit(ht * KSH + k2, e);
+            mx = fmaxf(mx, lg[k2][e]);
+          }
+        const float msub = online_rescale<FC / 32>(mx, kLog2e, m_used, l, o);
+#pragma unroll
+        for (int k2 = 0; k2 < KSH; ++k2) {
+          const int ks = ht * KSH + k2;
+          float pv[8];
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            pv[e] = __builtin_amdgcn_exp2f(__builtin_fmaf(lg[k2][e], kLog2e, -msub));
+            l += pv[e];
+          }
+          const bf16x8 pb = pack8(pv);
+          pipelined<FC / 32>([&](int cb) { return lds_tr<CPR>(sm.v, ks * 16, voff[cb][0], voff[cb][1]); },
+                             [&](int cb, const bf16x8& a) { o[cb] = mfma32(a, pb, o[cb]); });
         }
-      const float msub = online_rescale<FC / 32>(mx, kLog2e, m_used, l, o);
-#pragma unroll
-      for (int ks = 0; ks < 4; ++ks) {
-        float pv[8];
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          float x;
-          if constexpr (FC <= 128) x = lg[ks][e];
-          else x = logit(ks, e);
-          pv[e] = __builtin_amdgcn_exp2f(__builtin_fmaf(x, kLog2e, -msub));
-          l += pv[e];
-        }
-        const bf16x8 pb = pack8(pv);
-        pipelined<FC / 32>([&](int cb) { return lds_tr<CPR>(sm.v, ks * 16, voff[cb][0], voff[cb][1]); },
-                           [&](int cb, const bf16x8& a) { o[cb] = mfma32(a, pb, o[cb]); });
       }
     }
   };
