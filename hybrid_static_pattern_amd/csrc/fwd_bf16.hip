@@ -25,7 +25,7 @@
 // Key tiles (and a frozen item's per-wave alpha / rho tables) go from HBM straight into one of
 // NS LDS stages, NS - 1 tiles ahead of their use (no staging registers), one barrier per
 // tile; V is stored row-major and read transposed (ds_read_b64_tr_b16). Two workgroups (three
-// at D = 64 with at most 128 folded columns) share a CU: their waves are not tied by a common
+// at D = 64 with 128 folded columns, four with 64) share a CU: their waves are not tied by a common
 // barrier, so one runs its softmax arithmetic while another keeps the matrix cores busy. Items are issued heaviest q-tile first; key
 // tiles above a wave's causal diagonal are skipped by that wave.
 #include "saf_device.h"
@@ -369,8 +369,10 @@ __device__ void frz_item(const FwdParams& p, int h, int chunk, int qt, unsigned 
   }
 }
 
+// four workgroups per CU for D = 64 with at most 64 folded columns (124 registers), else two
+// (three at D = 64 with 128 columns, by registers and LDS)
 template <int D, int FC>
-__global__ __launch_bounds__(NTH, 2) void hybrid_fwd_kernel(const FwdParams p) {
+__global__ __launch_bounds__(NTH, (D == 64 && FC == 64) ? 4 : 2) void hybrid_fwd_kernel(const FwdParams p) {
   __shared__ __attribute__((aligned(16))) unsigned char smem[smem_bytes<D, FC>()];
   const int nd = p.B * p.n_dyn;
   int row, rem;
@@ -419,7 +421,13 @@ hipError_t launch_fwd_bf16(const AttnArgs& a, const void* q, const void* k, cons
   //  * T <= 512: at most 128, where a few query tiles make a short grid whose critical path
   //    the longer 256-column items set.
   const bool narrow = a.D == 64 || (a.B * a.D <= 512 && 4 * a.heads.n_frz <= a.H) || a.T <= 512;
-  const int fc = a.B * a.D <= 64 ? 64 : (a.B * a.D <= 128 || narrow ? 128 : FCOLS);
+  int fc = a.B * a.D <= 64 ? 64 : (a.B * a.D <= 128 || narrow ? 128 : FCOLS);
+  // a D = 64 launch without frozen heads takes the 64-column kernel, whose registers fit four
+  // workgroups per CU (alternating runs, forward at r = 0: 124M shape 0.265 -> 0.257 ms,
+  // B = 64 prefill shape at T = 2048 0.688 -> 0.637 ms); with frozen heads the 64-column
+  // items cost more than the fourth workgroup gains (B = 64, T = 2048, r = 50%: 0.519 ->
+  // 0.563 ms)
+  if (a.D == 64 && a.heads.n_frz == 0) fc = 64;
   p.n_chunks = (a.B * a.D + fc - 1) / fc;
   p.per_qt = a.B * p.n_dyn + p.n_frz * p.n_chunks;
   for (int x = 0; x < kMaxHeads; ++x) {
