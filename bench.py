@@ -127,7 +127,7 @@ def main():
                          "known-size reference for the FETCH_SIZE / WRITE_SIZE counters")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py measures one GPU: the layer's heads are independent and this build has no "
+        print("bench.py measures one GPU: the layer's heads are independent and libsaf has no "
               "multi-GPU path; run with --gpus 1", file=sys.stderr)
         sys.exit(2)
 

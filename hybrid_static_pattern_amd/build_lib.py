@@ -25,7 +25,7 @@ ARCH = "gfx950"
 FLAGS = [
     f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC",
     f"-I{INCLUDE}", f"-I{CSRC}",
-    # packed fp32 VALU forms are kept out of every kernel (see the design notes)
+    # no packed two-wide fp32 arithmetic in any kernel: the compiler is told not to form it
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-Wno-unused-result",
 ]

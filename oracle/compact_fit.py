@@ -20,7 +20,7 @@ Citations refer to the web page "When Can Attention Heads Be Statically Defined?
     is at most 0.2 nat; a candidate that fails is skipped and the next one in variance
     order is tried (Appendix A.2).
 
-Readings taken where the page is silent (each one is listed in the design notes):
+Readings taken where the page is silent:
   * the objective is the mean over the T rows of -sum_{j<=i} A(i,j) log P-hat(i,j), and the
     acceptance measure is the mean over the T rows of KL(A_i || P-hat_i) (row 0 included,
     where both are 0);

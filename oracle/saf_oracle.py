@@ -22,7 +22,7 @@ Citations refer to the web page "When Can Attention Heads Be Statically Defined?
     buffers without gradient; a frozen head still multiplies the current V, and its
     attention backward is only dV = P-hat^T dZ.
 
-Readings taken where the page is silent (each one is listed in the design notes):
+Readings taken where the page is silent:
   * positions are 0-indexed: query i, key j, distance d = i - j in [0, T); the page's
     1-indexed sum k = 1..i becomes j = 0..i, and the diagonal j = i is included;
   * frozen logits alpha + rho are not scaled by 1/sqrt(d_h); dynamic logits are;
