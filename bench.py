@@ -186,10 +186,33 @@ def main():
             saf.prof_enable(False)
         return ms, recs
 
-    log(f"timing {args.steps} steps of {args.workload}")
     mask = L["frozen"]
     n_frz = int(mask.sum())
     n_dyn = H - n_frz
+    # The shader clock climbs over the first ~100 ms of sustained load (about 1.8 -> 2.0 GHz on
+    # this layer), longer than W + K steps take. The layer is timed once first, from idle, and
+    # reported as cold_start; the other workloads then run, and the layer's reported value is
+    # timed right after them, with the clock where back-to-back steps keep it.
+    log(f"timing {args.steps} steps of {args.workload} from idle (cold start)")
+    ms_cold, _ = timed(mask, args.steps, args.warmup)
+    extra = {}
+    if not args.no_l124m:
+        log("timing the 124M-shaped layer")
+        extra["l124m"] = l124m(torch, inputs, saf, args.steps, args.warmup)
+    if not args.no_calibration:
+        log("timing the calibration score")
+        extra["calibration"] = calibration(torch, inputs, profiling, saf, args.steps, args.warmup)
+    if not args.no_fit:
+        log("timing the compact pattern fit")
+        extra["fit"] = fit(torch, inputs, saf, args.no_cpu_baseline)
+    if not args.no_prefill:
+        log("timing the causal prefill workload")
+        extra["prefill"] = prefill(torch, inputs, saf, args.steps, args.warmup)
+    if not args.no_gqa:
+        log("timing the grouped-query-attention layer")
+        extra["gqa"] = gqa(torch, inputs, saf, args.steps, args.warmup)
+
+    log(f"timing {args.steps} steps of {args.workload}")
     ms, recs = timed(mask, args.steps, args.warmup, prof=True)
 
     per_kernel = {}
@@ -224,6 +247,8 @@ def main():
             "kernel": dominant, "bound": "mfma", "achieved": achieved, "peak": PEAK_BF16_TFLOPS,
             "unit": "TFLOP/s", "frac": achieved / PEAK_BF16_TFLOPS, "traffic": traffic_bytes(profiling, dominant),
         },
+        "cold_start": {"ms_per_step": ms_cold, "tokens_per_s": B * T / (ms_cold * 1e-3),
+                       "note": f"the same {args.warmup} + {args.steps} steps timed first, from idle"},
     }
     if not args.no_sweep:
         sweep = {}
@@ -239,21 +264,7 @@ def main():
     # the frozen path alone: every head of the same layer frozen
     if not args.no_frozen_path:
         out["frozen_path"] = frozen_path(timed, args, B, H, T, D, out)
-    if not args.no_l124m:
-        log("timing the 124M-shaped layer")
-        out["l124m"] = l124m(torch, inputs, saf, args.steps, args.warmup)
-    if not args.no_calibration:
-        log("timing the calibration score")
-        out["calibration"] = calibration(torch, inputs, profiling, saf, args.steps, args.warmup)
-    if not args.no_fit:
-        log("timing the compact pattern fit")
-        out["fit"] = fit(torch, inputs, saf, args.no_cpu_baseline)
-    if not args.no_gqa:
-        log("timing the grouped-query-attention layer")
-        out["gqa"] = gqa(torch, inputs, saf, args.steps, args.warmup)
-    if not args.no_prefill:
-        log("timing the causal prefill workload")
-        out["prefill"] = prefill(torch, inputs, saf, args.steps, args.warmup)
+    out.update(extra)
     if not args.no_cpu_baseline:
         log("timing the CPU oracle on a sample of the layer")
     out["cpu_baseline"] = None if args.no_cpu_baseline else cpu_baseline(L, n_dyn, n_frz)

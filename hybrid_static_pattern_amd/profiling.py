@@ -179,7 +179,7 @@ def trace_summary(stats_csv: str, title: str, command: str, bench_log: str | Non
     live = live_timings(bench_log) if bench_log else {}
     if live:
         lines += ["", "Live HIP-event averages that the same traced bench.py run printed for its timed steps",
-                  "(the trace's averages above also count the warm-up calls):", "",
+                  "(the trace's averages above also count the warm-up and cold-start calls):", "",
                   "| kernel | average us |", "|---|---|"]
         lines += [f"| {k} | {1e3 * v:.1f} |" for k, v in live.items()]
     return "\n".join(lines) + "\n"
