@@ -287,7 +287,6 @@ def prefill(torch, inputs, saf, steps, warmup):
     P = inputs.PREFILL
     H, D = P["H"], P["D"]
     dev = torch.device("cuda:0")
-    gen = torch.Generator(device=dev)
 
     def masks(seed):
         out = []
@@ -299,8 +298,7 @@ def prefill(torch, inputs, saf, steps, warmup):
         return out
 
     def run(B, T, seed):
-        gen.manual_seed(seed)
-        q, k, v = (torch.randn((B, H, T, D), generator=gen, device=dev).to(torch.bfloat16) for _ in range(3))
+        q, k, v = inputs.randn_bf16_device(torch, [(B, H, T, D)] * 3, seed)
         alpha, rho = (torch.from_numpy(x).to(dev) for x in inputs.make_tables(np.random.default_rng(seed), H, T))
         o = torch.empty_like(v)
         lse = torch.empty((B, H, T), dtype=torch.float32, device=dev)
@@ -366,9 +364,7 @@ def l124m(torch, inputs, saf, steps, warmup):
     spec = dict(inputs.WORKLOADS["l124m_fwdbwd"])
     B, H, T, D = spec["B"], spec["H"], spec["T"], spec["D"]
     dev = torch.device("cuda:0")
-    gen = torch.Generator(device=dev)
-    gen.manual_seed(spec["seed"])
-    q, k, v, do = (torch.randn((B, H, T, D), generator=gen, device=dev).to(torch.bfloat16) for _ in range(4))
+    q, k, v, do = inputs.randn_bf16_device(torch, [(B, H, T, D)] * 4, spec["seed"])
     rng = np.random.default_rng(spec["seed"])
     alpha, rho = (torch.from_numpy(x).to(dev) for x in inputs.make_tables(rng, H, T))
     m25 = inputs.choose_frozen(rng, H, spec["n_frozen"])
@@ -420,11 +416,7 @@ def gqa(torch, inputs, saf, steps, warmup):
     spec = dict(inputs.WORKLOADS["gqa_4b"])
     B, H, Hkv, T, D = spec["B"], spec["H"], spec["kv_heads"], spec["T"], spec["D"]
     dev = torch.device("cuda:0")
-    gen = torch.Generator(device=dev)
-    gen.manual_seed(spec["seed"])
-    rnd = lambda shape: torch.randn(shape, generator=gen, device=dev).to(torch.bfloat16)
-    q, do = rnd((B, H, T, D)), rnd((B, H, T, D))
-    k, v = rnd((B, Hkv, T, D)), rnd((B, Hkv, T, D))
+    q, do, k, v = inputs.randn_bf16_device(torch, [(B, H, T, D)] * 2 + [(B, Hkv, T, D)] * 2, spec["seed"])
     alpha, rho = (torch.from_numpy(x).to(dev) for x in inputs.make_tables(np.random.default_rng(spec["seed"]), H, T))
     o = torch.empty_like(q)
     lse = torch.empty((B, H, T), dtype=torch.float32, device=dev)

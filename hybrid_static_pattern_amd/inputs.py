@@ -91,6 +91,17 @@ def make_layer(B: int, H: int, T: int, D: int, dtype: str = BF16, seed: int = 0,
                 B=B, H=H, H_kv=H_kv, T=T, D=D, dtype=dtype, seed=seed)
 
 
+def randn_bf16_device(torch, shapes, seed: int, device: str = "cuda:0"):
+    """Seeded N(0, 1) tensors drawn on the device by torch's generator, in float32 and rounded
+    to bfloat16 (nearest even), one per shape, in order. For the workloads too large to draw
+    on the host in reasonable time (the longest prefill: 2.4e9 values take minutes with
+    numpy); alpha, rho and the frozen set still come from make_tables / choose_frozen."""
+    gen = torch.Generator(device=device)
+    gen.manual_seed(seed)
+    return [torch.randn(tuple(s), generator=gen, device=device, dtype=torch.float32).to(torch.bfloat16)
+            for s in shapes]
+
+
 def temperatures(rng: np.random.Generator, H: int, lo: float = 0.1, hi: float = 4.0):
     """Per-head logit temperatures, log-spaced over [lo, hi] and permuted by the seed."""
     tau = np.exp(np.linspace(np.log(lo), np.log(hi), H))

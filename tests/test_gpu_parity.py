@@ -582,6 +582,29 @@ def test_full_prefill_t2048_half_frozen(S):
     _full(S, "prefill_t2048", [(31, first_frozen), (5, last_dynamic)], bwd=False)
 
 
+def test_full_prefill_t16384_sampled(S):
+    """The longest prefill the bench times (B=64, H=12, T=16384, D=64, 3 of 12 heads frozen):
+    Q, K, V drawn on the device by the seeded generator (a host draw of this size takes
+    minutes), two whole heads, a frozen one in the last batch entry and an ordinary one in
+    the first, copied back and checked against the oracle."""
+    B, H, T, D = 64, 12, 16384, 64
+    q, k, v = inputs.randn_bf16_device(torch, [(B, H, T, D)] * 3, seed=16)
+    rng = np.random.default_rng(16)
+    alpha, rho = inputs.make_tables(rng, H, T)
+    fz = inputs.choose_frozen(rng, H, 3)
+    heads = ((B - 1, first_frozen(fz)), (0, last_dynamic(fz)))
+    # the sampled heads' inputs are copied to the host before the kernel runs
+    host = {(b, h): [down(t[b:b + 1, h:h + 1]) for t in (q, k, v)] for b, h in heads}
+    o, lse = S.attn_fwd(q, k, v, fz, torch.from_numpy(alpha).to(dev()), torch.from_numpy(rho).to(dev()))
+    torch.cuda.synchronize()
+    scale = 1.0 / math.sqrt(D)
+    for b, h in heads:
+        O, ls = saf_oracle.attn_fwd(*host[b, h], fz[h:h + 1], alpha[h:h + 1], rho[h:h + 1], scale)
+        check(down(o[b, h]), O[0, 0], "bf16", f"O[{b},{h}]")
+        check(down(lse[b, h]), ls[0, 0], "bf16", f"lse[{b},{h}]", lse=True)
+    del q, k, v, o, lse
+
+
 def test_full_calibration_sampled(S):
     """The calibration workload: A-hat of three sampled heads entry by entry against the oracle,
     and every head's s_var (1e-3 relative), the sum of its A-hat squared and the full ranking

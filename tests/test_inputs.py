@@ -39,3 +39,16 @@ def test_calibration_temperatures_span():
     c = inputs.make_calibration(2, 12, 16, 8, seed=4)
     assert np.isclose(c["tau"].min(), 0.1) and np.isclose(c["tau"].max(), 4.0)
     assert not np.all(np.diff(c["tau"]) > 0)  # permuted, so rank order is not head order
+
+
+def test_device_generator_is_seeded_bf16():
+    """randn_bf16_device draws with torch's seeded generator (here on the CPU device): the same
+    seed gives the same tensors in the same order, the values are bfloat16 N(0, 1)."""
+    a = inputs.randn_bf16_device(torch, [(2, 3, 64, 8), (1, 3, 64, 8)], seed=7, device="cpu")
+    b = inputs.randn_bf16_device(torch, [(2, 3, 64, 8), (1, 3, 64, 8)], seed=7, device="cpu")
+    c = inputs.randn_bf16_device(torch, [(2, 3, 64, 8)], seed=8, device="cpu")
+    assert [t.shape for t in a] == [(2, 3, 64, 8), (1, 3, 64, 8)]
+    assert all(t.dtype == torch.bfloat16 for t in a)
+    assert all(torch.equal(x, y) for x, y in zip(a, b)) and not torch.equal(a[0], c[0])
+    x = a[0].float()
+    assert abs(x.mean().item()) < 0.1 and abs(x.std().item() - 1.0) < 0.1
