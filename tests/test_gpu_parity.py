@@ -578,6 +578,24 @@ def test_full_gqa_4b_sampled(S):
     compare_shared(S, L, out, groups=groups)
 
 
+@pytest.mark.parametrize("n_frozen", [0, 16])
+def test_full_gqa_4b_other_ratios(S, n_frozen):
+    """The shared-key/value shape at the bench's other ratios, r = 0 and r = 50%: two whole
+    groups against the oracle (the first and the last; at r = 50% the groups of the first
+    frozen and the last ordinary head)."""
+    spec = dict(inputs.WORKLOADS["gqa_4b"])
+    spec["n_frozen"] = n_frozen
+    L = inputs.make_layer(**spec)
+    out = run(S, L)
+    G = L["H"] // L["H_kv"]
+    fz = L["frozen"]
+    if fz.any():
+        groups = sorted({int(np.flatnonzero(fz)[0]) // G, int(np.flatnonzero(fz == 0)[-1]) // G})
+    else:
+        groups = [0, L["H_kv"] - 1]
+    compare_shared(S, L, out, groups=groups)
+
+
 def test_full_prefill_t2048_half_frozen(S):
     _full(S, "prefill_t2048", [(31, first_frozen), (5, last_dynamic)], bwd=False)
 
